@@ -1,0 +1,264 @@
+"""Python view of the CPU oracle (test infrastructure only).
+
+Only tests/, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  It wraps ``libkvq_oracle.so`` (plain C,
+``oracle/kvq_oracle.c``) with numpy marshalling and composes its functions
+into the reference for one decode step:
+
+  quantize on store -> dequantize -> softmax attention in fp64
+
+following the pipeline that "KV Cache 압축" (ryotta.opik.net) §5.1 lists and
+the store-time quantization with BF16 scales kept next to the codes that
+"KV 캐시 양자화(KV cache quantization) ..." (molayo1419.me) describes in its
+"what it is" section.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvq_oracle.so")
+
+FP8, INT8 = 1, 2
+PER_TENSOR, PER_HEAD, PER_TOKEN_HEAD = 0, 1, 2
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from oracle import build as _b
+            _b.build()
+        L = ctypes.CDLL(LIB_PATH)
+        L.kvqo_bf16_value.restype = ctypes.c_float
+        L.kvqo_bf16_value.argtypes = [ctypes.c_uint16]
+        for f in ("kvqo_bf16_rne", "kvqo_bf16_up", "kvqo_bf16_down"):
+            getattr(L, f).restype = ctypes.c_uint16
+            getattr(L, f).argtypes = [ctypes.c_float]
+        L.kvqo_f16_value.restype = ctypes.c_double
+        L.kvqo_f16_value.argtypes = [ctypes.c_uint16]
+        L.kvqo_f16_rne.restype = ctypes.c_uint16
+        L.kvqo_f16_rne.argtypes = [ctypes.c_double]
+        L.kvqo_bf16_to_f16_array.argtypes = [_P, ctypes.c_int64, _P]
+        L.kvqo_e4m3_value.restype = ctypes.c_double
+        L.kvqo_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.kvqo_e4m3_encode.restype = ctypes.c_uint8
+        L.kvqo_e4m3_encode.argtypes = [ctypes.c_float]
+        L.kvqo_e4m3_encode_range.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _P]
+        L.kvqo_e4m3_encode_array.argtypes = [_P, ctypes.c_int64, _P]
+        L.kvqo_fp8_row.argtypes = [_P, ctypes.c_int, _P, _P]
+        L.kvqo_fp8_row_static.argtypes = [_P, ctypes.c_int, ctypes.c_uint16, _P]
+        L.kvqo_int8_row.argtypes = [_P, ctypes.c_int, _P, _P, _P]
+        L.kvqo_uint_asym.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, ctypes.c_int, _P, _P]
+        L.kvqo_quantize_rows.argtypes = [ctypes.c_int, ctypes.c_int, _P, ctypes.c_int64, ctypes.c_int,
+                                         _P, _P, _P, _P]
+        L.kvqo_dequantize_rows.argtypes = [ctypes.c_int, ctypes.c_int, _P, ctypes.c_int64, ctypes.c_int,
+                                           _P, _P, _P]
+        L.kvqo_kivi_quantized_count.restype = ctypes.c_int64
+        L.kvqo_kivi_quantized_count.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+        L.kvqo_kivi_k.argtypes = [_P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P, _P]
+        L.kvqo_kivi_v.argtypes = [_P, ctypes.c_int64, ctypes.c_int, _P, _P, _P]
+        L.kvqo_attention.argtypes = [_P, _P, _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_double, _P, _P]
+        L.kvqo_lse_merge.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, _P, _P]
+        L.kvqo_kv_bytes.restype = ctypes.c_double
+        L.kvqo_kv_bytes.argtypes = [ctypes.c_double] * 6
+        _lib = L
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=dtype)
+
+
+# ---------------------------------------------------------------- formats
+def bf16_value(bits) -> np.ndarray:
+    b = _c(bits, np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_table() -> np.ndarray:
+    """fp64 value of each of the 256 E4M3 codes (NaN for 0x7F and 0xFF)."""
+    L = lib()
+    return np.array([L.kvqo_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_encode(y) -> np.ndarray:
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib().kvqo_e4m3_encode_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def e4m3_encode_range(first_bits: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.uint8)
+    lib().kvqo_e4m3_encode_range(first_bits, count, _ptr(out))
+    return out
+
+
+def f16_value(bits) -> np.ndarray:
+    return _c(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def f16_rne(x) -> np.ndarray:
+    L = lib()
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([L.kvqo_f16_rne(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def bf16_to_f16_bits(x_bf16) -> np.ndarray:
+    """fp16 bits (nearest-even) of bf16 values."""
+    x = _c(x_bf16, np.uint16)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().kvqo_bf16_to_f16_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- quantizers
+def quantize_rows(dtype: int, mode: int, x_bf16, static_scale=None):
+    """Quantize rows of bf16 bits [..., n] -> (codes u8, scale bf16 bits, zero bf16 bits or None)."""
+    x = _c(x_bf16, np.uint16)
+    n = x.shape[-1]
+    rows = x.size // n
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scale = np.empty(x.shape[:-1], dtype=np.uint16)
+    zero = np.empty(x.shape[:-1], dtype=np.uint16) if dtype == INT8 else None
+    ss = None
+    if mode != PER_TOKEN_HEAD:
+        ss = _c(np.broadcast_to(np.asarray(static_scale, dtype=np.uint16), x.shape[:-1]), np.uint16)
+    lib().kvqo_quantize_rows(dtype, mode, _ptr(x), rows, n, _ptr(ss), _ptr(codes), _ptr(scale), _ptr(zero))
+    return codes, scale, zero
+
+
+def dequantize_rows(dtype: int, codes, scale, zero=None) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    n = c.shape[-1]
+    s = _c(np.broadcast_to(np.asarray(scale, dtype=np.uint16), c.shape[:-1]), np.uint16)
+    z = None if zero is None else _c(np.broadcast_to(np.asarray(zero, dtype=np.uint16), c.shape[:-1]), np.uint16)
+    out = np.empty(c.shape, dtype=np.float64)
+    lib().kvqo_dequantize_rows(dtype, 2, _ptr(c), c.size // n, n, _ptr(s), _ptr(z), _ptr(out))
+    return out
+
+
+def uint_asym(x, levels: int):
+    """Asymmetric quantizer over a 1-D float32 vector -> (codes, s bits, z bits)."""
+    x = _c(x, np.float32)
+    codes = np.empty(x.size, dtype=np.uint8)
+    s = np.zeros(1, dtype=np.uint16)
+    z = np.zeros(1, dtype=np.uint16)
+    lib().kvqo_uint_asym(_ptr(x), x.size, 1, levels, _ptr(codes), 1, _ptr(s), _ptr(z))
+    return codes, int(s[0]), int(z[0])
+
+
+# ---------------------------------------------------------------- KIVI
+def kivi_quantized_count(T: int, resid: int, group: int) -> int:
+    return int(lib().kvqo_kivi_quantized_count(T, resid, group))
+
+
+def kivi_stream(x16_k, x16_v, resid: int, group: int):
+    """KIVI state of one (sequence, KV head): fp16 bits [T][n] for K and V.
+
+    Returns dict with nq, K codes/s/z (per channel per group), V codes/s/z
+    (per token), and the fp16 residual rows [nq, T).
+    """
+    k = _c(x16_k, np.uint16)
+    v = _c(x16_v, np.uint16)
+    T, n = k.shape
+    nq = kivi_quantized_count(T, resid, group)
+    kc = np.zeros((nq, n), dtype=np.uint8)
+    ks = np.zeros((nq // group, n), dtype=np.uint16)
+    kz = np.zeros((nq // group, n), dtype=np.uint16)
+    vc = np.zeros((nq, n), dtype=np.uint8)
+    vs = np.zeros(nq, dtype=np.uint16)
+    vz = np.zeros(nq, dtype=np.uint16)
+    L = lib()
+    if nq:
+        L.kvqo_kivi_k(_ptr(k), nq, n, group, _ptr(kc), _ptr(ks), _ptr(kz))
+        L.kvqo_kivi_v(_ptr(v), nq, n, _ptr(vc), _ptr(vs), _ptr(vz))
+    return dict(nq=nq, k_codes=kc, k_s=ks, k_z=kz, v_codes=vc, v_s=vs, v_z=vz,
+                k_res=k[nq:].copy(), v_res=v[nq:].copy())
+
+
+def kivi_dequant(st, group: int) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 K^, V^ [T][n] of one KIVI stream."""
+    nq = st["nq"]
+    kc = st["k_codes"].astype(np.float64)
+    ks = np.repeat(bf16_value(st["k_s"]).astype(np.float64), group, axis=0)
+    kz = np.repeat(bf16_value(st["k_z"]).astype(np.float64), group, axis=0)
+    vc = st["v_codes"].astype(np.float64)
+    vs = bf16_value(st["v_s"]).astype(np.float64)[:, None]
+    vz = bf16_value(st["v_z"]).astype(np.float64)[:, None]
+    kq = kc * ks[:nq] + kz[:nq]
+    vq = vc * vs + vz
+    k = np.concatenate([kq, f16_value(st["k_res"])], axis=0)
+    v = np.concatenate([vq, f16_value(st["v_res"])], axis=0)
+    return k, v
+
+
+# ---------------------------------------------------------------- attention
+def attention(q, k, v, softmax_scale: float):
+    """q [Hq][d], k/v [T][n_kv][d] (fp64) -> (out [Hq][d], lse [Hq])."""
+    q = _c(q, np.float64)
+    k = _c(k, np.float64)
+    v = _c(v, np.float64)
+    Hq, d = q.shape
+    T, n_kv, _ = k.shape if k.ndim == 3 else (0, 1, d)
+    out = np.empty((Hq, d), dtype=np.float64)
+    lse = np.empty(Hq, dtype=np.float64)
+    lib().kvqo_attention(_ptr(q), _ptr(k), _ptr(v), T, Hq, n_kv, d,
+                         float(np.float32(softmax_scale)), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def lse_merge(o_parts, lse_parts):
+    o = _c(o_parts, np.float64)
+    l = _c(lse_parts, np.float64)
+    P, d = o.shape
+    out = np.empty(d, dtype=np.float64)
+    lo = np.empty(1, dtype=np.float64)
+    lib().kvqo_lse_merge(_ptr(o), _ptr(l), P, d, _ptr(out), _ptr(lo))
+    return out, float(lo[0])
+
+
+def kv_bytes(layers, n_kv_heads, head_dim, seq_len, batch, bytes_per_elem) -> float:
+    return float(lib().kvqo_kv_bytes(layers, n_kv_heads, head_dim, seq_len, batch, bytes_per_elem))
+
+
+# ---------------------------------------------------------------- one decode step
+def decode_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD,
+                     static_kv=None, softmax_scale: Optional[float] = None):
+    """Reference for one sequence.
+
+    q_bf16 [Hq][d], k_bf16 / v_bf16 [T][n_kv][d] (bf16 bits).  ``static_kv`` =
+    (k_scale, v_scale) bf16 bits broadcastable to [n_kv] for static modes.
+    Returns dict: K/V codes, scales, zeros, and fp64 out [Hq][d], lse [Hq].
+    """
+    q = bf16_value(q_bf16).astype(np.float64)
+    d = q.shape[-1]
+    scale = (1.0 / np.sqrt(d)) if softmax_scale is None else softmax_scale
+    k_bf16 = _c(k_bf16, np.uint16)
+    v_bf16 = _c(v_bf16, np.uint16)
+    T, n_kv, _ = k_bf16.shape
+    res = {}
+    for name, x, idx in (("k", k_bf16, 0), ("v", v_bf16, 1)):
+        ss = None
+        if mode != PER_TOKEN_HEAD:
+            ss = np.broadcast_to(np.asarray(static_kv[idx], dtype=np.uint16), (n_kv,))
+            ss = np.broadcast_to(ss, (T, n_kv))
+        c, s, z = quantize_rows(dtype, mode, x, ss)
+        res[name + "_codes"], res[name + "_scale"], res[name + "_zero"] = c, s, z
+        res[name + "_hat"] = dequantize_rows(dtype, c, s, z)
+    out, lse = attention(q, res["k_hat"], res["v_hat"], scale)
+    res["out"], res["lse"] = out, lse
+    return res

@@ -1,0 +1,246 @@
+"""Seeded synthetic inputs for the paged quantized KV-cache decode path.
+
+This module holds input generation only: no quantization, no attention and
+no rounding rule of the method lives here.  Both sides of every comparison
+(the CPU oracle under ``oracle/`` and the HIP library under
+``quantized_kv_cache_08_amd/``) receive the same tensors from it, and neither
+side imports the other.
+
+Generator
+---------
+Counter-based and device-independent.  Element ``i`` of tensor ``tid`` under
+seed ``seed`` draws three SplitMix64 outputs (Steele, Lea & Flood, "Fast
+splittable pseudorandom number generators", OOPSLA 2014): state
+``key + (3*i + j + 1) * 0x9E3779B97F4A7C15`` passed through the SplitMix64
+finaliser, ``j = 0, 1, 2``.  The twelve 16-bit fields of those outputs are
+summed (Irwin-Hall with twelve uniforms), which gives mean 0 and variance 1:
+
+    x = (sum_k u_k + 6) / 65536 - 6,     u_k in [0, 65535]
+
+Every step is integer arithmetic or an exact float32 operation, so CPU and GPU
+produce the same bits; the final bf16 cast is round-to-nearest-even on both.
+Values are ``x * sigma`` with sigma in {1, 1.5, 20, 30}, all exact in float32
+before the bf16 cast.
+
+Workload shapes follow the decode configurations the pages motivate
+(Llama-3-8B-like 32 q / 8 kv heads, Llama-3-70B-like 64 q / 8 kv heads,
+head_dim 128, mixed chat lengths, KIVI-style long context).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "Workload", "WORKLOADS", "normal", "gen_q", "gen_kv", "gen_new_kv",
+    "outlier_channels", "seq_lens", "page_layout",
+]
+
+_MASK64 = (1 << 64) - 1
+
+
+def _i64(v: int) -> int:
+    v &= _MASK64
+    return v - (1 << 64) if v >= (1 << 63) else v
+
+
+_GOLD = _i64(0x9E3779B97F4A7C15)
+_M1 = _i64(0xBF58476D1CE4E5B9)
+_M2 = _i64(0x94D049BB133111EB)
+
+
+def _mix_int(z: int) -> int:
+    """SplitMix64 finaliser on a Python int (mod 2**64)."""
+    z &= _MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+    return z ^ (z >> 31)
+
+
+def _srl(x: torch.Tensor, k: int) -> torch.Tensor:
+    """Logical right shift of an int64 tensor viewed as uint64."""
+    return (x >> k) & ((1 << (64 - k)) - 1)
+
+
+def _mix(z: torch.Tensor) -> torch.Tensor:
+    """SplitMix64 finaliser on int64 tensors (multiplication wraps mod 2**64)."""
+    z = (z ^ _srl(z, 30)) * _M1
+    z = (z ^ _srl(z, 27)) * _M2
+    return z ^ _srl(z, 31)
+
+
+def _key(seed: int, tid: int) -> int:
+    return _i64(_mix_int(_mix_int(seed * 0x100000001B3 + 0x51ED27) ^ (tid * 0xD6E8FEB86659FD93)))
+
+
+def normal(seed: int, tid: int, idx: torch.Tensor) -> torch.Tensor:
+    """Approximately N(0, 1) float32 values, one per int64 counter in ``idx``.
+
+    Works on any device; results are bitwise identical across devices.
+    """
+    idx = idx.to(torch.int64)
+    key = _key(seed, tid)
+    acc = torch.zeros_like(idx)
+    base = idx * 3 + 1
+    for j in range(3):
+        z = _mix((base + j) * _GOLD + key)
+        acc = acc + (z & 0xFFFF) + ((z >> 16) & 0xFFFF) + ((z >> 32) & 0xFFFF) + _srl(z, 48)
+    return (acc + 6).to(torch.float32) * (1.0 / 65536.0) - 6.0
+
+
+def _uniform_keys(seed: int, tid: int, n: int) -> np.ndarray:
+    key = _key(seed, tid)
+    idx = torch.arange(n, dtype=torch.int64)
+    z = _mix((idx + 1) * _GOLD + key)
+    return _srl(z, 1).numpy()
+
+
+# --------------------------------------------------------------------------
+# Tensor ids (one stream per logical tensor)
+T_Q, T_K, T_V, T_LEN, T_PERM, T_OUTL, T_KNEW, T_VNEW = range(8)
+MAXPOS = 1 << 22          # positions per sequence in the counter space
+
+
+def outlier_channels(seed: int, head_dim: int, count: int) -> List[int]:
+    """``count`` channel indices, the same for every token and KV head."""
+    if count <= 0:
+        return []
+    keys = _uniform_keys(seed, T_OUTL, head_dim)
+    return sorted(int(c) for c in np.argsort(keys, kind="stable")[:count])
+
+
+def _scaled_bf16(x: torch.Tensor, sigma: float, outl: Optional[List[int]], outl_mult: float) -> torch.Tensor:
+    mult = torch.full((x.shape[-1],), float(sigma), dtype=torch.float32, device=x.device)
+    if outl:
+        mult[outl] = float(sigma) * float(outl_mult)
+    return (x * mult).to(torch.bfloat16)
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str                # "fp8" | "int8" | "kivi4"
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    context: int              # uniform context, or the cap for "mixed"
+    seed: int
+    sigma_k: float = 1.0
+    sigma_v: float = 1.0
+    n_outliers: int = 4
+    outlier_mult: float = 20.0
+    mixed: bool = False       # lognormal lengths + shuffled shared page pool
+    median_len: float = 1500.0
+    len_sigma: float = 0.7
+    spare_frac: float = 0.05
+    resid: int = 128          # KIVI fp16 recent window
+    group: int = 32           # KIVI group along tokens
+    description: str = ""
+
+    @property
+    def group_size(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", "fp8", 1, 8, 2, 128, 16, 512, seed=1,
+                     description="1 layer, batch 1, 8 q / 2 kv heads, d128, context 512, page 16, FP8 E4M3 "
+                                 "per-(token,head) scale, 4 K outlier channels x20"),
+    "llama8b": Workload("llama8b", "fp8", 32, 32, 8, 128, 16, 8192, seed=2,
+                        description="Llama-3-8B-shaped decode layer: 32 q / 8 kv heads, d128, batch 32, "
+                                    "context 8192, page 16, FP8 E4M3 per-(token,head) scales, outlier K channels"),
+    "llama70b": Workload("llama70b", "int8", 64, 64, 8, 128, 16, 32768, seed=3, sigma_k=1.5, sigma_v=1.5,
+                         n_outliers=0,
+                         description="Llama-3-70B-shaped layer: 64 q / 8 kv heads, d128, batch 64, context 32768, "
+                                     "page 16, INT8 per-(token,head) asymmetric, K/V ~N(0,1.5)"),
+    "mixed": Workload("mixed", "fp8", 256, 32, 8, 128, 16, 32768, seed=4, mixed=True,
+                      description="Mixed chat batch: 256 sequences, lognormal lengths (median 1500, sigma 0.7, "
+                                  "cap 32768), 32 q / 8 kv heads, d128, shuffled shared page pool, FP8 E4M3"),
+    "kivi": Workload("kivi", "kivi4", 4, 64, 8, 128, 32, 131072, seed=5,
+                     description="KIVI-style 4-bit: 64 q / 8 kv heads, d128, batch 4, context 131072; K per-channel "
+                                 "INT4 in 32-token groups, V per-token INT4, last 128 tokens fp16"),
+}
+
+
+def seq_lens(w: Workload) -> np.ndarray:
+    """Context lengths (int64) per sequence."""
+    if not w.mixed:
+        return np.full(w.batch, w.context, dtype=np.int64)
+    z = normal(w.seed, T_LEN, torch.arange(w.batch, dtype=torch.int64)).double().numpy()
+    lens = np.rint(np.exp(math.log(w.median_len) + w.len_sigma * z))
+    return np.clip(lens, 1, w.context).astype(np.int64)
+
+
+@dataclass
+class PageLayout:
+    num_pages: int
+    block_table: np.ndarray   # int32 [B][max_pages]
+    pages_per_seq: np.ndarray
+    spare_pages: List[int] = field(default_factory=list)
+
+
+def page_layout(w: Workload, lens: np.ndarray, page_size: Optional[int] = None,
+                shuffle: Optional[bool] = None) -> PageLayout:
+    """Block tables over one shared pool.
+
+    Contiguous runs per sequence, or (mixed workloads, or ``shuffle=True``) a
+    seeded random permutation of a pool with ``spare_frac`` unused pages.
+    """
+    ps = page_size or w.page_size
+    need = (lens + ps - 1) // ps
+    total = int(need.sum())
+    shuffle = w.mixed if shuffle is None else shuffle
+    maxp = max(1, int(need.max()) if len(need) else 1)
+    bt = np.zeros((len(lens), maxp), dtype=np.int32)
+    if shuffle:
+        pool = int(math.ceil(total * (1.0 + w.spare_frac))) + 1
+        perm = np.argsort(_uniform_keys(w.seed, T_PERM, pool), kind="stable").astype(np.int64)
+    else:
+        pool = total
+        perm = np.arange(pool, dtype=np.int64)
+    pos = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[pos:pos + n]
+        pos += int(n)
+    spare = sorted(int(p) for p in perm[pos:])
+    return PageLayout(pool, bt, need.astype(np.int64), spare)
+
+
+def _kv_index(w: Workload, b: int, pos0: int, npos: int, device) -> torch.Tensor:
+    p = torch.arange(pos0, pos0 + npos, dtype=torch.int64, device=device)
+    h = torch.arange(w.num_kv_heads, dtype=torch.int64, device=device)
+    d = torch.arange(w.head_dim, dtype=torch.int64, device=device)
+    return (((b * MAXPOS + p)[:, None, None] * w.num_kv_heads + h[None, :, None]) * w.head_dim
+            + d[None, None, :])
+
+
+def gen_kv(w: Workload, b: int, pos0: int, npos: int, device="cpu"):
+    """bf16 K and V of sequence ``b`` at positions [pos0, pos0+npos): [npos][n_kv][d] each."""
+    idx = _kv_index(w, b, pos0, npos, device)
+    outl = outlier_channels(w.seed, w.head_dim, w.n_outliers)
+    k = _scaled_bf16(normal(w.seed, T_K, idx), w.sigma_k, outl, w.outlier_mult)
+    v = _scaled_bf16(normal(w.seed, T_V, idx), w.sigma_v, None, 1.0)
+    return k, v
+
+
+def gen_new_kv(w: Workload, b: int, npos: int = 1, device="cpu"):
+    """bf16 K/V rows for freshly decoded tokens (a separate stream from the context)."""
+    idx = _kv_index(w, b, 0, npos, device)
+    outl = outlier_channels(w.seed, w.head_dim, w.n_outliers)
+    k = _scaled_bf16(normal(w.seed, T_KNEW, idx), w.sigma_k, outl, w.outlier_mult)
+    v = _scaled_bf16(normal(w.seed, T_VNEW, idx), w.sigma_v, None, 1.0)
+    return k, v
+
+
+def gen_q(w: Workload, device="cpu", batch: Optional[int] = None) -> torch.Tensor:
+    """bf16 decode queries [B][Hq][d] ~ N(0, 1)."""
+    bsz = w.batch if batch is None else batch
+    n = bsz * w.num_q_heads * w.head_dim
+    idx = torch.arange(n, dtype=torch.int64, device=device)
+    return normal(w.seed, T_Q, idx).to(torch.bfloat16).reshape(bsz, w.num_q_heads, w.head_dim)

@@ -1,0 +1,416 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print (tests/golden/), closed forms, library routines that implement
+the same definition independently (torch's float8_e4m3fn / bfloat16 casts,
+numpy's float16 cast, torch's scaled_dot_product_attention), invariants and
+brute force on small inputs.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "kv_size_examples.json")
+
+
+# ----------------------------------------------------------------- P1 sizes
+def test_kv_size_worked_examples(oracle):
+    g = json.load(open(GOLDEN))
+    for ex in g["examples"]:
+        b = oracle.kv_bytes(ex["layers"], ex["kv_heads"], ex["head_dim"], ex["seq_len"], ex["batch"],
+                            ex["bytes_per_elem"])
+        assert abs(b / ex["unit_bytes"] - ex["printed"]) <= ex["abs_tol"], (ex["name"], b)
+
+
+def test_kv_size_linear_and_fractions(oracle):
+    g = json.load(open(GOLDEN))
+    bpe = g["bytes_per_element"]
+    base = oracle.kv_bytes(80, 8, 128, 32768, 1, bpe["FP16"])
+    # linear in every factor
+    assert oracle.kv_bytes(80, 8, 128, 65536, 1, 2) == 2 * base
+    assert oracle.kv_bytes(80, 8, 128, 32768, 3, 2) == 3 * base
+    # FP8 = half, INT4 = a quarter, INT2 = an eighth of 16-bit storage
+    frac = g["fraction_of_bf16"]
+    assert oracle.kv_bytes(80, 8, 128, 32768, 1, bpe["FP8"]) / base == frac["FP8"]
+    assert oracle.kv_bytes(80, 8, 128, 32768, 1, bpe["INT4"]) / base == frac["INT4"]
+    assert oracle.kv_bytes(80, 8, 128, 32768, 1, bpe["INT2"]) / base == 0.125
+
+
+# ----------------------------------------------------------------- bf16 / fp16
+def test_bf16_rne_matches_torch(oracle):
+    rng = np.random.default_rng(7)
+    # random magnitudes plus exact ties (low 16 bits = 0x8000) and near-ties
+    bits = rng.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[((bits >> 23) & 0xFF) != 0xFF]            # finite only
+    ties = (bits & 0xFFFF0000) | 0x8000
+    near = (bits & 0xFFFF0000) | 0x7FFF
+    allb = np.concatenate([bits, ties, near]).astype(np.uint32)
+    f = allb.view(np.float32)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    L = oracle.lib()
+    got = np.array([L.kvqo_bf16_rne(float(x)) for x in f[:20000]], dtype=np.uint16)
+    assert np.array_equal(got, ref[:20000])
+    got_t = np.array([L.kvqo_bf16_rne(float(x)) for x in f[len(bits):len(bits) + 20000]], dtype=np.uint16)
+    assert np.array_equal(got_t, ref[len(bits):len(bits) + 20000])
+
+
+def test_bf16_directed_rounding_brackets(oracle):
+    """up(f) is the smallest bf16 >= f and down(f) the largest bf16 <= f."""
+    L = oracle.lib()
+    rng = np.random.default_rng(8)
+    bits = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[((bits >> 23) & 0xFF) < 0xFE]
+    for x in bits.view(np.float32)[:5000]:
+        x = float(x)
+        up, dn = L.kvqo_bf16_up(x), L.kvqo_bf16_down(x)
+        vu, vd = float(L.kvqo_bf16_value(up)), float(L.kvqo_bf16_value(dn))
+        assert vd <= x <= vu
+        if vu != x:
+            # the two results are adjacent bf16 values: nothing representable in between
+            assert vd != x
+            assert abs(int(up) - int(dn)) == 1 or (up & 0x7FFF) == 0 or (dn & 0x7FFF) == 0
+    # exact values are fixed points; zero stays zero
+    for x in (0.0, 1.0, -2.5, 448.0, 3.0 / 256):
+        assert L.kvqo_bf16_up(x) == L.kvqo_bf16_down(x) == L.kvqo_bf16_rne(x)
+
+
+def test_f16_rne_matches_numpy(oracle):
+    rng = np.random.default_rng(9)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * 3.0,
+        rng.standard_normal(5000) * 1e-5,                # subnormal range
+        np.ldexp(rng.integers(0, 2**12, 5000).astype(np.float64) + 0.5, -24),  # exact ties in subnormals
+        np.array([65504.0, 65519.9, 65520.0, -0.0, 0.0]),
+    ])
+    bf16 = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_to_f16_bits(bf16)
+    ref = oracle.bf16_value(bf16).astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+    L = oracle.lib()
+    for v in vals[-5000:]:
+        assert L.kvqo_f16_rne(float(v)) == np.float16(v).view(np.uint16)
+
+
+# ----------------------------------------------------------------- P2 E4M3 decode
+def test_e4m3_decode_table_matches_torch(oracle):
+    tab = oracle.e4m3_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(tab), nan)
+    assert np.array_equal(tab[~nan], ref[~nan])
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+
+
+def test_e4m3_decode_landmarks(oracle):
+    g = json.load(open(GOLDEN))["e4m3"]
+    tab = oracle.e4m3_table()
+    assert tab[0x7E] == g["max_finite"] and tab[0xFE] == -g["max_finite"]
+    assert tab[0x08] == g["min_normal"]
+    assert tab[0x01] == g["min_subnormal"]
+    assert tab[0x00] == 0.0 and math.copysign(1, tab[0x80]) == -1.0
+    pos = tab[:0x7F]
+    assert np.all(np.diff(pos) > 0)                        # strictly increasing codes 0..0x7E
+    assert np.array_equal(tab[0x80:0xFF], -pos)            # sign-magnitude
+    # 3 mantissa bits: 8 equally spaced values per binade
+    for e in range(1, 15):
+        seg = pos[e * 8:(e + 1) * 8]
+        assert np.allclose(np.diff(seg), seg[0] / 8)
+
+
+# ----------------------------------------------------------------- P3 E4M3 encode
+def test_e4m3_roundtrip(oracle):
+    tab = oracle.e4m3_table()
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    enc = oracle.e4m3_encode(tab[codes].astype(np.float32))
+    assert np.array_equal(enc, codes)
+
+
+def _nearest_e4m3(y: np.ndarray, tab: np.ndarray) -> np.ndarray:
+    """Independent search: nearest finite E4M3 value, ties to even code, saturating."""
+    codes = np.array([c for c in range(0x7F)], dtype=np.int64)            # 0..0x7E
+    vals = tab[codes]
+    a = np.abs(y.astype(np.float64))
+    a = np.minimum(a, 448.0)
+    dist = np.abs(a[:, None] - vals[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    cand = dist == best
+    # among tied candidates prefer the even mantissa (even code)
+    pick = np.where(cand & (codes[None, :] % 2 == 0), codes[None, :], 10**6).min(axis=1)
+    single = np.where(cand, codes[None, :], 10**6).min(axis=1)
+    pick = np.where(cand.sum(axis=1) > 1, pick, single)
+    sign = np.signbit(y).astype(np.int64) * 0x80
+    return (pick | sign).astype(np.uint8)
+
+
+def test_e4m3_encode_brute_force(oracle):
+    tab = oracle.e4m3_table()
+    rng = np.random.default_rng(11)
+    pos = tab[:0x7F]
+    mids = (pos[1:] + pos[:-1]) / 2
+    m32 = mids.astype(np.float32)
+    ulp_up = np.nextafter(m32, np.float32(np.inf))
+    ulp_dn = np.nextafter(m32, np.float32(-np.inf))
+    samples = np.concatenate([
+        m32, ulp_up, ulp_dn, pos.astype(np.float32),
+        (rng.standard_normal(50000) * 60).astype(np.float32),
+        np.ldexp(rng.random(50000), rng.integers(-14, 10, 50000)).astype(np.float32),
+        np.array([448.0, 464.0, 1e30, np.inf, 447.99, 2.0**-10, 2.0**-10 * 1.0000001], dtype=np.float32),
+    ])
+    samples = np.concatenate([samples, -samples])
+    got = oracle.e4m3_encode(samples)
+    ref = _nearest_e4m3(samples, tab)
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_encode_matches_torch_exhaustive_range(oracle):
+    """All float32 bit patterns with |y| in [2^-12, 448) vs torch's float8_e4m3fn cast.
+
+    torch rounds to nearest-even; it produces NaN (not saturation) above the
+    largest finite value, so that region is checked by the brute-force test.
+    """
+    lo = np.array([2.0**-12], dtype=np.float32).view(np.uint32)[0]
+    hi = np.array([448.0], dtype=np.float32).view(np.uint32)[0]
+    step = 1 << 24
+    for start in range(int(lo), int(hi), step):
+        n = min(step, int(hi) - start)
+        got = oracle.e4m3_encode_range(start, n)
+        y = torch.arange(start, start + n, dtype=torch.int64).to(torch.int32).view(torch.float32)
+        ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(got, ref), start
+        neg = torch.neg(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(got | 0x80, neg), start
+
+
+def test_e4m3_encode_monotone(oracle):
+    y = np.linspace(-500, 500, 200001).astype(np.float32)
+    tab = oracle.e4m3_table()
+    v = tab[oracle.e4m3_encode(y)]
+    assert np.all(np.diff(v) >= 0)
+
+
+# ----------------------------------------------------------------- P4 FP8 quantizer
+def _bf16(x) -> np.ndarray:
+    return torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_fp8_quantizer_bounds(oracle):
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((2000, 128)).astype(np.float32)
+    x[:, [3, 50, 77, 120]] *= 20.0
+    xb = _bf16(x)
+    codes, s, _ = oracle.quantize_rows(oracle.FP8, oracle.PER_TOKEN_HEAD, xb)
+    xv = oracle.bf16_value(xb).astype(np.float64)
+    sv = oracle.bf16_value(s).astype(np.float64)[:, None]
+    xh = oracle.dequantize_rows(oracle.FP8, codes, s)
+    assert np.all(np.abs(xv) / sv <= 448.0)                # per-row scale: nothing saturates
+    err = np.abs(xv - xh)
+    assert np.all(err <= np.maximum(2.0**-4 * np.abs(xv), 2.0**-10 * sv))
+    # the scale is the bf16 ceiling of amax/448 (outward rounding: >= exact ratio, < one bf16 step above)
+    amax = np.abs(xv).max(axis=1, keepdims=True)
+    assert np.all(sv >= amax / 448.0)
+    assert np.all(sv <= amax / 448.0 * (1 + 2.0**-7))
+
+
+def test_fp8_exactly_representable_rows_roundtrip(oracle):
+    rng = np.random.default_rng(13)
+    tab = oracle.e4m3_table()
+    for _ in range(200):
+        s = 2.0 ** int(rng.integers(-12, 4))
+        c = rng.integers(0, 0x7F, 128).astype(np.uint8) | (rng.integers(0, 2, 128).astype(np.uint8) << 7)
+        c[0] = 0x7E                                        # the row max is 448*s
+        x = (s * tab[c]).astype(np.float32)
+        codes, sc, _ = oracle.quantize_rows(oracle.FP8, oracle.PER_TOKEN_HEAD, _bf16(x)[None])
+        assert oracle.bf16_value(sc)[0] == s
+        assert np.array_equal(codes[0], c)
+
+
+def test_fp8_zero_row_and_static_saturation(oracle):
+    codes, s, _ = oracle.quantize_rows(oracle.FP8, oracle.PER_TOKEN_HEAD, np.zeros((1, 128), np.uint16))
+    assert s[0] == 0 and not codes.any()
+    x = _bf16(np.array([[1000.0, -1000.0, 0.5] + [0.0] * 125], dtype=np.float32))
+    c, _, _ = oracle.quantize_rows(oracle.FP8, oracle.PER_TENSOR, x, _bf16(np.float32(1.0)))
+    assert c[0, 0] == 0x7E and c[0, 1] == 0xFE and c[0, 2] == 0x30
+
+
+def test_per_token_beats_static_per_head_on_outliers(oracle):
+    """Per-(token, head) scales lose less than one static per-head scale when a
+    few tokens carry large values (the failure mode the formats notes of the
+    molayo1419.me page describe for per-head / per-tensor scaling)."""
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((512, 128)).astype(np.float32)
+    x[::37] *= 50.0                                        # a few outlier tokens
+    xb = _bf16(x)
+    xv = oracle.bf16_value(xb).astype(np.float64)
+    c1, s1, _ = oracle.quantize_rows(oracle.FP8, oracle.PER_TOKEN_HEAD, xb)
+    e1 = np.abs(oracle.dequantize_rows(oracle.FP8, c1, s1) - xv).mean()
+    stat = oracle.lib().kvqo_bf16_up(float(np.abs(xv).max() / 448.0))
+    c2, s2, _ = oracle.quantize_rows(oracle.FP8, oracle.PER_HEAD, xb, np.uint16(stat))
+    e2 = np.abs(oracle.dequantize_rows(oracle.FP8, c2, s2) - xv).mean()
+    assert e1 < e2
+
+
+# ----------------------------------------------------------------- P5 INT8 / INT4
+def test_int8_error_bound_and_nearest_code(oracle):
+    rng = np.random.default_rng(15)
+    x = (rng.standard_normal((3000, 128)) * 1.5).astype(np.float32)
+    x[::7] += 5.0
+    xb = _bf16(x)
+    codes, s, z = oracle.quantize_rows(oracle.INT8, oracle.PER_TOKEN_HEAD, xb)
+    xv = oracle.bf16_value(xb).astype(np.float64)
+    sv = oracle.bf16_value(s).astype(np.float64)[:, None]
+    zv = oracle.bf16_value(z).astype(np.float64)[:, None]
+    xh = oracle.dequantize_rows(oracle.INT8, codes, s, z)
+    assert np.allclose(xh, codes * sv + zv, rtol=0, atol=0)
+    assert np.all(np.abs(xv - xh) <= sv * (0.5 + 2.0**-12))
+    # z is the row minimum and maps to code 0; the bf16 ceiling of the step is at
+    # most 2^-7 above (max - min)/255, so the maximum lands on 253, 254 or 255
+    assert np.array_equal(zv[:, 0], xv.min(axis=1))
+    assert np.all(codes[np.arange(len(x)), xv.argmin(axis=1)] == 0)
+    assert np.all(codes[np.arange(len(x)), xv.argmax(axis=1)] >= 253)
+    # brute force over all 256 codes: the chosen one is (one of) the nearest
+    grid = np.arange(256, dtype=np.float64)
+    for r in range(0, 3000, 97):
+        d = np.abs(xv[r][:, None] - (grid[None, :] * sv[r] + zv[r]))
+        chosen = d[np.arange(128), codes[r]]
+        assert np.all(chosen <= d.min(axis=1) + sv[r] * 2.0**-12)
+
+
+def test_int8_constant_row(oracle):
+    xb = _bf16(np.full((1, 128), 0.75, np.float32))
+    codes, s, z = oracle.quantize_rows(oracle.INT8, oracle.PER_TOKEN_HEAD, xb)
+    assert s[0] == 0 and not codes.any()
+    assert oracle.dequantize_rows(oracle.INT8, codes, s, z)[0, 0] == 0.75
+
+
+def test_int4_asym_bound(oracle):
+    rng = np.random.default_rng(16)
+    for _ in range(300):
+        x = (rng.standard_normal(32) * rng.choice([1, 20])).astype(np.float16).astype(np.float32)
+        c, s, z = oracle.uint_asym(x, 15)
+        sv, zv = float(oracle.bf16_value([s])[0]), float(oracle.bf16_value([z])[0])
+        assert zv <= x.min() and c.max() <= 15
+        assert np.all(np.abs(x - (c * sv + zv)) <= sv * (0.5 + 2.0**-12))
+        grid = np.arange(16) * sv + zv
+        d = np.abs(x[:, None].astype(np.float64) - grid[None, :])
+        assert np.all(d[np.arange(32), c] <= d.min(axis=1) + sv * 2.0**-12)
+
+
+def test_kivi_window_rule(oracle):
+    # tokens leave the fp16 window in whole 32-token groups once more than 128 are held
+    assert oracle.kivi_quantized_count(131072, 128, 32) == 130944
+    assert 131072 - oracle.kivi_quantized_count(131072, 128, 32) == 128
+    assert oracle.kivi_quantized_count(127, 128, 32) == 0
+    assert oracle.kivi_quantized_count(159, 128, 32) == 0
+    assert oracle.kivi_quantized_count(160, 128, 32) == 32
+    for T in range(0, 1000, 7):
+        nq = oracle.kivi_quantized_count(T, 128, 32)
+        assert nq % 32 == 0 and (T < 128 or 128 <= T - nq < 160)
+
+
+def test_kivi_groups_per_channel_and_per_token(oracle):
+    """K statistics run along tokens (one (s, z) per channel per group); V along channels."""
+    rng = np.random.default_rng(17)
+    T, n = 200, 128
+    k = (rng.standard_normal((T, n)) * np.where(np.arange(n) % 31 == 0, 20, 1)).astype(np.float16)
+    v = rng.standard_normal((T, n)).astype(np.float16)
+    st = oracle.kivi_stream(k.view(np.uint16), v.view(np.uint16), 128, 32)
+    assert st["nq"] == 64 and st["k_s"].shape == (2, n) and st["v_s"].shape == (64,)
+    kh, vh = oracle.kivi_dequant(st, 32)
+    ks = np.repeat(oracle.bf16_value(st["k_s"]), 32, axis=0)
+    assert np.all(np.abs(kh[:64] - k[:64].astype(np.float64)) <= ks * (0.5 + 2.0**-12))
+    vs = oracle.bf16_value(st["v_s"])[:, None]
+    assert np.all(np.abs(vh[:64] - v[:64].astype(np.float64)) <= vs * (0.5 + 2.0**-12))
+    assert np.array_equal(kh[64:], k[64:].astype(np.float64))         # window kept exactly
+    # an outlier channel gets its own, larger step; ordinary channels are not widened by it
+    assert ks[0, 0] > 5 * np.median(ks[0])
+
+
+# ----------------------------------------------------------------- P6 attention
+def _sdpa(q, k, v, scale):
+    """torch reference in fp64; GQA by repeating KV heads."""
+    Hq, d = q.shape
+    T, n_kv, _ = k.shape
+    G = Hq // n_kv
+    kk = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(G, 0)      # [Hq][T][d]
+    vv = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(G, 0)
+    qq = torch.from_numpy(q)[:, None, :]                                    # [Hq][1][d]
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale)
+    return o[:, 0, :].numpy()
+
+
+def test_attention_matches_torch_sdpa(oracle):
+    rng = np.random.default_rng(18)
+    for (T, Hq, n_kv, d) in [(1, 4, 4, 8), (3, 8, 2, 4), (37, 8, 2, 16), (300, 16, 4, 32)]:
+        q = rng.standard_normal((Hq, d))
+        k = rng.standard_normal((T, n_kv, d)) * 2
+        v = rng.standard_normal((T, n_kv, d))
+        scale = float(np.float32(1 / math.sqrt(d)))
+        out, lse = oracle.attention(q, k, v, scale)
+        assert np.allclose(out, _sdpa(q, k, v, scale), rtol=1e-12, atol=1e-12)
+        G = Hq // n_kv
+        sc = np.einsum("hd,thd->ht", q, np.repeat(k, G, axis=1)) * scale
+        assert np.allclose(lse, np.log(np.exp(sc).sum(axis=1)), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_special_cases(oracle):
+    rng = np.random.default_rng(19)
+    d = 128
+    v = rng.standard_normal((1, 2, d))
+    q = rng.standard_normal((8, d))
+    k = rng.standard_normal((1, 2, d))
+    out, _ = oracle.attention(q, k, v, 0.088)
+    assert np.array_equal(out[:4], np.repeat(v[0, :1], 4, 0)) and np.array_equal(out[4:], np.repeat(v[0, 1:], 4, 0))
+    # q = 0 -> plain mean of the values
+    k = rng.standard_normal((50, 2, d)); v = rng.standard_normal((50, 2, d))
+    out, lse = oracle.attention(np.zeros((2, d)), k, v, 0.1)
+    assert np.allclose(out, v.mean(axis=0), atol=1e-14) and np.allclose(lse, math.log(50))
+    # two tokens: p0 = 1 / (1 + exp(s1 - s0))
+    k2 = rng.standard_normal((2, 1, d)); v2 = rng.standard_normal((2, 1, d)); q2 = rng.standard_normal((1, d))
+    s0, s1 = 0.05 * (q2[0] @ k2[0, 0]), 0.05 * (q2[0] @ k2[1, 0])
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    out, _ = oracle.attention(q2, k2, v2, 0.05)
+    assert np.allclose(out[0], p0 * v2[0, 0] + (1 - p0) * v2[1, 0], atol=1e-14)
+    # one dominant score picks its value row
+    k3 = np.zeros((5, 1, d)); k3[2, 0, 0] = 1e4
+    out, _ = oracle.attention(np.eye(1, d), k3, v2.repeat(3, 0)[:5], 1.0)
+    assert np.array_equal(out[0], v2.repeat(3, 0)[2, 0])
+    # empty context
+    out, lse = oracle.attention(q, np.zeros((0, 2, d)), np.zeros((0, 2, d)), 0.1)
+    assert not out.any() and np.all(np.isneginf(lse))
+
+
+def test_attention_gqa_equals_expanded_mha(oracle):
+    rng = np.random.default_rng(20)
+    q = rng.standard_normal((16, 32)); k = rng.standard_normal((40, 2, 32)); v = rng.standard_normal((40, 2, 32))
+    a, la = oracle.attention(q, k, v, 0.2)
+    b, lb = oracle.attention(q, np.repeat(k, 8, axis=1), np.repeat(v, 8, axis=1), 0.2)
+    assert np.allclose(a, b, atol=1e-14) and np.allclose(la, lb, atol=1e-13)
+
+
+def test_lse_merge_reproduces_unsplit(oracle):
+    rng = np.random.default_rng(21)
+    d, T = 64, 500
+    q = rng.standard_normal((1, d)); k = rng.standard_normal((T, 1, d)) * 3; v = rng.standard_normal((T, 1, d))
+    full, lfull = oracle.attention(q, k, v, 0.125)
+    for _ in range(10):
+        cuts = np.sort(rng.choice(np.arange(1, T), size=rng.integers(1, 8), replace=False))
+        bounds = [0] + list(cuts) + [T]
+        os_, ls = [], []
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            o, l = oracle.attention(q, k[a:b], v[a:b], 0.125)
+            os_.append(o[0]); ls.append(l[0])
+        m, lm = oracle.lse_merge(np.array(os_), np.array(ls))
+        assert np.allclose(m, full[0], atol=1e-12) and abs(lm - lfull[0]) < 1e-12
+
+
+def test_decode_reference_context_one_returns_value_row(oracle):
+    rng = np.random.default_rng(22)
+    kb = _bf16(rng.standard_normal((1, 2, 128))); vb = _bf16(rng.standard_normal((1, 2, 128)))
+    qb = _bf16(rng.standard_normal((8, 128)))
+    for dt in (oracle.FP8, oracle.INT8):
+        r = oracle.decode_reference(qb, kb, vb, dt)
+        assert np.array_equal(r["out"][:4], np.repeat(r["v_hat"][0, :1], 4, 0))
