@@ -1,0 +1,255 @@
+"""Benchmark of the paged FP8 / INT8 KV-cache decode step on one MI355X.
+
+One step = the whole hot path for one decode token per sequence:
+  kvq_append (quantize the new K/V row into its page slot)
+  + split-K decode attention over the quantized paged cache
+  + log-sum-exp merge of the partial results.
+Inputs are seeded synthetic tensors (``synthetic.py``) with the workload's
+shapes, resident in HBM before timing starts.
+
+    python bench.py [--config llama8b] [--steps 100] [--warmup 10]
+
+Prints one JSON line.  ``value`` is algorithmic bytes of the step / step time
+(GB/s); ``roofline`` reports the split-K decode kernel (the dominant one)
+against the 8 TB/s HBM peak with per-launch HIP-event timing; ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DECODE_SRC = os.path.join(ROOT, "quantized_kv_cache_08_amd", "csrc", "decode.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama8b", choices=["tiny", "llama8b", "llama70b", "mixed"])
+    ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto)")
+    ap.add_argument("--partition-pages", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU work budget for the oracle sample")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.dirname(DECODE_SRC))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(os.path.dirname(DECODE_SRC), f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(w, lens: np.ndarray):
+    """Algorithmic bytes of one step, split by kernel."""
+    n_kv, d, Hq = w.num_kv_heads, w.head_dim, w.num_q_heads
+    meta = 2 if w.dtype == "fp8" else 4            # bf16 scale (+ bf16 zero-point) per (token, head)
+    tokens = int(lens.sum())
+    B = len(lens)
+    pages = int(((lens + w.page_size - 1) // w.page_size).sum())
+    kv = tokens * n_kv * 2 * (d + meta)
+    split = kv + pages * 4 + B * Hq * d * 2        # K/V codes+scales, block-table entries, q
+    reduce = B * Hq * d * 4                        # out (fp32)
+    append = B * n_kv * 2 * (d * 2 + d + meta) + B * 4
+    return dict(kv=kv, split=split, reduce=reduce, append=append, total=split + reduce + append,
+                tokens=tokens, pages=pages)
+
+
+def slots_for(layout, b: int, pos0: int, n: int, ps: int):
+    import torch
+    pos = np.arange(pos0, pos0 + n, dtype=np.int64)
+    pages = layout.block_table[b, pos // ps].astype(np.int64)
+    return torch.from_numpy((pages * ps + pos % ps).astype(np.int32)).cuda()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The CPU oracle (as it stands) on a bounded sample of the workload:
+    quantize-on-store of the sampled sequences plus fp64 decode attention."""
+    import torch
+    import synthetic
+    from oracle import oracle as O
+
+    lens = synthetic.seq_lens(w)
+    order = list(range(len(lens)))
+    dt = O.FP8 if w.dtype == "fp8" else O.INT8
+    q_all = synthetic.gen_q(w, "cpu")
+    done, t_total, sample = [], 0.0, []
+    for b in order:
+        T = int(lens[b])
+        k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
+        kb = k.view(torch.int16).numpy().view(np.uint16)
+        vb = v.view(torch.int16).numpy().view(np.uint16)
+        qb = q_all[b].contiguous().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        O.decode_reference(qb, kb, vb, dt)
+        t_total += time.perf_counter() - t0
+        done.append(T)
+        if t_total >= budget_s or len(done) >= len(lens):
+            break
+    sl = np.array(done)
+    by = step_bytes(w, sl)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(by["kv"] / t_total / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(done)} of {len(lens)} sequences ({int(sl.sum())} tokens): quantize-on-store of "
+                      f"their K/V plus fp64 attention, {t_total:.1f} s; value = their K/V code+scale bytes / time",
+            "tokens_per_s": round(len(done) / t_total, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "single-GPU build: this benchmark runs on one GPU only",
+                          "requested_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    import quantized_kv_cache_08_amd as kvq
+    import synthetic
+
+    if args.copy_calib_mib:
+        copy_calibration(args.copy_calib_mib)
+        return
+
+    torch.cuda.set_device(0)
+    w = synthetic.WORKLOADS[args.config]
+    lens = synthetic.seq_lens(w)
+    B, Hq, d = len(lens), w.num_q_heads, w.head_dim
+    by = step_bytes(w, lens)
+    reps = args.replicas or (2 if by["kv"] < (1 << 30) else 1)
+
+    # each cache replica holds the context minus the newest token (pages laid
+    # out for the full length); every step appends that token, then decodes
+    full_layout = synthetic.page_layout(w, lens)
+    caches = []
+    for r in range(reps):
+        code = kvq.KVQ_FP8_E4M3 if w.dtype == "fp8" else kvq.KVQ_INT8_ASYM
+        cache = kvq.Cache(code, full_layout.num_pages, w.num_kv_heads, w.page_size, d)
+        for b, n in enumerate(lens):
+            m = int(n) - 1
+            for p0 in range(0, m, 1 << 16):
+                mm = min(1 << 16, m - p0)
+                k, v = synthetic.gen_kv(w, b, p0, mm, "cuda")
+                kvq.append(cache, k, v, slots_for(full_layout, b, p0, mm, w.page_size))
+        caches.append(cache)
+    bt_dev = torch.from_numpy(full_layout.block_table).cuda()
+    cl_dev = torch.from_numpy(lens.astype(np.int32)).cuda()
+    q = synthetic.gen_q(w, "cuda")
+    knew = torch.empty(B, w.num_kv_heads, d, dtype=torch.bfloat16, device="cuda")
+    vnew = torch.empty_like(knew)
+    for b in range(B):
+        kk, vv = synthetic.gen_new_kv(w, b, 1, "cuda")
+        knew[b], vnew[b] = kk[0], vv[0]
+    pos = lens - 1
+    slot = (full_layout.block_table[np.arange(B), pos // w.page_size].astype(np.int64) * w.page_size
+            + pos % w.page_size).astype(np.int32)
+    slot_dev = torch.from_numpy(slot).cuda()
+    max_ctx = int(lens.max())
+    ws_bytes = kvq.decode_workspace_bytes(caches[0], B, Hq, max_ctx, args.partition_pages)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c = caches[i % reps]
+        if ev is not None:
+            ev[0].record()
+        kvq.append(c, knew, vnew, slot_dev)
+        if ev is not None:
+            ev[1].record()
+        kvq.decode_split(c, q, bt_dev, cl_dev, max_ctx, scale, ws, out, None, args.partition_pages)
+        if ev is not None:
+            ev[2].record()
+        kvq.decode_reduce(c, B, Hq, max_ctx, ws, out, None, args.partition_pages)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    t_app = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    t_split = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    t_red = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    value = by["total"] / (ms_step * 1e-3) / 1e9
+    split_gbs = by["split"] / (t_split.mean() * 1e-3) / 1e9
+    attn_ms = t_split.mean() + t_red.mean()
+    kv_gbs = (by["split"] + by["reduce"]) / (attn_ms * 1e-3) / 1e9
+
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", f"traffic_split_{args.config}.json")
+    if os.path.exists(tf):
+        t = json.load(open(tf))
+        if t.get("source_hash") == source_hash():
+            traffic = t.get("bytes_per_launch")
+
+    res = {
+        "metric": "paged FP8/INT8 decode-attn KV GB/s (% of HBM peak) + tokens/s at 1 GPU",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "int8": "u8"}[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "batch": B, "num_q_heads": Hq,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": d, "page_size": w.page_size,
+                   "context_tokens": by["tokens"], "max_context": max_ctx, "cache_replicas": reps,
+                   "partition_pages": args.partition_pages or "auto"},
+        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "decode_attention_kv_gbs": round(kv_gbs, 2),
+        "pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+        "kernel_ms": {"append": round(float(t_app.mean()), 5), "split": round(float(t_split.mean()), 5),
+                      "reduce": round(float(t_red.mean()), 5),
+                      "split_p50": round(float(np.median(t_split)), 5),
+                      "split_p95": round(float(np.percentile(t_split, 95)), 5)},
+        "algorithmic_bytes": {k: by[k] for k in ("kv", "split", "reduce", "append", "total")},
+        "roofline": {"bound": "hbm", "kernel": "split_kernel (paged split-K decode attention)",
+                     "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "source_hash": source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

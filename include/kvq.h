@@ -1,0 +1,181 @@
+/*
+ * kvq.h -- paged FP8 / INT8 (and KIVI-style INT4) KV cache for MI355X (gfx950).
+ *
+ * C ABI of libkvq.so.  Every pointer argument except `cache` and `bytes` is a
+ * DEVICE pointer owned by the caller; the library never allocates, frees or
+ * synchronises.  All work is enqueued on the caller's HIP stream.  Scalars are
+ * validated on the host before any HIP call; an invalid request returns a
+ * kvq_status other than KVQ_OK and launches nothing.  The contents of device
+ * arrays (slot mappings, block tables, context lengths) are the caller's
+ * contract and are not read by the host.
+ *
+ * What the calls compute (pages cited by title and section):
+ *  - The KV cache is re-read in full at every decode step and keeps growing by
+ *    one K/V row per token ("KV cache FP8로 동시 요청 76배 수용하기",
+ *    storycompiler.tistory.com, sections 1-2).
+ *  - Quantization happens once, when a token's K/V row is stored, from the
+ *    full-precision values; the scales are kept in BF16 next to the codes, and
+ *    dequantization is fused into the attention kernel, whose arithmetic stays
+ *    in high precision ("KV 캐시 양자화(KV cache quantization): FP8/INT8 K 및 V가
+ *    실제로 제공하는 이점과 한계점", molayo1419.me, section "KV 캐시 양자화란
+ *    실제로 무엇인가"; "KV Cache 압축", ryotta.opik.net, sections 5.1 and 6.3).
+ *  - Formats: FP8 E4M3 and INT8 per-token asymmetric with a (scale,
+ *    zero_point) pair; per-tensor and per-head static scales (molayo1419.me,
+ *    formats table notes; ryotta.opik.net section 3.1).  KIVI: K quantized per
+ *    channel, V per token, the most recent tokens kept in full precision
+ *    (ryotta.opik.net section 3.1, KIVI; molayo1419.me formats notes on mixed
+ *    4-bit).
+ *  - Storage is paged: fixed-size blocks in one pool, mapped per request by a
+ *    block table ("FP8 KV Cache부터 INT4 Weight-Only까지", daewooki.github.io,
+ *    core concept 2) PagedAttention).
+ *  - Accumulation is fp32 (storycompiler.tistory.com, section 4).
+ *
+ * Numeric definitions (the pages give no formula; these readings are fixed):
+ *  FP8 per-(token,head):  s = bf16_ceil(amax / 448), code = e4m3_rne_sat(x / s)
+ *  FP8 static:            code = e4m3_rne_sat(x / s_static)
+ *  INT8 per-(token,head): z = bf16_floor(min), s = bf16_ceil((max - z) / 255),
+ *                         code = clamp(rne((x - z) / s), 0, 255), x^ = code*s + z
+ *  KIVI INT4:             the same asymmetric rule with 15 steps; K over the 32
+ *                         tokens of a group per channel, V over the channels of
+ *                         a token.  s == 0 (constant row) gives all-zero codes.
+ *  Every "/" is one IEEE float32 division; E4M3 is the OCP encoding (max 448).
+ *
+ * Page records.  A pool holds num_pages x num_kv_heads records; record
+ * (page p, head h) starts at byte (p * num_kv_heads + h) * kvq_record_bytes().
+ * A record stores, in order:
+ *   page_size rows of head_dim code bytes (token-major; INT4: head_dim/2 bytes
+ *   per row, low nibble = even channel), then
+ *   per-(token,head) modes: page_size bf16 scales, then (INT8) page_size bf16
+ *   zero-points;  KIVI K: head_dim bf16 scales then head_dim bf16 zero-points
+ *   (one per channel for the page's 32-token group);  KIVI V: page_size bf16
+ *   scales then page_size bf16 zero-points;
+ *   padded to a multiple of 16 bytes.
+ * Token t of a sequence lives in page block_table[seq][t / page_size], row
+ * t % page_size.  slot = page * page_size + row.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID = 1,      /* null pointer, negative size, inconsistent descriptor     */
+    KVQ_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the kernels implement      */
+    KVQ_ERR_WORKSPACE = 3,    /* workspace smaller than kvq_decode_workspace_bytes()     */
+    KVQ_ERR_HIP = 4           /* a HIP runtime call or a kernel launch failed            */
+} kvq_status;
+
+typedef enum kvq_dtype {
+    KVQ_FP8_E4M3 = 1,         /* OCP E4M3, 1 byte per element                            */
+    KVQ_INT8_ASYM = 2,        /* u8 code with per-(token,head) scale and zero-point      */
+    KVQ_INT4_KIVI = 3         /* 4-bit codes, K per channel / V per token, fp16 window   */
+} kvq_dtype;
+
+typedef enum kvq_scale_mode {
+    KVQ_SCALE_PER_TENSOR = 0,      /* one static bf16 scale for K and one for V (FP8 only) */
+    KVQ_SCALE_PER_HEAD = 1,        /* one static bf16 scale per KV head for K and V (FP8)  */
+    KVQ_SCALE_PER_TOKEN_HEAD = 2   /* computed at append time per (token, KV head)         */
+} kvq_scale_mode;
+
+/* Descriptor of one layer's cache.  Plain data; the library keeps no copy. */
+typedef struct kvq_cache {
+    int32_t dtype;            /* kvq_dtype                                               */
+    int32_t scale_mode;       /* kvq_scale_mode; INT8 and INT4 need PER_TOKEN_HEAD       */
+    int32_t num_pages;        /* pages in each pool                                      */
+    int32_t page_size;        /* tokens per page: 16 or 32 (INT4: 32 = the group size)   */
+    int32_t num_kv_heads;     /* >= 1                                                    */
+    int32_t head_dim;         /* 128                                                     */
+    void* k_pages;            /* device: num_pages*num_kv_heads K records                */
+    void* v_pages;            /* device: num_pages*num_kv_heads V records                */
+    const void* static_scales;/* device bf16; PER_TENSOR: [2] = {K, V};
+                                 PER_HEAD: [2][num_kv_heads]; otherwise NULL             */
+    /* INT4 (KIVI) only: fp16 recent-token window, a ring of window_tokens rows
+       per (sequence, KV head); token t sits at row t % window_tokens.          */
+    void* k_window;           /* device fp16 [max_seqs][num_kv_heads][window_tokens][head_dim] */
+    void* v_window;
+    int32_t max_seqs;         /* rows of the window arrays                               */
+    int32_t window_tokens;    /* residual + page_size (160 for residual 128, group 32)   */
+    int32_t residual;         /* tokens always kept in fp16 (128)                        */
+    int32_t reserved;
+} kvq_cache;
+
+/* Bytes of one page record: which = 0 for K, 1 for V.  0 for an invalid combination. */
+size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size,
+                        int32_t head_dim, int32_t which);
+
+/* Quantize-on-append (FP8 / INT8).
+ * k, v:          device bf16 [num_tokens][num_kv_heads][head_dim], contiguous.
+ * slot_mapping:  device int32 [num_tokens]; slot = page*page_size + row; a
+ *                negative slot (or one beyond the pool) skips that token.
+ * Writes the token's code row, scale and zero-point into its page record for K
+ * and for V.  Two tokens with the same slot race. */
+kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,
+                      const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
+
+/* Workspace bytes that kvq_decode_attention / kvq_decode_split need for this
+ * shape.  partition_pages as in kvq_decode_attention. */
+kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_context_len,
+                                      int32_t partition_pages, size_t* bytes);
+
+/* One decode step of attention for one query token per sequence, reading the
+ * quantized paged cache (FP8 / INT8) with dequantization fused in:
+ *   out[b][h] = sum_t softmax_t(softmax_scale * q[b][h] . k^[t]) v^[t]
+ * over every cached token t < context_lens[b] of KV head h / (num_q_heads /
+ * num_kv_heads).  fp32 accumulation, flash-decoding split over the context.
+ * q:             device bf16 [num_seqs][num_q_heads][head_dim]
+ * block_table:   device int32 [num_seqs][max_pages_per_seq]
+ * context_lens:  device int32 [num_seqs]; values above max_context_len are
+ *                clamped to it; 0 gives out = 0 and lse = -inf.
+ * max_context_len: host bound on context_lens (<= max_pages_per_seq*page_size).
+ * partition_pages: 0 = balance the work over the resident waves of the device;
+ *                >0 = pages of work per wave (testing and tuning).
+ * workspace:     device scratch of at least kvq_decode_workspace_bytes().
+ * out:           device fp32 [num_seqs][num_q_heads][head_dim]
+ * lse:           device fp32 [num_seqs][num_q_heads] natural-log sum-exp of the
+ *                scaled scores, or NULL.
+ * num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16. */
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t num_seqs,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, float softmax_scale,
+                                int32_t partition_pages, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, hipStream_t stream);
+
+/* The two launches of kvq_decode_attention, exposed separately so that each
+ * kernel can be timed and a context-sharded caller can run the merge itself.
+ * kvq_decode_split writes every (sequence, head) whose context one wave covers
+ * straight to out/lse and the others as partial results into the workspace;
+ * kvq_decode_reduce merges the partial results (log-sum-exp weights).  Call
+ * them in this order on one stream with identical arguments. */
+kvq_status kvq_decode_split(const kvq_cache* cache, const void* q, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t* block_table,
+                            int32_t max_pages_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, float softmax_scale,
+                            int32_t partition_pages, void* workspace, size_t workspace_bytes,
+                            float* out, float* lse, hipStream_t stream);
+kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t max_context_len, int32_t partition_pages,
+                             void* workspace, size_t workspace_bytes,
+                             float* out, float* lse, hipStream_t stream);
+
+/* The FP8 E4M3 encoder of kvq_append applied to n float32 values (nearest-even,
+ * saturating at +-448, sign of zero kept, NaN -> 0x7F).  x: device fp32 [n],
+ * codes: device u8 [n]. */
+kvq_status kvq_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* kvq_status_string(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,194 @@
+"""Paged FP8 / INT8 (and KIVI-style INT4) KV cache for MI355X.
+
+Thin ctypes binding over ``libkvq.so`` (HIP kernels for gfx950, C ABI in
+``include/kvq.h``).  Argument marshalling only: every step of the path runs in
+the library's kernels on the caller's (torch's current) HIP stream.  PyTorch
+provides device memory and streams.  The library must be built
+(``python quantized_kv_cache_08_amd/build.py``); without it every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI",
+    "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
+    "KvqError", "Cache", "lib", "record_bytes", "append", "decode_workspace_bytes",
+    "decode_attention", "decode_split", "decode_reduce", "e4m3_encode", "status_string",
+    "LIB_PATH",
+]
+
+KVQ_FP8_E4M3, KVQ_INT8_ASYM, KVQ_INT4_KIVI = 1, 2, 3
+KVQ_SCALE_PER_TENSOR, KVQ_SCALE_PER_HEAD, KVQ_SCALE_PER_TOKEN_HEAD = 0, 1, 2
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("dtype", _I32), ("scale_mode", _I32), ("num_pages", _I32), ("page_size", _I32),
+        ("num_kv_heads", _I32), ("head_dim", _I32),
+        ("k_pages", _P), ("v_pages", _P), ("static_scales", _P),
+        ("k_window", _P), ("v_window", _P),
+        ("max_seqs", _I32), ("window_tokens", _I32), ("residual", _I32), ("reserved", _I32),
+    ]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+_DECODE_ARGS = [ctypes.POINTER(CacheDesc), _P, _I32, _I32, _P, _I32, _P, _I32, ctypes.c_float, _I32,
+                _P, ctypes.c_size_t, _P, _P, _P]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libkvq.so not built ({LIB_PATH}); run quantized_kv_cache_08_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kvq_record_bytes.restype = ctypes.c_size_t
+        L.kvq_record_bytes.argtypes = [_I32] * 5
+        L.kvq_append.restype = ctypes.c_int
+        L.kvq_append.argtypes = [ctypes.POINTER(CacheDesc), _P, _P, _P, _I32, _P]
+        L.kvq_decode_workspace_bytes.restype = ctypes.c_int
+        L.kvq_decode_workspace_bytes.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+        for fn in ("kvq_decode_attention", "kvq_decode_split"):
+            getattr(L, fn).restype = ctypes.c_int
+            getattr(L, fn).argtypes = _DECODE_ARGS
+        L.kvq_decode_reduce.restype = ctypes.c_int
+        L.kvq_decode_reduce.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32, _P,
+                                        ctypes.c_size_t, _P, _P, _P]
+        L.kvq_e4m3_encode.restype = ctypes.c_int
+        L.kvq_e4m3_encode.argtypes = [_P, _P, ctypes.c_int64, _P]
+        L.kvq_status_string.restype = ctypes.c_char_p
+        L.kvq_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kvq_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise KvqError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def record_bytes(dtype: int, scale_mode: int, page_size: int, head_dim: int, which: int) -> int:
+    return int(lib().kvq_record_bytes(dtype, scale_mode, page_size, head_dim, which))
+
+
+class Cache:
+    """One layer's paged cache: page pools allocated with torch (uint8, device)
+    plus the C descriptor.  ``fill`` initialises the pools with a byte value."""
+
+    def __init__(self, dtype: int, num_pages: int, num_kv_heads: int, page_size: int = 16,
+                 head_dim: int = 128, scale_mode: int = KVQ_SCALE_PER_TOKEN_HEAD,
+                 static_scales: Optional[torch.Tensor] = None, device="cuda", fill: Optional[int] = None,
+                 max_seqs: int = 0, residual: int = 128):
+        self.dtype, self.scale_mode = dtype, scale_mode
+        self.num_pages, self.num_kv_heads = num_pages, num_kv_heads
+        self.page_size, self.head_dim = page_size, head_dim
+        self.rec_k = record_bytes(dtype, scale_mode, page_size, head_dim, 0)
+        self.rec_v = record_bytes(dtype, scale_mode, page_size, head_dim, 1)
+        if self.rec_k == 0 or self.rec_v == 0:
+            raise KvqError("kvq_record_bytes", 1)
+        n = num_pages * num_kv_heads
+        alloc = torch.empty if fill is None else (lambda *a, **k: torch.full(*a, fill, **k))
+        self.k_pages = alloc((n * self.rec_k,), dtype=torch.uint8, device=device)
+        self.v_pages = alloc((n * self.rec_v,), dtype=torch.uint8, device=device)
+        self.static_scales = static_scales
+        self.max_seqs, self.residual = max_seqs, residual
+        self.window_tokens = residual + page_size if dtype == KVQ_INT4_KIVI else 0
+        self.k_window = self.v_window = None
+        if dtype == KVQ_INT4_KIVI and max_seqs > 0:
+            shape = (max_seqs, num_kv_heads, self.window_tokens, head_dim)
+            self.k_window = torch.zeros(shape, dtype=torch.float16, device=device)
+            self.v_window = torch.zeros(shape, dtype=torch.float16, device=device)
+        self.desc = CacheDesc(dtype, scale_mode, num_pages, page_size, num_kv_heads, head_dim,
+                              self.k_pages.data_ptr(), self.v_pages.data_ptr(),
+                              None if static_scales is None else static_scales.data_ptr(),
+                              None if self.k_window is None else self.k_window.data_ptr(),
+                              None if self.v_window is None else self.v_window.data_ptr(),
+                              max_seqs, self.window_tokens, residual, 0)
+
+    def records(self, which: int) -> torch.Tensor:
+        """Pool ``which`` (0 = K, 1 = V) viewed as [num_pages][num_kv_heads][record bytes]."""
+        pool, rec = (self.k_pages, self.rec_k) if which == 0 else (self.v_pages, self.rec_v)
+        return pool.view(self.num_pages, self.num_kv_heads, rec)
+
+
+def append(cache: Cache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Quantize bf16 K/V rows [T][n_kv][d] into their slots (kvq_append)."""
+    _check("kvq_append", lib().kvq_append(ctypes.byref(cache.desc), _ptr(k), _ptr(v), _ptr(slot_mapping),
+                                          int(slot_mapping.numel()), _stream(stream)))
+
+
+def decode_workspace_bytes(cache: Cache, num_seqs: int, num_q_heads: int, max_context_len: int,
+                           partition_pages: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check("kvq_decode_workspace_bytes",
+           lib().kvq_decode_workspace_bytes(ctypes.byref(cache.desc), num_seqs, num_q_heads,
+                                            max_context_len, partition_pages, ctypes.byref(out)))
+    return int(out.value)
+
+
+def _decode(fn: str, cache, q, block_table, context_lens, max_context_len, softmax_scale, workspace, out,
+            lse, partition_pages, stream):
+    num_seqs, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    _check(fn, getattr(lib(), fn)(
+        ctypes.byref(cache.desc), _ptr(q), num_seqs, num_q_heads, _ptr(block_table),
+        int(block_table.shape[1]), _ptr(context_lens), int(max_context_len), float(softmax_scale),
+        int(partition_pages), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+        _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def decode_attention(cache: Cache, q, block_table, context_lens, max_context_len: int, softmax_scale: float,
+                     workspace, out, lse=None, partition_pages: int = 0, stream=None) -> None:
+    """One decode step over the quantized paged cache (kvq_decode_attention)."""
+    _decode("kvq_decode_attention", cache, q, block_table, context_lens, max_context_len, softmax_scale,
+            workspace, out, lse, partition_pages, stream)
+
+
+def decode_split(cache: Cache, q, block_table, context_lens, max_context_len: int, softmax_scale: float,
+                 workspace, out, lse=None, partition_pages: int = 0, stream=None) -> None:
+    _decode("kvq_decode_split", cache, q, block_table, context_lens, max_context_len, softmax_scale,
+            workspace, out, lse, partition_pages, stream)
+
+
+def decode_reduce(cache: Cache, num_seqs: int, num_q_heads: int, max_context_len: int, workspace, out,
+                  lse=None, partition_pages: int = 0, stream=None) -> None:
+    _check("kvq_decode_reduce", lib().kvq_decode_reduce(
+        ctypes.byref(cache.desc), num_seqs, num_q_heads, int(max_context_len), int(partition_pages),
+        _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse),
+        _stream(stream)))
+
+
+def e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
+    """float32 -> OCP E4M3 codes with the encoder the append kernel uses."""
+    _check("kvq_e4m3_encode", lib().kvq_e4m3_encode(_ptr(x), _ptr(codes), int(x.numel()), _stream(stream)))

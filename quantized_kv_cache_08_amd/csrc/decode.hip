@@ -1,0 +1,511 @@
+// decode.hip -- paged FP8 / INT8 decode attention with fused dequantization
+// (gfx950), flash-decoding split over the context plus a log-sum-exp merge.
+//
+// What is computed: for each sequence and query head, softmax attention of the
+// one decode query over every cached token, reading the quantized K/V pages
+// through the block table and dequantizing inside the kernel, with fp32
+// accumulation.  A separate dequantization pass would give back the bandwidth
+// saving, so dequantization is fused ("KV Cache 압축", ryotta.opik.net,
+// sections 5.1 and 6.3); the attention arithmetic stays in high precision and
+// only the bytes shrink ("KV 캐시 양자화(KV cache quantization) ...",
+// molayo1419.me, section "KV 캐시 양자화란 실제로 무엇인가" and TL;DR); dot
+// products accumulate in fp32 ("KV cache FP8로 동시 요청 76배 수용하기",
+// storycompiler.tistory.com, section 4); the cache is paged into fixed-size
+// blocks mapped by a per-request table ("FP8 KV Cache부터 INT4 Weight-Only까지",
+// daewooki.github.io, core concept 2).
+//
+// Work decomposition.  Each (sequence, KV head) is an "item" of pages; the
+// items are laid end to end and the resulting page space is cut into equal
+// ranges, one per resident wave (flash-decoding split over context partitions,
+// balanced across the whole batch).  A wave walks its range 32 tokens at a
+// time; where a range covers a whole item the result goes straight to `out`,
+// otherwise a partial (normalised o, log2-sum-exp) goes to the workspace and
+// the reduce kernel merges the partials.
+//
+// Per 32-token chunk and wave (lane l: j = l % 16, g = l / 16):
+//  QK  S^T[token][head] = K[token][:] . Q[head][:] with MFMA 16x16x32 bf16.
+//      K codes convert exactly to bf16 (E4M3 through the hardware converter,
+//      u8 through fp32), q is bf16, so the products are exact; the per-token
+//      scale (and INT8 zero-point times sum(q)) is applied to the fp32 result.
+//      A operand: lane (token j, g) holds channels [32g, 32g+32) of its row,
+//      loaded as two 16-byte vectors; Q (B operand) is permuted to match.
+//  softmax  online, exp2 domain, rescaling only when the running maximum
+//      grows by more than 2^8 (values stay exact to fp32 rounding).
+//  PV  O[head][chan] += P'[head][token] . V[token][chan], P' = p * v_scale
+//      split into bf16 hi + lo (two MFMAs) so P' keeps 16 significant bits.
+//      The QK result layout is already the PV A layout (lane = head, slots =
+//      tokens 4g..4g+3 of each half); V is loaded as 8-byte row pieces
+//      (lane (chan-block j, g): channels 8j..8j+7 of tokens 4g..4g+3) and
+//      transposed in registers with byte permutes before conversion.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+constexpr int kFP8 = 1;
+constexpr int kINT8 = 2;
+constexpr float kRescaleHeadroom = 8.0f;  // log2 units
+
+struct ChunkBuf {
+    u32x4_t k[2][2];   // [half][part]: K channels 32g..32g+15 / +16..+31 of token j
+    u32x2_t v[2][4];   // [half][r]: V channels 8j..8j+7 of token 4g+r
+    u32x2_t ks[2];     // bf16 K scales of tokens 4g..4g+3
+    u32x2_t vs[2];
+    u32x2_t kz[2];     // INT8 zero-points
+    u32x2_t vz[2];
+};
+
+__device__ __forceinline__ int pages_of(int len, int max_ctx, int ps) {
+    len = len < 0 ? 0 : (len > max_ctx ? max_ctx : len);
+    return (len + ps - 1) / ps;
+}
+
+template <int DT, bool STATIC, int PS>
+__device__ __forceinline__ void process_segment(const SplitParams& p, const int b, const int h,
+                                                const int page0, const int page1, const int seg,
+                                                const int n_seg, const int lane) {
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int G = p.group;
+    const int len = min(max(p.context_lens[b], 0), p.max_ctx);
+    const int tok_base = page0 * PS;
+    const int tok_end = min(len, page1 * PS);
+
+    // ---- query operand (B of QK): head j, channels 32g + 8kb + [0, 8)
+    u32x4_t qb[4];
+    float qsum = 0.0f;
+    if (j < G) {
+        const u32x4_t* qp =
+            (const u32x4_t*)(p.q + ((size_t)b * p.n_q + (size_t)h * G + j) * kHeadDim + 32 * g);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qb[kb] = qp[kb];
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qb[kb] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if constexpr (DT == kINT8) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qsum += bf16lo(qb[kb][i]) + bf16hi(qb[kb][i]);
+        qsum += __shfl_xor(qsum, 16);
+        qsum += __shfl_xor(qsum, 32);
+    }
+
+    float k_static = 0.0f, v_static = 0.0f;
+    if constexpr (STATIC) {
+        k_static = bf16lo(p.static_scales[h * p.static_head_stride]) * p.score_scale;
+        v_static = bf16lo(p.static_scales[p.static_kv_stride + h * p.static_head_stride]);
+    }
+
+    f32x4_t acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_used = -INFINITY;
+    float lsum = 0.0f;
+    float pz = 0.0f;
+
+    const int* bt = p.block_table + (size_t)b * p.max_pages_per_seq;
+    const int n_chunks = (PS == 16) ? (page1 - page0 + 1) / 2 : (page1 - page0);
+    int ids_base = page0;
+    int ids = (page0 + lane < page1) ? bt[page0 + lane] : 0;
+
+    auto load = [&](ChunkBuf& cb, const int c) {
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+            const int pidx = (PS == 16) ? page0 + 2 * c + hp : page0 + c;
+            const int tok0 = (PS == 16) ? 0 : 16 * hp;
+            // a 16-token half past the segment (odd page count) is never read
+            const bool live = (PS == 32) || (pidx < page1);
+            if (live && pidx - ids_base >= 64) {
+                ids_base = pidx;
+                ids = (pidx + lane < page1) ? bt[pidx + lane] : 0;
+            }
+            // page ids come from the caller's table: clamp so that a bad entry
+            // reads a wrong page instead of leaving the pool
+            int page = live ? __builtin_amdgcn_readlane(ids, pidx - ids_base) : 0;
+            page = min(max(page, 0), p.num_pages - 1);
+            const uint8_t* krec = p.k_pages + ((size_t)page * p.n_kv + h) * (size_t)p.rec_k;
+            const uint8_t* vrec = p.v_pages + ((size_t)page * p.n_kv + h) * (size_t)p.rec_v;
+            const uint8_t* kr = krec + (tok0 + j) * kHeadDim + 32 * g;
+            const u32x4_t z4 = {0u, 0u, 0u, 0u};
+            const u32x2_t z2 = {0u, 0u};
+            cb.k[hp][0] = live ? *(const u32x4_t*)kr : z4;
+            cb.k[hp][1] = live ? *(const u32x4_t*)(kr + 16) : z4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                cb.v[hp][r] =
+                    live ? *(const u32x2_t*)(vrec + (tok0 + 4 * g + r) * kHeadDim + 8 * j) : z2;
+            if constexpr (!STATIC) {
+                const int so = PS * kHeadDim + 2 * (tok0 + 4 * g);
+                cb.ks[hp] = live ? *(const u32x2_t*)(krec + so) : z2;
+                cb.vs[hp] = live ? *(const u32x2_t*)(vrec + so) : z2;
+                if constexpr (DT == kINT8) {
+                    cb.kz[hp] = live ? *(const u32x2_t*)(krec + so + 2 * PS) : z2;
+                    cb.vz[hp] = live ? *(const u32x2_t*)(vrec + so + 2 * PS) : z2;
+                }
+            }
+        }
+    };
+
+    auto compute = [&](ChunkBuf& cb, const int c) {
+        const int ctok = tok_base + c * 32;
+        const bool tail = ctok + 32 > tok_end;
+        if (tail) {
+            // rows past the end of the context may hold anything (including
+            // E4M3 NaN patterns): clear them before they reach an MFMA
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (ctok + 16 * hp + 4 * g + r >= tok_end) cb.v[hp][r] = u32x2_t{0u, 0u};
+        }
+
+        // ---- QK
+        float sc[2][4];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const u32x4_t src = cb.k[hp][kb >> 1];
+                const uint32_t d0 = src[(kb & 1) * 2];
+                const uint32_t d1 = src[(kb & 1) * 2 + 1];
+                u32x4_t a;
+                if constexpr (DT == kFP8) {
+                    a = u32x4_t{e4m3x2_to_bf16x2<false>(d0), e4m3x2_to_bf16x2<true>(d0),
+                                e4m3x2_to_bf16x2<false>(d1), e4m3x2_to_bf16x2<true>(d1)};
+                } else {
+                    a = u32x4_t{hi_halves(u8_to_f32<0>(d0), u8_to_f32<1>(d0)),
+                                hi_halves(u8_to_f32<2>(d0), u8_to_f32<3>(d0)),
+                                hi_halves(u8_to_f32<0>(d1), u8_to_f32<1>(d1)),
+                                hi_halves(u8_to_f32<2>(d1), u8_to_f32<3>(d1))};
+                }
+                d = mfma_16x16x32_bf16(a, qb[kb], d);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float s;
+                if constexpr (STATIC) {
+                    s = d[r] * k_static;
+                } else {
+                    const uint32_t kw = cb.ks[hp][r >> 1];
+                    const float ksr = (r & 1) ? bf16hi(kw) : bf16lo(kw);
+                    if constexpr (DT == kINT8) {
+                        const uint32_t zw = cb.kz[hp][r >> 1];
+                        const float kzr = (r & 1) ? bf16hi(zw) : bf16lo(zw);
+                        s = (d[r] * ksr + kzr * qsum) * p.score_scale;
+                    } else {
+                        s = d[r] * (ksr * p.score_scale);
+                    }
+                }
+                sc[hp][r] = s;
+            }
+        }
+        if (tail) {
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (ctok + 16 * hp + 4 * g + r >= tok_end) sc[hp][r] = -INFINITY;
+        }
+
+        // ---- online softmax (per head j; all four lane groups agree)
+        float mx = sc[0][0];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[hp][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (__any(mx > m_used + kRescaleHeadroom)) {
+            const float m_new = fmaxf(m_used, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+            lsum *= alpha;
+            pz *= alpha;
+            m_used = m_new;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc[t][r] *= ar;
+            }
+        }
+        float pp[2][4];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pr = __builtin_amdgcn_exp2f(sc[hp][r] - m_used);
+                lsum += pr;
+                float vsr, vzr = 0.0f;
+                if constexpr (STATIC) {
+                    vsr = v_static;
+                } else {
+                    const uint32_t vw = cb.vs[hp][r >> 1];
+                    vsr = (r & 1) ? bf16hi(vw) : bf16lo(vw);
+                    if constexpr (DT == kINT8) {
+                        const uint32_t zw = cb.vz[hp][r >> 1];
+                        vzr = (r & 1) ? bf16hi(zw) : bf16lo(zw);
+                    }
+                }
+                float q = pr * vsr;
+                float qz = pr * vzr;
+                if (tail && ctok + 16 * hp + 4 * g + r >= tok_end) {
+                    q = 0.0f;
+                    qz = 0.0f;
+                }
+                pp[hp][r] = q;
+                if constexpr (DT == kINT8) pz += qz;
+            }
+        }
+
+        // ---- P' as bf16 hi + lo (A operands of PV)
+        u32x4_t ahi, alo;
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+#pragma unroll
+            for (int rp = 0; rp < 2; ++rp) {
+                const float a0 = pp[hp][2 * rp], a1 = pp[hp][2 * rp + 1];
+                const uint32_t hw = pack_bf16_rne(a0, a1);
+                ahi[2 * hp + rp] = hw;
+                alo[2 * hp + rp] = pack_bf16_rne(a0 - bf16lo(hw), a1 - bf16hi(hw));
+            }
+        }
+
+        // ---- V operands per 16-channel tile and PV
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            u32x4_t bv;
+            const int w = t >> 2;
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+                if constexpr (DT == kFP8) {
+                    const uint32_t bp = (uint32_t)(t & 2);
+                    const uint32_t sel = bp | ((4u + bp) << 8) | ((bp + 1u) << 16) | ((5u + bp) << 24);
+                    const uint32_t x01 = perm(cb.v[hp][1][w], cb.v[hp][0][w], sel);
+                    const uint32_t x23 = perm(cb.v[hp][3][w], cb.v[hp][2][w], sel);
+                    if (t & 1) {
+                        bv[2 * hp] = e4m3x2_to_bf16x2<true>(x01);
+                        bv[2 * hp + 1] = e4m3x2_to_bf16x2<true>(x23);
+                    } else {
+                        bv[2 * hp] = e4m3x2_to_bf16x2<false>(x01);
+                        bv[2 * hp + 1] = e4m3x2_to_bf16x2<false>(x23);
+                    }
+                } else {
+                    const int by = t & 3;
+                    const uint32_t v0 = cb.v[hp][0][w], v1 = cb.v[hp][1][w];
+                    const uint32_t v2 = cb.v[hp][2][w], v3 = cb.v[hp][3][w];
+                    bv[2 * hp] = hi_halves((float)((v0 >> (8 * by)) & 0xFFu),
+                                           (float)((v1 >> (8 * by)) & 0xFFu));
+                    bv[2 * hp + 1] = hi_halves((float)((v2 >> (8 * by)) & 0xFFu),
+                                               (float)((v3 >> (8 * by)) & 0xFFu));
+                }
+            }
+            acc[t] = mfma_16x16x32_bf16(ahi, bv, acc[t]);
+            acc[t] = mfma_16x16x32_bf16(alo, bv, acc[t]);
+        }
+    };
+
+    // ---- software pipeline: the next chunk's loads are in flight while this
+    // chunk is computed
+    ChunkBuf b0, b1;
+    load(b0, 0);
+    for (int c = 0;;) {
+        if (c + 1 < n_chunks) load(b1, c + 1);
+        compute(b0, c);
+        if (++c >= n_chunks) break;
+        if (c + 1 < n_chunks) load(b0, c + 1);
+        compute(b1, c);
+        if (++c >= n_chunks) break;
+    }
+
+    // ---- epilogue
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    if constexpr (DT == kINT8) {
+        pz += __shfl_xor(pz, 16);
+        pz += __shfl_xor(pz, 32);
+    }
+    const size_t row0 = (size_t)b * p.n_q + (size_t)h * G;   // first query head of the group
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int head = 4 * g + r;
+        const float lr = __shfl(lsum, head & 15);
+        const float pzr = (DT == kINT8) ? __shfl(pz, head & 15) : 0.0f;
+        if (head < G) {
+            const float inv = 1.0f / lr;
+            f32x4_t o0, o1;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                o0[t] = (acc[t][r] + pzr) * inv;
+                o1[t] = (acc[t + 4][r] + pzr) * inv;
+            }
+            float* dst = (n_seg == 1)
+                             ? p.out + (row0 + head) * kHeadDim + 8 * j
+                             : p.part_o + ((row0 + head) * p.max_parts + seg) * kHeadDim + 8 * j;
+            *(f32x4_t*)dst = o0;
+            *(f32x4_t*)(dst + 4) = o1;
+        }
+    }
+    if (g == 0 && j < G) {
+        const float l2 = m_used + __log2f(lsum);
+        if (n_seg == 1) {
+            if (p.lse) p.lse[row0 + j] = l2 * kLn2;
+        } else {
+            p.part_lse[(row0 + j) * p.max_parts + seg] = l2;
+        }
+    }
+}
+
+template <int DT, bool STATIC, int PS>
+__global__ __launch_bounds__(256) void split_kernel(SplitParams p) {
+    extern __shared__ int s_pfx[];   // [num_seqs + 1]
+    __shared__ int s_wsum[4];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int B = p.num_seqs;
+
+    // ---- pages per sequence and their exclusive prefix sum (every workgroup)
+    const int per = (B + 255) / 256;
+    const int beg = min(tid * per, B);
+    const int end = min(beg + per, B);
+    int local = 0;
+    for (int i = beg; i < end; ++i) local += pages_of(p.context_lens[i], p.max_ctx, PS);
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_wsum[wid] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wid; ++w) run += s_wsum[w];
+    for (int i = beg; i < end; ++i) {
+        s_pfx[i] = run;
+        run += pages_of(p.context_lens[i], p.max_ctx, PS);
+    }
+    if (tid == 0) s_pfx[B] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    __syncthreads();
+
+    const long long W = (long long)s_pfx[B] * p.n_kv;
+    long long chunk;
+    if (p.forced_chunk > 0) {
+        chunk = p.forced_chunk;
+    } else {
+        chunk = (W + p.total_waves - 1) / p.total_waves;
+        if (chunk < p.min_chunk) chunk = p.min_chunk;
+    }
+    if (blockIdx.x == 0) {
+        if (tid == 0) p.ws_header[0] = (int)chunk;
+        for (int i = tid; i <= B; i += 256) p.ws_pfx[i] = s_pfx[i];
+    }
+
+    const long long waves = (long long)gridDim.x * 4;
+    for (long long k = (long long)blockIdx.x * 4 + wid; k * chunk < W; k += waves) {
+        long long x = k * chunk;
+        const long long xend = min(x + chunk, W);
+        while (x < xend) {
+            int lo = 0, hi = B - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((long long)s_pfx[mid] * p.n_kv <= x) lo = mid;
+                else hi = mid - 1;
+            }
+            const int b = uniform(lo);
+            const int pb = uniform(s_pfx[b + 1] - s_pfx[b]);
+            const long long start_b = (long long)s_pfx[b] * p.n_kv;
+            const int h = uniform((int)((x - start_b) / pb));
+            const long long item_start = start_b + (long long)h * pb;
+            const long long item_end = item_start + pb;
+            const long long seg_end = min(xend, item_end);
+            const int page0 = uniform((int)(x - item_start));
+            const int page1 = uniform((int)(seg_end - item_start));
+            const long long first_seg = item_start / chunk;
+            const int n_seg = uniform((int)((item_end - 1) / chunk - first_seg + 1));
+            const int seg = uniform((int)(x / chunk - first_seg));
+            process_segment<DT, STATIC, PS>(p, b, h, page0, page1, seg, n_seg, lane);
+            x = seg_end;
+        }
+    }
+}
+
+// Merge of the partial results of one (sequence, query head):
+//   L = max_i lse_i,  w_i = 2^(lse_i - L),  out = sum_i w_i o_i / sum_i w_i,
+//   lse = (L + log2 sum_i w_i) * ln 2.
+// One wave per (sequence, query head), two channels per lane.
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
+    const int lane = threadIdx.x & 63;
+    const long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (idx >= (long long)p.num_seqs * p.n_q) return;
+    const int b = (int)(idx / p.n_q);
+    const int hq = (int)(idx - (long long)b * p.n_q);
+    const int h = hq / p.group;
+    const long long chunk = p.ws_header[0];
+    const int pb = p.ws_pfx[b + 1] - p.ws_pfx[b];
+    float* out = p.out + idx * kHeadDim + 2 * lane;
+    if (pb == 0) {
+        out[0] = 0.0f;
+        out[1] = 0.0f;
+        if (p.lse && lane == 0) p.lse[idx] = -INFINITY;
+        return;
+    }
+    const long long item_start = (long long)p.ws_pfx[b] * p.n_kv + (long long)h * pb;
+    const int n_seg = (int)((item_start + pb - 1) / chunk - item_start / chunk + 1);
+    if (n_seg == 1) return;   // written by the split kernel
+    const float* pl = p.part_lse + idx * p.max_parts;
+    const float* po = p.part_o + idx * p.max_parts * kHeadDim + 2 * lane;
+    float L = -INFINITY;
+    for (int i = 0; i < n_seg; ++i) L = fmaxf(L, pl[i]);
+    float ws = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int i = 0; i < n_seg; ++i) {
+        const float w = __builtin_amdgcn_exp2f(pl[i] - L);
+        ws += w;
+        o0 += w * po[(size_t)i * kHeadDim];
+        o1 += w * po[(size_t)i * kHeadDim + 1];
+    }
+    const float inv = 1.0f / ws;
+    out[0] = o0 * inv;
+    out[1] = o1 * inv;
+    if (p.lse && lane == 0) p.lse[idx] = (L + __log2f(ws)) * kLn2;
+}
+
+template <int DT, bool STATIC, int PS>
+static const void* split_fn() {
+    return (const void*)&split_kernel<DT, STATIC, PS>;
+}
+
+static const void* pick_split(int dtype, bool static_scale, int page_size) {
+    if (dtype == kFP8) {
+        if (static_scale) return page_size == 16 ? split_fn<kFP8, true, 16>() : split_fn<kFP8, true, 32>();
+        return page_size == 16 ? split_fn<kFP8, false, 16>() : split_fn<kFP8, false, 32>();
+    }
+    return page_size == 16 ? split_fn<kINT8, false, 16>() : split_fn<kINT8, false, 32>();
+}
+
+hipError_t split_occupancy(int dtype, bool static_scale, int page_size, size_t lds_bytes,
+                           int* blocks_per_cu) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        blocks_per_cu, pick_split(dtype, static_scale, page_size), kSplitThreads, lds_bytes);
+}
+
+hipError_t launch_split(int dtype, bool static_scale, int page_size, const SplitParams& p, int grid,
+                        size_t lds_bytes, hipStream_t stream) {
+    if (grid <= 0) return hipSuccess;
+    SplitParams args = p;
+    void* kargs[] = {&args};
+    return hipLaunchKernel(pick_split(dtype, static_scale, page_size), dim3(grid),
+                           dim3(kSplitThreads), kargs, lds_bytes, stream);
+}
+
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream) {
+    const long long rows = (long long)p.num_seqs * p.n_q;
+    const long long grid = (rows + 3) / 4;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

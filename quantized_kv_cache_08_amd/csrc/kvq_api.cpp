@@ -1,0 +1,317 @@
+// kvq_api.cpp -- the C ABI of libkvq (declared in include/kvq.h): argument
+// validation, page-record accounting, workspace layout, work-range planning
+// and kernel launches.  No allocation, no host synchronisation.
+#include "kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+    int cus = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_mu;
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_dev[dev].cus == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        g_dev[dev].cus = n;
+    }
+    return g_dev[dev].cus;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool valid_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// Common descriptor checks for the FP8 / INT8 paths.
+kvq_status check_cache(const kvq_cache* c) {
+    if (!c) return KVQ_ERR_INVALID;
+    if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_INT8_ASYM) {
+        return c->dtype == KVQ_INT4_KIVI ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
+    }
+    if (c->scale_mode < KVQ_SCALE_PER_TENSOR || c->scale_mode > KVQ_SCALE_PER_TOKEN_HEAD)
+        return KVQ_ERR_INVALID;
+    if (c->dtype == KVQ_INT8_ASYM && c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD)
+        return KVQ_ERR_UNSUPPORTED;
+    if (c->num_pages <= 0 || c->num_kv_heads <= 0 || c->page_size <= 0 || c->head_dim <= 0)
+        return KVQ_ERR_INVALID;
+    if (c->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
+    if (c->page_size != 16 && c->page_size != 32) return KVQ_ERR_UNSUPPORTED;
+    if (!c->k_pages || !c->v_pages) return KVQ_ERR_INVALID;
+    if (c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD && !c->static_scales) return KVQ_ERR_INVALID;
+    return KVQ_OK;
+}
+
+struct Plan {
+    int max_pages = 0;     // ceil(max_context_len / page_size)
+    int max_parts = 1;
+    int min_chunk = 1;
+    int forced_chunk = 0;
+    size_t off_pfx = 0, off_lse = 0, off_o = 0, total = 0;
+};
+
+Plan make_plan(int page_size, int num_seqs, int num_q_heads, int max_ctx, int partition_pages) {
+    Plan pl;
+    pl.max_pages = (max_ctx + page_size - 1) / page_size;
+    const int mp = std::max(1, pl.max_pages);
+    if (partition_pages > 0) {
+        const long long need = (mp + (long long)partition_pages - 1) / partition_pages + 1;
+        pl.max_parts = (int)std::max(1LL, std::min<long long>(mp, need));
+        pl.forced_chunk = partition_pages;
+        pl.min_chunk = partition_pages;
+    } else {
+        pl.max_parts = std::min(mp, kMaxParts);
+        pl.min_chunk = kMinChunkPages;
+        if (mp > pl.max_parts) {
+            const int bound = (mp + pl.max_parts - 2) / (pl.max_parts - 1);
+            pl.min_chunk = std::max(pl.min_chunk, bound);
+        }
+    }
+    const size_t rows = (size_t)num_seqs * (size_t)num_q_heads;
+    pl.off_pfx = 256;
+    pl.off_lse = pl.off_pfx + align256(((size_t)num_seqs + 1) * sizeof(int32_t));
+    pl.off_o = pl.off_lse + align256(rows * pl.max_parts * sizeof(float));
+    pl.total = pl.off_o + align256(rows * pl.max_parts * kHeadDim * sizeof(float));
+    return pl;
+}
+
+kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                        const int32_t* block_table, int32_t max_pages_per_seq,
+                        const int32_t* context_lens, int32_t max_context_len,
+                        int32_t partition_pages, void* workspace, size_t workspace_bytes,
+                        float* out, Plan* plan) {
+    kvq_status st = check_cache(c);
+    if (st != KVQ_OK) return st;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_pages_per_seq < 0 ||
+        partition_pages < 0)
+        return KVQ_ERR_INVALID;
+    if (num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID;
+    if (!valid_group(num_q_heads / c->num_kv_heads)) return KVQ_ERR_UNSUPPORTED;
+    if ((long long)max_context_len > (long long)max_pages_per_seq * c->page_size)
+        return KVQ_ERR_INVALID;
+    if (num_seqs > 16383) return KVQ_ERR_UNSUPPORTED;   // prefix table lives in LDS
+    if (num_seqs == 0) return KVQ_OK;
+    if (!q || !block_table || !context_lens || !out || !workspace) return KVQ_ERR_INVALID;
+    *plan = make_plan(c->page_size, num_seqs, num_q_heads, max_context_len, partition_pages);
+    if (workspace_bytes < plan->total) return KVQ_ERR_WORKSPACE;
+    return KVQ_OK;
+}
+
+kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                     const int32_t* block_table, int32_t max_pages_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
+                     const Plan& pl, void* workspace, float* out, float* lse, hipStream_t stream) {
+    const bool is_static = c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD;
+    uint8_t* ws = (uint8_t*)workspace;
+    SplitParams p{};
+    p.k_pages = (const uint8_t*)c->k_pages;
+    p.v_pages = (const uint8_t*)c->v_pages;
+    p.q = (const uint16_t*)q;
+    p.block_table = block_table;
+    p.context_lens = context_lens;
+    p.static_scales = (const uint16_t*)c->static_scales;
+    p.out = out;
+    p.lse = lse;
+    p.part_o = (float*)(ws + pl.off_o);
+    p.part_lse = (float*)(ws + pl.off_lse);
+    p.ws_header = (int32_t*)ws;
+    p.ws_pfx = (int32_t*)(ws + pl.off_pfx);
+    p.rec_k = (long long)kvq_record_bytes(c->dtype, c->scale_mode, c->page_size, c->head_dim, 0);
+    p.rec_v = (long long)kvq_record_bytes(c->dtype, c->scale_mode, c->page_size, c->head_dim, 1);
+    p.num_seqs = num_seqs;
+    p.n_q = num_q_heads;
+    p.n_kv = c->num_kv_heads;
+    p.group = num_q_heads / c->num_kv_heads;
+    p.num_pages = c->num_pages;
+    p.max_pages_per_seq = max_pages_per_seq;
+    p.max_ctx = max_context_len;
+    p.max_pages = pl.max_pages;
+    p.max_parts = pl.max_parts;
+    p.min_chunk = pl.min_chunk;
+    p.forced_chunk = pl.forced_chunk;
+    p.static_head_stride = c->scale_mode == KVQ_SCALE_PER_HEAD ? 1 : 0;
+    p.static_kv_stride = c->scale_mode == KVQ_SCALE_PER_HEAD ? c->num_kv_heads : 1;
+    p.score_scale = softmax_scale * 1.4426950408889634f;
+
+    const size_t lds = ((size_t)num_seqs + 1) * sizeof(int32_t);
+    int per_cu = 0;
+    if (split_occupancy(c->dtype, is_static, c->page_size, lds, &per_cu) != hipSuccess)
+        return KVQ_ERR_HIP;
+    const int cus = device_cus();
+    if (cus <= 0 || per_cu <= 0) return KVQ_ERR_HIP;
+    const int grid = per_cu * cus;
+    p.total_waves = grid * (kSplitThreads / 64);
+    if (launch_split(c->dtype, is_static, c->page_size, p, grid, lds, stream) != hipSuccess)
+        return KVQ_ERR_HIP;
+    return KVQ_OK;
+}
+
+kvq_status run_reduce(const kvq_cache* c, int32_t num_seqs, int32_t num_q_heads, const Plan& pl,
+                      void* workspace, float* out, float* lse, hipStream_t stream) {
+    uint8_t* ws = (uint8_t*)workspace;
+    ReduceParams r{};
+    r.part_o = (const float*)(ws + pl.off_o);
+    r.part_lse = (const float*)(ws + pl.off_lse);
+    r.ws_header = (const int32_t*)ws;
+    r.ws_pfx = (const int32_t*)(ws + pl.off_pfx);
+    r.out = out;
+    r.lse = lse;
+    r.num_seqs = num_seqs;
+    r.n_q = num_q_heads;
+    r.n_kv = c->num_kv_heads;
+    r.group = num_q_heads / c->num_kv_heads;
+    r.max_parts = pl.max_parts;
+    return launch_reduce(r, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size, int32_t head_dim,
+                        int32_t which) {
+    if (page_size <= 0 || head_dim <= 0 || (which != 0 && which != 1)) return 0;
+    size_t codes, meta;
+    if (dtype == KVQ_FP8_E4M3) {
+        if (scale_mode < KVQ_SCALE_PER_TENSOR || scale_mode > KVQ_SCALE_PER_TOKEN_HEAD) return 0;
+        codes = (size_t)page_size * head_dim;
+        meta = scale_mode == KVQ_SCALE_PER_TOKEN_HEAD ? 2u * page_size : 0u;
+    } else if (dtype == KVQ_INT8_ASYM) {
+        if (scale_mode != KVQ_SCALE_PER_TOKEN_HEAD) return 0;
+        codes = (size_t)page_size * head_dim;
+        meta = 4u * page_size;
+    } else if (dtype == KVQ_INT4_KIVI) {
+        if (scale_mode != KVQ_SCALE_PER_TOKEN_HEAD || (head_dim & 1)) return 0;
+        codes = (size_t)page_size * head_dim / 2;
+        meta = which == 0 ? 4u * (size_t)head_dim : 4u * page_size;
+    } else {
+        return 0;
+    }
+    return (codes + meta + 15) & ~size_t(15);
+}
+
+kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,
+                      const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    if (num_tokens < 0) return KVQ_ERR_INVALID;
+    if (num_tokens == 0) return KVQ_OK;
+    if (!k || !v || !slot_mapping) return KVQ_ERR_INVALID;
+    AppendParams p{};
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.slot_mapping = slot_mapping;
+    p.k_pages = (uint8_t*)cache->k_pages;
+    p.v_pages = (uint8_t*)cache->v_pages;
+    p.static_scales = (const uint16_t*)cache->static_scales;
+    p.rec_k = (long long)kvq_record_bytes(cache->dtype, cache->scale_mode, cache->page_size,
+                                          cache->head_dim, 0);
+    p.rec_v = (long long)kvq_record_bytes(cache->dtype, cache->scale_mode, cache->page_size,
+                                          cache->head_dim, 1);
+    p.num_slots = (long long)cache->num_pages * cache->page_size;
+    p.num_tokens = num_tokens;
+    p.n_kv = cache->num_kv_heads;
+    p.static_head_stride = cache->scale_mode == KVQ_SCALE_PER_HEAD ? 1 : 0;
+    p.static_kv_stride = cache->scale_mode == KVQ_SCALE_PER_HEAD ? cache->num_kv_heads : 1;
+    const bool is_static = cache->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD;
+    if (launch_append(cache->dtype, is_static, cache->page_size, p, stream) != hipSuccess)
+        return KVQ_ERR_HIP;
+    return KVQ_OK;
+}
+
+kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t max_context_len,
+                                      int32_t partition_pages, size_t* bytes) {
+    if (!bytes) return KVQ_ERR_INVALID;
+    *bytes = 0;
+    if (!cache) return KVQ_ERR_INVALID;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_pages < 0)
+        return KVQ_ERR_INVALID;
+    if (cache->page_size <= 0) return KVQ_ERR_INVALID;
+    *bytes = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages)
+                 .total;
+    return KVQ_OK;
+}
+
+kvq_status kvq_decode_split(const kvq_cache* cache, const void* q, int32_t num_seqs,
+                            int32_t num_q_heads, const int32_t* block_table,
+                            int32_t max_pages_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, float softmax_scale, int32_t partition_pages,
+                            void* workspace, size_t workspace_bytes, float* out, float* lse,
+                            hipStream_t stream) {
+    Plan pl;
+    kvq_status st = check_decode(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq,
+                                 context_lens, max_context_len, partition_pages, workspace,
+                                 workspace_bytes, out, &pl);
+    if (st != KVQ_OK || num_seqs == 0) return st;
+    return run_split(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
+                     max_context_len, softmax_scale, pl, workspace, out, lse, stream);
+}
+
+kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t max_context_len, int32_t partition_pages, void* workspace,
+                             size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
+    if (!cache) return KVQ_ERR_INVALID;
+    if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_pages < 0)
+        return KVQ_ERR_INVALID;
+    if (cache->num_kv_heads <= 0 || cache->page_size <= 0 || num_q_heads % cache->num_kv_heads)
+        return KVQ_ERR_INVALID;
+    if (num_seqs == 0) return KVQ_OK;
+    if (!workspace || !out) return KVQ_ERR_INVALID;
+    Plan pl = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages);
+    if (workspace_bytes < pl.total) return KVQ_ERR_WORKSPACE;
+    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, stream);
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t num_seqs,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, float softmax_scale,
+                                int32_t partition_pages, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, hipStream_t stream) {
+    Plan pl;
+    kvq_status st = check_decode(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq,
+                                 context_lens, max_context_len, partition_pages, workspace,
+                                 workspace_bytes, out, &pl);
+    if (st != KVQ_OK || num_seqs == 0) return st;
+    st = run_split(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
+                   max_context_len, softmax_scale, pl, workspace, out, lse, stream);
+    if (st != KVQ_OK) return st;
+    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, stream);
+}
+
+kvq_status kvq_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
+    if (n < 0) return KVQ_ERR_INVALID;
+    if (n == 0) return KVQ_OK;
+    if (!x || !codes) return KVQ_ERR_INVALID;
+    return launch_e4m3_encode(x, codes, n, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+const char* kvq_status_string(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_INVALID: return "invalid argument";
+        case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KVQ_ERR_WORKSPACE: return "workspace too small";
+        case KVQ_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// kvq_device.h -- device helpers shared by the gfx950 kernels of libkvq.
+//
+// Number-format primitives (BF16 directed rounding, OCP E4M3 encode through
+// the hardware converter, exact code -> bf16 conversions) and the MFMA
+// wrapper.  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bits_to_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f32_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// bf16 bits (low 16 of u) -> fp32, exact.
+__device__ __forceinline__ float bf16lo(uint32_t u) { return bits_to_f32(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return bits_to_f32(u & 0xFFFF0000u); }
+
+// Smallest bf16 >= f (finite f); result as bf16 bits.  The upper half of an
+// fp32 is the bf16 truncation toward zero; a non-zero lower half on a positive
+// value means the ceiling is one unit further from zero.
+__device__ __forceinline__ uint32_t bf16_up_bits(float f) {
+    uint32_t u = f32_to_bits(f);
+    uint32_t t = u >> 16;
+    if ((u & 0xFFFFu) != 0u && !(u >> 31)) t += 1u;
+    return t;
+}
+// Largest bf16 <= f.
+__device__ __forceinline__ uint32_t bf16_down_bits(float f) {
+    uint32_t u = f32_to_bits(f);
+    uint32_t t = u >> 16;
+    if ((u & 0xFFFFu) != 0u && (u >> 31)) t += 1u;
+    return t;
+}
+
+// Two fp32 -> packed bf16 pair (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+    bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four fp32 -> four OCP E4M3 codes (byte i = code of the i-th argument):
+// nearest-even through the gfx950 converter after an explicit clamp to
+// +-448 (saturation); -0 keeps its sign; NaN gives 0x7F.
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+    float ca = fminf(fmaxf(a, -448.0f), 448.0f);
+    float cb = fminf(fmaxf(b, -448.0f), 448.0f);
+    float cc = fminf(fmaxf(c, -448.0f), 448.0f);
+    float cd = fminf(fmaxf(d, -448.0f), 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cc, cd, w, true);
+    uint32_t r = (uint32_t)w;
+    if (a != a) r = (r & 0xFFFFFF00u) | 0x7Fu;
+    if (b != b) r = (r & 0xFFFF00FFu) | 0x7F00u;
+    if (c != c) r = (r & 0xFF00FFFFu) | 0x7F0000u;
+    if (d != d) r = (r & 0x00FFFFFFu) | 0x7F000000u;
+    return r;
+}
+
+// Two E4M3 codes (bytes 0,1 or 2,3 of w) -> packed exact bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+    bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Byte select: result byte i = selector byte i of `sel` choosing from
+// {lo bytes 0..3 (values 0..3), hi bytes 0..3 (values 4..7)}.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Two u8 codes (byte positions BA, BB of wa, wb) -> packed exact bf16 pair.
+// The fp32 value of a byte is exact and has at most 8 significant bits, so its
+// upper half is the exact bf16.
+template <int BA>
+__device__ __forceinline__ float u8_to_f32(uint32_t w) {
+    return (float)((w >> (8 * BA)) & 0xFFu);
+}
+__device__ __forceinline__ uint32_t hi_halves(float a, float b) {
+    return perm(f32_to_bits(b), f32_to_bits(a), 0x07060302u);
+}
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+    return (T)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+}  // namespace kvq
