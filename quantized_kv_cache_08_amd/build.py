@@ -5,6 +5,7 @@
 hipcc cross-compiles for gfx950 without a GPU.  Flags:
   -fhip-fp32-correctly-rounded-divide-sqrt   IEEE division in the quantizers
   -Xclang -target-feature -Xclang -packed-fp32-ops   no packed-fp32 instructions
+  -mllvm -amdgpu-mfma-vgpr-form=1   MFMA accumulators in VGPRs (no AGPR copies)
 """
 import concurrent.futures as cf
 import glob
@@ -23,6 +24,7 @@ ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
          "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wno-unused-command-line-argument", "-I", INC, "-I", CSRC]
 
 

@@ -45,6 +45,7 @@ namespace kvq {
 constexpr int kFP8 = 1;
 constexpr int kINT8 = 2;
 constexpr float kRescaleHeadroom = 8.0f;  // log2 units
+constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, dword 3 (gfx9 family)
 
 struct ChunkBuf {
     u32x4_t k[2][2];   // [half][part]: K channels 32g..32g+15 / +16..+31 of token j
@@ -105,44 +106,52 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
     float lsum = 0.0f;
     float pz = 0.0f;
 
-    const int* bt = p.block_table + (size_t)b * p.max_pages_per_seq;
+    // the block table is read-only here: reading it through the constant
+    // address space makes the (uniform) page-id loads scalar, so waiting for a
+    // page id never waits for the K/V vector loads in flight
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(p.block_table) +
+        (size_t)b * p.max_pages_per_seq;
     const int n_chunks = (PS == 16) ? (page1 - page0 + 1) / 2 : (page1 - page0);
-    int ids_base = page0;
-    int ids = (page0 + lane < page1) ? bt[page0 + lane] : 0;
 
+    // per-lane byte offsets inside a page record
+    const int voff_k = j * kHeadDim + 32 * g;       // K row j, channels [32g, 32g+32)
+    const int voff_v = 4 * g * kHeadDim + 8 * j;    // V rows 4g.., channels [8j, 8j+8)
+    const int voff_s = PS * kHeadDim + 8 * g;       // bf16 metadata of tokens 4g..4g+3
+
+    // Loads of chunk c through buffer resources spanning one page record.  A
+    // chunk or half that does not exist (past the segment, or the second half
+    // of an odd page count) gets a zero-size resource: its loads are issued
+    // (so every pipeline stage issues the same loads) but fetch nothing and
+    // return zeros, and its tokens are masked.
     auto load = [&](ChunkBuf& cb, const int c) {
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
             const int pidx = (PS == 16) ? page0 + 2 * c + hp : page0 + c;
-            const int tok0 = (PS == 16) ? 0 : 16 * hp;
-            // a 16-token half past the segment (odd page count) is never read
-            const bool live = (PS == 32) || (pidx < page1);
-            if (live && pidx - ids_base >= 64) {
-                ids_base = pidx;
-                ids = (pidx + lane < page1) ? bt[pidx + lane] : 0;
-            }
+            const bool live = (c < n_chunks) && (pidx < page1);
             // page ids come from the caller's table: clamp so that a bad entry
             // reads a wrong page instead of leaving the pool
-            int page = live ? __builtin_amdgcn_readlane(ids, pidx - ids_base) : 0;
-            page = min(max(page, 0), p.num_pages - 1);
-            const uint8_t* krec = p.k_pages + ((size_t)page * p.n_kv + h) * (size_t)p.rec_k;
-            const uint8_t* vrec = p.v_pages + ((size_t)page * p.n_kv + h) * (size_t)p.rec_v;
-            const uint8_t* kr = krec + (tok0 + j) * kHeadDim + 32 * g;
-            const u32x4_t z4 = {0u, 0u, 0u, 0u};
-            const u32x2_t z2 = {0u, 0u};
-            cb.k[hp][0] = live ? *(const u32x4_t*)kr : z4;
-            cb.k[hp][1] = live ? *(const u32x4_t*)(kr + 16) : z4;
+            const int page = min(max(bt[min(pidx, page1 - 1)], 0), p.num_pages - 1);
+            const size_t rec_idx = (size_t)page * p.n_kv + h;
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(p.k_pages + rec_idx * (size_t)p.rec_k), (short)0, live ? (int)p.rec_k : 0,
+                kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(p.v_pages + rec_idx * (size_t)p.rec_v), (short)0, live ? (int)p.rec_v : 0,
+                kBufferFlags);
+            const int t0 = (PS == 16) ? 0 : 16 * hp;     // first token row of this half
+            cb.k[hp][0] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + t0 * kHeadDim, 0, 0);
+            cb.k[hp][1] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k + t0 * kHeadDim + 16, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 cb.v[hp][r] =
-                    live ? *(const u32x2_t*)(vrec + (tok0 + 4 * g + r) * kHeadDim + 8 * j) : z2;
+                    __builtin_amdgcn_raw_buffer_load_b64(rv, voff_v + (t0 + r) * kHeadDim, 0, 0);
             if constexpr (!STATIC) {
-                const int so = PS * kHeadDim + 2 * (tok0 + 4 * g);
-                cb.ks[hp] = live ? *(const u32x2_t*)(krec + so) : z2;
-                cb.vs[hp] = live ? *(const u32x2_t*)(vrec + so) : z2;
+                cb.ks[hp] = __builtin_amdgcn_raw_buffer_load_b64(rk, voff_s + 2 * t0, 0, 0);
+                cb.vs[hp] = __builtin_amdgcn_raw_buffer_load_b64(rv, voff_s + 2 * t0, 0, 0);
                 if constexpr (DT == kINT8) {
-                    cb.kz[hp] = live ? *(const u32x2_t*)(krec + so + 2 * PS) : z2;
-                    cb.vz[hp] = live ? *(const u32x2_t*)(vrec + so + 2 * PS) : z2;
+                    cb.kz[hp] = __builtin_amdgcn_raw_buffer_load_b64(rk, voff_s + 2 * t0 + 2 * PS, 0, 0);
+                    cb.vz[hp] = __builtin_amdgcn_raw_buffer_load_b64(rv, voff_s + 2 * t0 + 2 * PS, 0, 0);
                 }
             }
         }
@@ -307,16 +316,20 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
         }
     };
 
-    // ---- software pipeline: the next chunk's loads are in flight while this
-    // chunk is computed
-    ChunkBuf b0, b1;
+    // ---- software pipeline: three buffers, the loads of the next two chunks
+    // are in flight while a chunk is computed
+    ChunkBuf b0, b1, b2;
     load(b0, 0);
+    load(b1, 1);
     for (int c = 0;;) {
-        if (c + 1 < n_chunks) load(b1, c + 1);
+        load(b2, c + 2);
         compute(b0, c);
         if (++c >= n_chunks) break;
-        if (c + 1 < n_chunks) load(b0, c + 1);
+        load(b0, c + 2);
         compute(b1, c);
+        if (++c >= n_chunks) break;
+        load(b1, c + 2);
+        compute(b2, c);
         if (++c >= n_chunks) break;
     }
 
