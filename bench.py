@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama8b", choices=["tiny", "llama8b", "llama70b", "mixed"])
+    ap.add_argument("--config", default="llama8b", choices=["tiny", "llama8b", "llama70b", "mixed", "kivi"])
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto)")
     ap.add_argument("--partition-pages", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -57,17 +57,35 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def kivi_quantized(w, lens: np.ndarray) -> np.ndarray:
+    """Tokens per sequence held as INT4 groups: 32 * floor(max(0, n - residual) / 32)."""
+    over = np.maximum(0, np.asarray(lens, dtype=np.int64) - w.resid)
+    return (over // w.page_size) * w.page_size
+
+
 def step_bytes(w, lens: np.ndarray):
     """Algorithmic bytes of one step, split by kernel."""
     n_kv, d, Hq = w.num_kv_heads, w.head_dim, w.num_q_heads
-    meta = 2 if w.dtype == "fp8" else 4            # bf16 scale (+ bf16 zero-point) per (token, head)
     tokens = int(lens.sum())
     B = len(lens)
-    pages = int(((lens + w.page_size - 1) // w.page_size).sum())
-    kv = tokens * n_kv * 2 * (d + meta)
-    split = kv + pages * 4 + B * Hq * d * 2        # K/V codes+scales, block-table entries, q
-    reduce = B * Hq * d * 4                        # out (fp32)
-    append = B * n_kv * 2 * (d * 2 + d + meta) + B * 4
+    if w.dtype == "kivi4":
+        rk, rv = 2048 + 4 * d, 2048 + 4 * w.page_size      # INT4 page records (codes + bf16 s, z)
+        nq = kivi_quantized(w, lens)
+        pages = int((nq // w.page_size).sum())
+        window = (tokens - int(nq.sum())) * n_kv * d * 2 * 2  # fp16 K and V rows
+        kv = pages * n_kv * (rk + rv) + window
+        split = kv + pages * 4 + B * Hq * d * 2
+        # one new token per sequence: bf16 in, fp16 window row out; a group flush
+        # (32 fp16 window rows in, one K and one V record out) when it completes one
+        flushes = int((kivi_quantized(w, lens) > kivi_quantized(w, lens - 1)).sum())
+        append = B * n_kv * d * 2 * 2 * 2 + flushes * n_kv * (32 * d * 2 * 2 + rk + rv) + B * 8
+    else:
+        meta = 2 if w.dtype == "fp8" else 4            # bf16 scale (+ bf16 zero-point) per (token, head)
+        pages = int(((lens + w.page_size - 1) // w.page_size).sum())
+        kv = tokens * n_kv * 2 * (d + meta)
+        split = kv + pages * 4 + B * Hq * d * 2        # K/V codes+scales, block-table entries, q
+        append = B * n_kv * 2 * (d * 2 + d + meta) + B * 4
+    reduce = B * Hq * d * 4                            # out (fp32)
     return dict(kv=kv, split=split, reduce=reduce, append=append, total=split + reduce + append,
                 tokens=tokens, pages=pages)
 
@@ -103,8 +121,27 @@ def cpu_baseline(w, budget_s: float):
     from oracle import oracle as O
 
     lens = synthetic.seq_lens(w)
+    kivi = w.dtype == "kivi4"
+    if kivi:
+        # a 16384-token prefix of each sequence keeps one pass to a few seconds
+        lens = np.minimum(lens, 16384)
     dt = O.FP8 if w.dtype == "fp8" else O.INT8
     q_all = synthetic.gen_q(w, "cpu")
+    scale = 1.0 / math.sqrt(w.head_dim)
+
+    def run_oracle(qb, kb, vb):
+        if not kivi:
+            O.decode_reference(qb, kb, vb, dt)
+            return
+        k16, v16 = O.bf16_to_f16_bits(kb), O.bf16_to_f16_bits(vb)
+        T = kb.shape[0]
+        kd = np.zeros((T, w.num_kv_heads, w.head_dim))
+        vd = np.zeros_like(kd)
+        for h in range(w.num_kv_heads):
+            st = O.kivi_stream(k16[:, h], v16[:, h], w.resid, w.page_size)
+            kd[:, h], vd[:, h] = O.kivi_dequant(st, w.page_size)
+        O.attention(O.bf16_value(qb).astype(np.float64), kd, vd, scale)
+
     held = []
     t_total, done = 0.0, []
     wall0 = time.perf_counter()
@@ -125,7 +162,7 @@ def cpu_baseline(w, budget_s: float):
             i += 1
         T, qb, kb, vb = cur
         t0 = time.perf_counter()
-        O.decode_reference(qb, kb, vb, dt)
+        run_oracle(qb, kb, vb)
         t_total += time.perf_counter() - t0
         done.append(T)
         if len(done) % 16 == 1:
@@ -135,6 +172,7 @@ def cpu_baseline(w, budget_s: float):
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(by["kv"] / t_total / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(done)} sequence passes over the first {len(held)} of {len(lens)} sequences "
+                      + ("(16384-token prefixes) " if kivi else "") +
                       f"({int(sl.sum())} tokens): quantize-on-store of their K/V plus fp64 attention, "
                       f"{t_total:.1f} s; value = their K/V code+scale bytes / time",
             "tokens_per_s": round(len(done) / t_total, 4)}
@@ -182,20 +220,42 @@ def main():
 
     # each cache replica holds the context minus the newest token (pages laid
     # out for the full length); every step appends that token, then decodes
+    kivi = w.dtype == "kivi4"
     full_layout = synthetic.page_layout(w, lens)
+    bt_dev = torch.from_numpy(full_layout.block_table).cuda()
     caches = []
     for r in range(reps):
-        code = kvq.KVQ_FP8_E4M3 if w.dtype == "fp8" else kvq.KVQ_INT8_ASYM
-        cache = kvq.Cache(code, full_layout.num_pages, w.num_kv_heads, w.page_size, d)
-        for b, n in enumerate(lens):
-            m = int(n) - 1
-            for p0 in range(0, m, 1 << 16):
-                mm = min(1 << 16, m - p0)
-                k, v = synthetic.gen_kv(w, b, p0, mm, "cuda")
-                kvq.append(cache, k, v, slots_for(full_layout, b, p0, mm, w.page_size))
+        if kivi:
+            cache = kvq.Cache(kvq.KVQ_INT4_KIVI, full_layout.num_pages, w.num_kv_heads, w.page_size, d,
+                              max_seqs=B, residual=w.resid)
+            held = np.zeros(B, dtype=np.int64)
+            target = lens - 1
+            while (held < target).any():
+                step_n = np.minimum(target - held, 1 << 14)
+                ks, vs = [], []
+                for b in range(B):
+                    if step_n[b]:
+                        k, v = synthetic.gen_kv(w, b, int(held[b]), int(step_n[b]), "cuda")
+                        ks.append(k)
+                        vs.append(v)
+                offs = torch.from_numpy(np.concatenate([[0], np.cumsum(step_n)]).astype(np.int32)).cuda()
+                kvq.kivi_append(cache, torch.cat(ks), torch.cat(vs), offs,
+                                torch.from_numpy(held.astype(np.int32)).cuda(), bt_dev, int(step_n.max()))
+                held += step_n
+        else:
+            code = kvq.KVQ_FP8_E4M3 if w.dtype == "fp8" else kvq.KVQ_INT8_ASYM
+            cache = kvq.Cache(code, full_layout.num_pages, w.num_kv_heads, w.page_size, d)
+            for b, n in enumerate(lens):
+                m = int(n) - 1
+                for p0 in range(0, m, 1 << 16):
+                    mm = min(1 << 16, m - p0)
+                    k, v = synthetic.gen_kv(w, b, p0, mm, "cuda")
+                    kvq.append(cache, k, v, slots_for(full_layout, b, p0, mm, w.page_size))
         caches.append(cache)
-    bt_dev = torch.from_numpy(full_layout.block_table).cuda()
+        print(f"[bench] cache replica {r} filled", file=sys.stderr, flush=True)
     cl_dev = torch.from_numpy(lens.astype(np.int32)).cuda()
+    cl_before = torch.from_numpy((lens - 1).astype(np.int32)).cuda()
+    new_offs = torch.arange(B + 1, dtype=torch.int32, device="cuda")
     q = synthetic.gen_q(w, "cuda")
     knew = torch.empty(B, w.num_kv_heads, d, dtype=torch.bfloat16, device="cuda")
     vnew = torch.empty_like(knew)
@@ -217,7 +277,10 @@ def main():
         c = caches[i % reps]
         if ev is not None:
             ev[0].record()
-        kvq.append(c, knew, vnew, slot_dev)
+        if kivi:
+            kvq.kivi_append(c, knew, vnew, new_offs, cl_before, bt_dev, 1)
+        else:
+            kvq.append(c, knew, vnew, slot_dev)
         if ev is not None:
             ev[1].record()
         kvq.decode_split(c, q, bt_dev, cl_dev, max_ctx, scale, ws, out, None, args.partition_pages)
@@ -256,7 +319,7 @@ def main():
         "metric": "paged FP8/INT8 decode-attn KV GB/s (% of HBM peak) + tokens/s at 1 GPU",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "int8": "u8"}[w.dtype],
+        "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "int8": "u8", "kivi4": "u4"}[w.dtype],
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": w.num_kv_heads, "head_dim": d, "page_size": w.page_size,

@@ -111,7 +111,8 @@ typedef struct kvq_cache {
 size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size,
                         int32_t head_dim, int32_t which);
 
-/* Quantize-on-append (FP8 / INT8).
+/* Quantize-on-append (FP8 / INT8; a KVQ_INT4_KIVI cache returns
+ * KVQ_ERR_UNSUPPORTED, it has kvq_kivi_append).
  * k, v:          device bf16 [num_tokens][num_kv_heads][head_dim], contiguous.
  * slot_mapping:  device int32 [num_tokens]; slot = page*page_size + row; a
  *                negative slot (or one beyond the pool) skips that token.
@@ -120,6 +121,31 @@ size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size,
 kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,
                       const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
 
+/* KIVI-style INT4 append (cache->dtype == KVQ_INT4_KIVI): new tokens of each
+ * sequence enter the fp16 window; whole 32-token groups leave it, oldest
+ * first, once it would hold more than cache->residual tokens, and are written
+ * quantized (K per channel over the group, V per token) into the page that
+ * block_table[b][group index] names.  A sequence of n tokens thus holds its
+ * first n_q = 32 * floor(max(0, n - residual) / 32) tokens as INT4 pages and
+ * tokens [n_q, n) as fp16 window rows (token t at row t % window_tokens).
+ * k, v:           device bf16 [total new tokens][num_kv_heads][head_dim]; the
+ *                 rows of sequence b are [token_offsets[b], token_offsets[b+1]).
+ * token_offsets:  device int32 [num_seqs + 1], non-decreasing.
+ * context_lens:   device int32 [num_seqs]: tokens sequence b holds BEFORE this
+ *                 call (the caller adds the new count afterwards).
+ * block_table:    device int32 [num_seqs][max_pages_per_seq].
+ * max_new_tokens: host bound on token_offsets[b+1] - token_offsets[b] (grid
+ *                 size); larger counts are the caller's error.
+ * Sequence b uses window slot b (num_seqs <= cache->max_seqs).  fp16 window
+ * values are the bf16 inputs rounded to nearest-even; the quantizers read
+ * those fp16 values.  Requires page_size 32 and window_tokens >= residual + 32.
+ * KIVI (ryotta.opik.net "KV Cache 압축" section 3.1; molayo1419.me formats-table
+ * notes on mixed-precision 4-bit). */
+kvq_status kvq_kivi_append(const kvq_cache* cache, const void* k, const void* v,
+                           const int32_t* token_offsets, const int32_t* context_lens,
+                           const int32_t* block_table, int32_t max_pages_per_seq, int32_t num_seqs,
+                           int32_t max_new_tokens, hipStream_t stream);
+
 /* Workspace bytes that kvq_decode_attention / kvq_decode_split need for this
  * shape.  partition_pages as in kvq_decode_attention. */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
@@ -127,7 +153,8 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
                                       int32_t partition_pages, size_t* bytes);
 
 /* One decode step of attention for one query token per sequence, reading the
- * quantized paged cache (FP8 / INT8) with dequantization fused in:
+ * quantized paged cache (FP8 / INT8, or INT4 pages plus the fp16 window for
+ * KVQ_INT4_KIVI, sequence b reading window slot b) with dequantization fused in:
  *   out[b][h] = sum_t softmax_t(softmax_scale * q[b][h] . k^[t]) v^[t]
  * over every cached token t < context_lens[b] of KV head h / (num_q_heads /
  * num_kv_heads).  fp32 accumulation, flash-decoding split over the context.

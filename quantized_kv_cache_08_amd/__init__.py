@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI",
     "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
-    "KvqError", "Cache", "lib", "record_bytes", "append", "decode_workspace_bytes",
+    "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
     "decode_attention", "decode_split", "decode_reduce", "e4m3_encode", "status_string",
     "LIB_PATH",
 ]
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_record_bytes.argtypes = [_I32] * 5
         L.kvq_append.restype = ctypes.c_int
         L.kvq_append.argtypes = [ctypes.POINTER(CacheDesc), _P, _P, _P, _I32, _P]
+        L.kvq_kivi_append.restype = ctypes.c_int
+        L.kvq_kivi_append.argtypes = [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]
         L.kvq_decode_workspace_bytes.restype = ctypes.c_int
         L.kvq_decode_workspace_bytes.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32,
                                                  ctypes.POINTER(ctypes.c_size_t)]
@@ -147,6 +149,17 @@ def append(cache: Cache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.T
     """Quantize bf16 K/V rows [T][n_kv][d] into their slots (kvq_append)."""
     _check("kvq_append", lib().kvq_append(ctypes.byref(cache.desc), _ptr(k), _ptr(v), _ptr(slot_mapping),
                                           int(slot_mapping.numel()), _stream(stream)))
+
+
+def kivi_append(cache: Cache, k: torch.Tensor, v: torch.Tensor, token_offsets: torch.Tensor,
+                context_lens: torch.Tensor, block_table: torch.Tensor, max_new_tokens: int, stream=None) -> None:
+    """INT4 (KIVI) append (kvq_kivi_append): new bf16 rows [total][n_kv][d] of each
+    sequence (rows token_offsets[b]..token_offsets[b+1]); context_lens = tokens
+    held before the call."""
+    num_seqs = int(context_lens.numel())
+    _check("kvq_kivi_append", lib().kvq_kivi_append(
+        ctypes.byref(cache.desc), _ptr(k), _ptr(v), _ptr(token_offsets), _ptr(context_lens), _ptr(block_table),
+        int(block_table.shape[1]), num_seqs, int(max_new_tokens), _stream(stream)))
 
 
 def decode_workspace_bytes(cache: Cache, num_seqs: int, num_q_heads: int, max_context_len: int,

@@ -39,6 +39,7 @@
 //      transposed in registers with byte permutes before conversion.
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "splitk.h"
 
 namespace kvq {
 
@@ -55,11 +56,6 @@ struct ChunkBuf {
     u32x2_t kz[2];     // INT8 zero-points
     u32x2_t vz[2];
 };
-
-__device__ __forceinline__ int pages_of(int len, int max_ctx, int ps) {
-    len = len < 0 ? 0 : (len > max_ctx ? max_ctx : len);
-    return (len + ps - 1) / ps;
-}
 
 template <int DT, bool STATIC, int PS>
 __device__ __forceinline__ void process_segment(const SplitParams& p, const int b, const int h,
@@ -157,10 +153,14 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
         }
     };
 
+    // Only the last chunk of a segment can hold rows past the context end; its
+    // masking runs in branches that the empty volatile asm statements keep
+    // from being flattened into code that every chunk would execute.
     auto compute = [&](ChunkBuf& cb, const int c) {
         const int ctok = tok_base + c * 32;
         const bool tail = ctok + 32 > tok_end;
-        if (tail) {
+        if (__builtin_expect(tail, 0)) {
+            __asm__ volatile("");
             // rows past the end of the context may hold anything (including
             // E4M3 NaN patterns): clear them before they reach an MFMA
 #pragma unroll
@@ -211,7 +211,8 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
                 sc[hp][r] = s;
             }
         }
-        if (tail) {
+        if (__builtin_expect(tail, 0)) {
+            __asm__ volatile("");
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
@@ -227,7 +228,10 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[hp][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (__any(mx > m_used + kRescaleHeadroom)) {
+        if (__builtin_expect(__any(mx > m_used + kRescaleHeadroom), 0)) {
+            // rare: kept as a branch (an empty volatile asm stops the compiler
+            // from flattening it into straight-line code run every chunk)
+            __asm__ volatile("");
             const float m_new = fmaxf(m_used, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
             lsum *= alpha;
@@ -240,7 +244,7 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
                 for (int t = 0; t < 8; ++t) acc[t][r] *= ar;
             }
         }
-        float pp[2][4];
+        float pp[2][4], pzr[2][4];
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
 #pragma unroll
@@ -258,15 +262,27 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
                         vzr = (r & 1) ? bf16hi(zw) : bf16lo(zw);
                     }
                 }
-                float q = pr * vsr;
-                float qz = pr * vzr;
-                if (tail && ctok + 16 * hp + 4 * g + r >= tok_end) {
-                    q = 0.0f;
-                    qz = 0.0f;
-                }
-                pp[hp][r] = q;
-                if constexpr (DT == kINT8) pz += qz;
+                pp[hp][r] = pr * vsr;
+                pzr[hp][r] = pr * vzr;
             }
+        }
+        if (__builtin_expect(tail, 0)) {
+            // masked rows have p = 0, but their scale bytes may be anything
+            __asm__ volatile("");
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (ctok + 16 * hp + 4 * g + r >= tok_end) {
+                        pp[hp][r] = 0.0f;
+                        pzr[hp][r] = 0.0f;
+                    }
+        }
+        if constexpr (DT == kINT8) {
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pz += pzr[hp][r];
         }
 
         // ---- P' as bf16 hi + lo (A operands of PV)
@@ -373,82 +389,17 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
 
 template <int DT, bool STATIC, int PS>
 __global__ __launch_bounds__(256) void split_kernel(SplitParams p) {
-    extern __shared__ int s_pfx[];   // [num_seqs + 1]
-    __shared__ int s_wsum[4];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wid = tid >> 6;
-    const int B = p.num_seqs;
-
-    // ---- pages per sequence and their exclusive prefix sum (every workgroup)
-    const int per = (B + 255) / 256;
-    const int beg = min(tid * per, B);
-    const int end = min(beg + per, B);
-    int local = 0;
-    for (int i = beg; i < end; ++i) local += pages_of(p.context_lens[i], p.max_ctx, PS);
-    int incl = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) s_wsum[wid] = incl;
-    __syncthreads();
-    int run = incl - local;
-    for (int w = 0; w < wid; ++w) run += s_wsum[w];
-    for (int i = beg; i < end; ++i) {
-        s_pfx[i] = run;
-        run += pages_of(p.context_lens[i], p.max_ctx, PS);
-    }
-    if (tid == 0) s_pfx[B] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    __syncthreads();
-
-    const long long W = (long long)s_pfx[B] * p.n_kv;
-    long long chunk;
-    if (p.forced_chunk > 0) {
-        chunk = p.forced_chunk;
-    } else {
-        chunk = (W + p.total_waves - 1) / p.total_waves;
-        if (chunk < p.min_chunk) chunk = p.min_chunk;
-    }
-    if (blockIdx.x == 0) {
-        if (tid == 0) p.ws_header[0] = (int)chunk;
-        for (int i = tid; i <= B; i += 256) p.ws_pfx[i] = s_pfx[i];
-    }
-
-    const long long waves = (long long)gridDim.x * 4;
-    for (long long k = (long long)blockIdx.x * 4 + wid; k * chunk < W; k += waves) {
-        long long x = k * chunk;
-        const long long xend = min(x + chunk, W);
-        while (x < xend) {
-            int lo = 0, hi = B - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if ((long long)s_pfx[mid] * p.n_kv <= x) lo = mid;
-                else hi = mid - 1;
-            }
-            const int b = uniform(lo);
-            const int pb = uniform(s_pfx[b + 1] - s_pfx[b]);
-            const long long start_b = (long long)s_pfx[b] * p.n_kv;
-            const int h = uniform((int)((x - start_b) / pb));
-            const long long item_start = start_b + (long long)h * pb;
-            const long long item_end = item_start + pb;
-            const long long seg_end = min(xend, item_end);
-            const int page0 = uniform((int)(x - item_start));
-            const int page1 = uniform((int)(seg_end - item_start));
-            const long long first_seg = item_start / chunk;
-            const int n_seg = uniform((int)((item_end - 1) / chunk - first_seg + 1));
-            const int seg = uniform((int)(x / chunk - first_seg));
-            process_segment<DT, STATIC, PS>(p, b, h, page0, page1, seg, n_seg, lane);
-            x = seg_end;
-        }
-    }
+    for_each_segment<PS>(p, [&](int b, int h, int page0, int page1, int seg, int n_seg, int lane) {
+        process_segment<DT, STATIC, PS>(p, b, h, page0, page1, seg, n_seg, lane);
+    });
 }
 
 // Merge of the partial results of one (sequence, query head):
 //   L = max_i lse_i,  w_i = 2^(lse_i - L),  out = sum_i w_i o_i / sum_i w_i,
 //   lse = (L + log2 sum_i w_i) * ln 2.
-// One wave per (sequence, query head), two channels per lane.
+// One wave per (sequence, query head): the partial lse values are read one
+// per lane, and each lane merges two channels with eight partial rows in
+// flight at a time.
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & 63;
     const long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -460,8 +411,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const int pb = p.ws_pfx[b + 1] - p.ws_pfx[b];
     float* out = p.out + idx * kHeadDim + 2 * lane;
     if (pb == 0) {
-        out[0] = 0.0f;
-        out[1] = 0.0f;
+        *(float2*)out = make_float2(0.0f, 0.0f);
         if (p.lse && lane == 0) p.lse[idx] = -INFINITY;
         return;
     }
@@ -471,17 +421,37 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const float* pl = p.part_lse + idx * p.max_parts;
     const float* po = p.part_o + idx * p.max_parts * kHeadDim + 2 * lane;
     float L = -INFINITY;
-    for (int i = 0; i < n_seg; ++i) L = fmaxf(L, pl[i]);
+    for (int i = lane; i < n_seg; i += 64) L = fmaxf(L, pl[i]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L = fmaxf(L, __shfl_xor(L, o));
     float ws = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int i = 0; i < n_seg; ++i) {
-        const float w = __builtin_amdgcn_exp2f(pl[i] - L);
-        ws += w;
-        o0 += w * po[(size_t)i * kHeadDim];
-        o1 += w * po[(size_t)i * kHeadDim + 1];
+    for (int base = 0; base < n_seg; base += 64) {
+        const int cnt = min(64, n_seg - base);
+        const float wl = lane < cnt ? __builtin_amdgcn_exp2f(pl[base + lane] - L) : 0.0f;
+        ws += wl;
+        int i = 0;
+        for (; i + 8 <= cnt; i += 8) {
+            float2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *(const float2*)(po + (size_t)(base + i + u) * kHeadDim);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float w = __shfl(wl, i + u);
+                o0 += w * v[u].x;
+                o1 += w * v[u].y;
+            }
+        }
+        for (; i < cnt; ++i) {
+            const float2 v = *(const float2*)(po + (size_t)(base + i) * kHeadDim);
+            const float w = __shfl(wl, i);
+            o0 += w * v.x;
+            o1 += w * v.y;
+        }
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
     const float inv = 1.0f / ws;
-    out[0] = o0 * inv;
-    out[1] = o1 * inv;
+    *(float2*)out = make_float2(o0 * inv, o1 * inv);
     if (p.lse && lane == 0) p.lse[idx] = (L + __log2f(ws)) * kLn2;
 }
 

@@ -1,0 +1,551 @@
+// kivi.hip -- KIVI-style 4-bit KV cache (gfx950): K quantized per channel
+// over groups of 32 tokens, V per token, the most recent tokens kept in
+// fp16 ("KV Cache 압축", ryotta.opik.net, section 3.1 KIVI; "KV 캐시
+// 양자화(KV cache quantization) ...", molayo1419.me, formats-table notes on
+// mixed-precision 4-bit: K per channel for its channel outliers, V per
+// token), with attention over the quantized pages and the fp16 window fused
+// into one split-K decode kernel.
+//
+// Window rule: a sequence of n tokens holds its first
+//   n_q = 32 * floor(max(0, n - residual) / 32)
+// tokens as 4-bit groups (one 32-token group per page) and tokens [n_q, n)
+// as fp16 rows in a ring of `window` >= residual + 32 rows (token t at row
+// t % window).  Tokens leave the window whole groups at a time, oldest first.
+//
+// Quantizer (both K and V; 15 steps):  z = bf16 floor of the minimum,
+//   s = bf16 ceil of (max - z) / 15,  code = clamp(rne((x - z) / s), 0, 15),
+//   x^ = code * s + z, every "/" one IEEE float32 division.  The inputs are
+//   the fp16 values (bf16 input rounded to nearest-even fp16).
+//
+// Decode of one 32-token page, per wave (lane l: j = l % 16, g = l / 16):
+//   score_t = sum_c q_c (n_tc s_c + z_c) = sum_c n_tc (q_c s_c) + sum_c q_c z_c.
+//   q'_c = q_c s_c is the product of two bf16 values, at most 16 significant
+//   bits, so it splits exactly into bf16 hi + lo; codes enter the MFMA as the
+//   bf16 value 128 + n (one byte permute per pair), and the offset
+//   128 sum_c q'_c is removed, together with the zero-point term, through the
+//   accumulator's initial value: bias = sum_c q_c z_c - 128 sum_c q_c s_c,
+//   computed by one more small MFMA (rows z and s against q).
+//   PV: O += P'.(128 + n_v) with P' = p * s_t split into bf16 hi + lo; the
+//   offset 128 sum_t P'_t and the zero-point term sum_t p_t z_t are removed
+//   at the end.  fp16 window chunks use fp16 MFMAs on the exact fp16 values.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "splitk.h"
+
+namespace kvq {
+
+constexpr int kKiviBufferFlags = 0x00020000;
+constexpr float kKiviHeadroom = 8.0f;      // log2 units
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int kivi_nq(int n, int resid) {
+    const int over = n - resid;
+    return over <= 0 ? 0 : (over / kKiviGroup) * kKiviGroup;
+}
+
+__device__ __forceinline__ float f16_value(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
+    f16x2_t v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// ============================================================== append
+// Asymmetric 15-step quantizer of one value given the row's (z, s).
+__device__ __forceinline__ uint32_t kivi_code(float x, float zf, float sf) {
+#pragma clang fp contract(off)
+    if (sf == 0.0f) return 0u;
+    float t = rintf((x - zf) / sf);
+    t = fminf(fmaxf(t, 0.0f), 15.0f);
+    return (uint32_t)t;
+}
+
+// One workgroup quantizes one 32-token group of one (sequence, KV head): K
+// per channel (one thread per channel), V per token (one wave per 16 tokens,
+// two channels per lane).  Token rows come from the fp16 window (tokens held
+// before this call) or from the new bf16 rows (rounded to fp16).
+__global__ __launch_bounds__(128) void kivi_flush_kernel(KiviAppendParams p) {
+#pragma clang fp contract(off)
+    const int b = blockIdx.z;
+    const int h = blockIdx.y;
+    const int n0 = max(p.context_lens[b], 0);
+    const int m = p.offsets[b + 1] - p.offsets[b];
+    if (m <= 0) return;
+    const int n1 = n0 + m;
+    const int nq0 = kivi_nq(n0, p.residual);
+    const int nq1 = kivi_nq(n1, p.residual);
+    const int grp = nq0 / kKiviGroup + (int)blockIdx.x;
+    if (grp * kKiviGroup >= nq1 || grp >= p.max_pages_per_seq) return;
+    const int page = p.block_table[(size_t)b * p.max_pages_per_seq + grp];
+    if (page < 0 || page >= p.num_pages) return;
+    const int tid = threadIdx.x;
+    const size_t wrow0 = ((size_t)b * p.n_kv + h) * p.window;
+    const int in0 = p.offsets[b];
+
+    auto value = [&](const uint16_t* win, const uint16_t* in, int pos, int c) -> float {
+        if (pos < n0) return f16_value(win[(wrow0 + pos % p.window) * kHeadDim + c]);
+        const float x = bf16lo(in[((size_t)(in0 + pos - n0) * p.n_kv + h) * kHeadDim + c]);
+        return (float)(_Float16)x;
+    };
+
+    // ---- K: channel c over the group's 32 tokens
+    uint8_t* krec = p.k_pages + ((size_t)page * p.n_kv + h) * (size_t)p.rec_k;
+    {
+        const int c = tid;
+        float x[kKiviGroup];
+        float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < kKiviGroup; ++t) {
+            x[t] = value(p.k_window, p.k, grp * kKiviGroup + t, c);
+            lo = fminf(lo, x[t]);
+            hi = fmaxf(hi, x[t]);
+        }
+        const uint32_t zb = bf16_down_bits(lo);
+        const float zf = bf16lo(zb);
+        const uint32_t sb = bf16_up_bits((hi - zf) / 15.0f);
+        const float sf = bf16lo(sb);
+#pragma unroll
+        for (int t = 0; t < kKiviGroup; ++t) {
+            const uint32_t code = kivi_code(x[t], zf, sf);
+            const uint32_t other = (uint32_t)__shfl_xor((int)code, 1);
+            if ((c & 1) == 0) krec[t * (kHeadDim / 2) + (c >> 1)] = (uint8_t)(code | (other << 4));
+        }
+        *(uint16_t*)(krec + kKiviGroup * kHeadDim / 2 + 2 * c) = (uint16_t)sb;
+        *(uint16_t*)(krec + kKiviGroup * kHeadDim / 2 + 2 * kHeadDim + 2 * c) = (uint16_t)zb;
+    }
+
+    // ---- V: token t over its 128 channels
+    uint8_t* vrec = p.v_pages + ((size_t)page * p.n_kv + h) * (size_t)p.rec_v;
+    {
+        const int w = tid >> 6;
+        const int l = tid & 63;
+        for (int i = 0; i < kKiviGroup / 2; ++i) {
+            const int t = w * (kKiviGroup / 2) + i;
+            const int pos = grp * kKiviGroup + t;
+            const float x0 = value(p.v_window, p.v, pos, 2 * l);
+            const float x1 = value(p.v_window, p.v, pos, 2 * l + 1);
+            float lo = fminf(x0, x1), hi = fmaxf(x0, x1);
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                lo = fminf(lo, __shfl_xor(lo, o));
+                hi = fmaxf(hi, __shfl_xor(hi, o));
+            }
+            const uint32_t zb = bf16_down_bits(lo);
+            const float zf = bf16lo(zb);
+            const uint32_t sb = bf16_up_bits((hi - zf) / 15.0f);
+            const float sf = bf16lo(sb);
+            const uint32_t c0 = kivi_code(x0, zf, sf);
+            const uint32_t c1 = kivi_code(x1, zf, sf);
+            vrec[t * (kHeadDim / 2) + l] = (uint8_t)(c0 | (c1 << 4));
+            if (l == 0) {
+                *(uint16_t*)(vrec + kKiviGroup * kHeadDim / 2 + 2 * t) = (uint16_t)sb;
+                *(uint16_t*)(vrec + kKiviGroup * kHeadDim / 2 + 2 * kKiviGroup + 2 * t) = (uint16_t)zb;
+            }
+        }
+    }
+}
+
+// New tokens that stay in full precision: fp16 rows into the window ring.
+// 16 threads per (token, KV head) row, 8 channels each.  Runs after the
+// flush kernel, which may still read window rows this kernel overwrites.
+__global__ __launch_bounds__(256) void kivi_window_kernel(KiviAppendParams p) {
+    const int b = blockIdx.z;
+    const int h = blockIdx.y;
+    const int i = (int)blockIdx.x * 16 + (int)(threadIdx.x >> 4);
+    const int part = threadIdx.x & 15;
+    const int m = p.offsets[b + 1] - p.offsets[b];
+    if (i >= m) return;
+    const int n0 = max(p.context_lens[b], 0);
+    const int pos = n0 + i;
+    if (pos < kivi_nq(n0 + m, p.residual)) return;      // quantized straight from the input
+    const size_t src = ((size_t)(p.offsets[b] + i) * p.n_kv + h) * kHeadDim + 8 * part;
+    const size_t dst = (((size_t)b * p.n_kv + h) * p.window + pos % p.window) * kHeadDim + 8 * part;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+        const u32x4_t w = *(const u32x4_t*)((kv ? p.v : p.k) + src);
+        u32x4_t o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_f16_rne(bf16lo(w[e]), bf16hi(w[e]));
+        *(u32x4_t*)((kv ? p.v_window : p.k_window) + dst) = o;
+    }
+}
+
+hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream) {
+    if (p.num_seqs <= 0 || p.max_new <= 0) return hipSuccess;
+    const int groups = (p.max_new + kKiviGroup - 1) / kKiviGroup + 1;
+    hipLaunchKernelGGL(kivi_flush_kernel, dim3(groups, p.n_kv, p.num_seqs), dim3(128), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kivi_window_kernel, dim3((p.max_new + 15) / 16, p.n_kv, p.num_seqs), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+// ============================================================== decode
+struct KiviBuf {
+    u32x4_t kc[2];     // [half]: K codes of token 16 hp + j, channels [32g, 32g+32)
+    u32x4_t ks[4];     // bf16 K scales of channels 32g + 8kb + [0, 8)
+    u32x4_t kz[4];     // bias operand: lane j = 0 zero-points, j = 1 scales, else 0
+    uint32_t vc[2][4]; // [half][r]: V codes of token 16 hp + 4g + r, channels [8j, 8j+8)
+    u32x2_t vs[2];     // bf16 V scales of tokens 16 hp + 4g + [0, 4)
+    u32x2_t vz[2];
+};
+
+struct KiviState {
+    f32x4_t acc[8];
+    float m_used, lsum, pz, pcorr;
+};
+
+// Online-softmax update with the scores of one 32-token chunk (exp2 domain);
+// returns p per (half, r) in pp.  All four lane groups hold the same head.
+__device__ __forceinline__ void kivi_softmax(KiviState& st, float (&sc)[2][4], float (&pp)[2][4],
+                                             const int g) {
+    float mx = sc[0][0];
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[hp][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__builtin_expect(__any(mx > st.m_used + kKiviHeadroom), 0)) {
+        __asm__ volatile("");   // keep the rare rescale a branch, not straight-line code
+        const float m_new = fmaxf(st.m_used, mx);
+        const float alpha = __builtin_amdgcn_exp2f(st.m_used - m_new);
+        st.lsum *= alpha;
+        st.pz *= alpha;
+        st.pcorr *= alpha;
+        st.m_used = m_new;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st.acc[t][r] *= ar;
+        }
+    }
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(sc[hp][r] - st.m_used);
+            st.lsum += pr;
+            pp[hp][r] = pr;
+        }
+}
+
+__device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const int b, const int h,
+                                             const int page0, const int page1, const int seg,
+                                             const int n_seg, const int lane) {
+    const SplitParams& p = kp.s;
+    const int j = lane & 15;
+    const int g = lane >> 4;
+    const int G = p.group;
+    const int len = min(max(p.context_lens[b], 0), p.max_ctx);
+    const int nq = kivi_nq(len, kp.residual);
+    const int pq = nq / kKiviGroup;
+
+    // query (B operand): head j, channels 32g + 8kb + [0, 8)
+    u32x4_t qb[4];
+    if (j < G) {
+        const u32x4_t* qp =
+            (const u32x4_t*)(p.q + ((size_t)b * p.n_q + (size_t)h * G + j) * kHeadDim + 32 * g);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qb[kb] = qp[kb];
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qb[kb] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+
+    KiviState st;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m_used = -INFINITY;
+    st.lsum = 0.0f;
+    st.pz = 0.0f;
+    st.pcorr = 0.0f;
+
+    const int* bt = p.block_table + (size_t)b * p.max_pages_per_seq;
+    const int qend = min(page1, pq);            // quantized pages of this segment: [page0, qend)
+    const int n_q = qend - page0;
+    const uint32_t kC = 0x43434343u;           // bf16 high byte of 128 + n
+
+    const int off_kc = j * (kHeadDim / 2) + 16 * g;
+    const int off_ks = kKiviGroup * kHeadDim / 2 + 64 * g;
+    const int off_kz = (j == 0) ? off_ks + 2 * kHeadDim : (j == 1 ? off_ks : (int)p.rec_k);
+    const int off_vc = 4 * g * (kHeadDim / 2) + 4 * j;
+    const int off_vs = kKiviGroup * kHeadDim / 2 + 8 * g;
+
+    auto load = [&](KiviBuf& cb, const int c) {
+        const bool live = c < n_q;
+        const int pidx = page0 + min(c, max(n_q - 1, 0));
+        const int page = min(max(bt[pidx], 0), p.num_pages - 1);
+        const size_t rec_idx = (size_t)page * p.n_kv + h;
+        const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.k_pages + rec_idx * (size_t)p.rec_k), (short)0, live ? (int)p.rec_k : 0,
+            kKiviBufferFlags);
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.v_pages + rec_idx * (size_t)p.rec_v), (short)0, live ? (int)p.rec_v : 0,
+            kKiviBufferFlags);
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp)
+            cb.kc[hp] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_kc + hp * 16 * (kHeadDim / 2), 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            cb.ks[kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_ks + 16 * kb, 0, 0);
+            cb.kz[kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_kz + 16 * kb, 0, 0);
+        }
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                cb.vc[hp][r] = __builtin_amdgcn_raw_buffer_load_b32(
+                    rv, off_vc + (16 * hp + r) * (kHeadDim / 2), 0, 0);
+            cb.vs[hp] = __builtin_amdgcn_raw_buffer_load_b64(rv, off_vs + 32 * hp, 0, 0);
+            cb.vz[hp] = __builtin_amdgcn_raw_buffer_load_b64(rv, off_vs + 2 * kKiviGroup + 32 * hp, 0, 0);
+        }
+    };
+
+    auto compute_quant = [&](KiviBuf& cb) {
+        // bias = sum_c q_c z_c - 128 sum_c q_c s_c for head j (rows 0, 1 of an MFMA)
+        f32x4_t d2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) d2 = mfma_16x16x32_bf16(cb.kz[kb], qb[kb], d2);
+        const float bias = __shfl(d2[0] - 128.0f * d2[1], j);
+
+        // q' = q s (exact as bf16 hi + lo), slots ordered like the code bytes
+        u32x4_t bh[4], bl[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            float qs[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qs[2 * i] = bf16lo(qb[kb][i]) * bf16lo(cb.ks[kb][i]);
+                qs[2 * i + 1] = bf16hi(qb[kb][i]) * bf16hi(cb.ks[kb][i]);
+            }
+            const int ord[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a0 = qs[ord[2 * e]], a1 = qs[ord[2 * e + 1]];
+                const uint32_t hw = pack_bf16_rne(a0, a1);
+                bh[kb][e] = hw;
+                bl[kb][e] = pack_bf16_rne(a0 - bf16lo(hw), a1 - bf16hi(hw));
+            }
+        }
+
+        float sc[2][4];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+            f32x4_t d = {bias, bias, bias, bias};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint32_t w = cb.kc[hp][kb];
+                const uint32_t x = w & 0x0F0F0F0Fu;
+                const uint32_t y = (w >> 4) & 0x0F0F0F0Fu;
+                const u32x4_t a = {perm(kC, x, 0x04010400u), perm(kC, y, 0x04010400u),
+                                   perm(kC, x, 0x04030402u), perm(kC, y, 0x04030402u)};
+                d = mfma_16x16x32_bf16(a, bh[kb], d);
+                d = mfma_16x16x32_bf16(a, bl[kb], d);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[hp][r] = d[r] * p.score_scale;
+        }
+
+        float pp[2][4];
+        kivi_softmax(st, sc, pp, g);
+
+        // P' = p s_t as bf16 hi + lo; offset and zero-point sums
+        u32x4_t ahi, alo;
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+#pragma unroll
+            for (int rp = 0; rp < 2; ++rp) {
+                const uint32_t sw = cb.vs[hp][rp];
+                const uint32_t zw = cb.vz[hp][rp];
+                const float p0 = pp[hp][2 * rp], p1 = pp[hp][2 * rp + 1];
+                const float a0 = p0 * bf16lo(sw), a1 = p1 * bf16hi(sw);
+                st.pz += p0 * bf16lo(zw) + p1 * bf16hi(zw);
+                const uint32_t hw = pack_bf16_rne(a0, a1);
+                const uint32_t lw = pack_bf16_rne(a0 - bf16lo(hw), a1 - bf16hi(hw));
+                ahi[2 * hp + rp] = hw;
+                alo[2 * hp + rp] = lw;
+                st.pcorr += (bf16lo(hw) + bf16hi(hw)) + (bf16lo(lw) + bf16hi(lw));
+            }
+        }
+
+        // V codes: channel 8j + t, tokens 16 hp + 4g + r
+        uint32_t xs[2][4], ys[2][4];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                xs[hp][r] = cb.vc[hp][r] & 0x0F0F0F0Fu;
+                ys[hp][r] = (cb.vc[hp][r] >> 4) & 0x0F0F0F0Fu;
+            }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const uint32_t by = (uint32_t)(t >> 1);
+            const uint32_t sel = by | (0x0Cu << 8) | ((4u + by) << 16) | (0x0Cu << 24);
+            u32x4_t bv;
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                for (int rp = 0; rp < 2; ++rp) {
+                    const uint32_t s0 = (t & 1) ? ys[hp][2 * rp] : xs[hp][2 * rp];
+                    const uint32_t s1 = (t & 1) ? ys[hp][2 * rp + 1] : xs[hp][2 * rp + 1];
+                    bv[2 * hp + rp] = perm(s1, s0, sel) | 0x43004300u;
+                }
+            st.acc[t] = mfma_16x16x32_bf16(ahi, bv, st.acc[t]);
+            st.acc[t] = mfma_16x16x32_bf16(alo, bv, st.acc[t]);
+        }
+    };
+
+    // ---- quantized pages, loads of the next page in flight during compute
+    if (n_q > 0) {
+        KiviBuf b0, b1;
+        load(b0, 0);
+        for (int c = 0;;) {
+            load(b1, c + 1);
+            compute_quant(b0);
+            if (++c >= n_q) break;
+            load(b0, c + 1);
+            compute_quant(b1);
+            if (++c >= n_q) break;
+        }
+    }
+
+    // ---- fp16 window chunks: tokens nq + 32 (c - pq) + [0, 32)
+    const int rfirst = max(page0, pq);
+    if (rfirst < page1) {
+        u32x4_t qh[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qh[kb][i] = pack_f16_rne(bf16lo(qb[kb][i]), bf16hi(qb[kb][i]));
+        const uint16_t* kw = (const uint16_t*)kp.k_window + ((size_t)b * p.n_kv + h) * kp.window * kHeadDim;
+        const uint16_t* vw = (const uint16_t*)kp.v_window + ((size_t)b * p.n_kv + h) * kp.window * kHeadDim;
+        for (int c = rfirst; c < page1; ++c) {
+            const int rbase = nq + kKiviGroup * (c - pq);
+            float sc[2][4];
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+                const int pos = rbase + 16 * hp + j;
+                u32x4_t kr[4];
+                if (pos < len) {
+                    const u32x4_t* src = (const u32x4_t*)(kw + (size_t)(pos % kp.window) * kHeadDim + 32 * g);
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) kr[kb] = src[kb];
+                } else {
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) kr[kb] = u32x4_t{0u, 0u, 0u, 0u};
+                }
+                f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) d = mfma_16x16x32_f16(kr[kb], qh[kb], d);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sc[hp][r] = (rbase + 16 * hp + 4 * g + r < len) ? d[r] * p.score_scale : -INFINITY;
+            }
+            float pp[2][4];
+            kivi_softmax(st, sc, pp, g);
+            u32x4_t ahi, alo;
+            u32x4_t vr[2][4];
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int pos = rbase + 16 * hp + 4 * g + r;
+                    if (pos < len)
+                        vr[hp][r] = *(const u32x4_t*)(vw + (size_t)(pos % kp.window) * kHeadDim + 8 * j);
+                    else
+                        vr[hp][r] = u32x4_t{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int rp = 0; rp < 2; ++rp) {
+                    const float a0 = pp[hp][2 * rp], a1 = pp[hp][2 * rp + 1];
+                    const uint32_t hw = pack_f16_rne(a0, a1);
+                    ahi[2 * hp + rp] = hw;
+                    alo[2 * hp + rp] = pack_f16_rne(a0 - f16_value(hw & 0xFFFFu), a1 - f16_value(hw >> 16));
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+                u32x4_t bv;
+#pragma unroll
+                for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                    for (int rp = 0; rp < 2; ++rp)
+                        bv[2 * hp + rp] = perm(vr[hp][2 * rp + 1][t >> 1], vr[hp][2 * rp][t >> 1], sel);
+                st.acc[t] = mfma_16x16x32_f16(ahi, bv, st.acc[t]);
+                st.acc[t] = mfma_16x16x32_f16(alo, bv, st.acc[t]);
+            }
+        }
+    }
+
+    // ---- epilogue (same output format as the FP8 / INT8 kernel)
+    float lsum = st.lsum, pz = st.pz, pcorr = st.pcorr;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    pz += __shfl_xor(pz, 16);
+    pz += __shfl_xor(pz, 32);
+    pcorr += __shfl_xor(pcorr, 16);
+    pcorr += __shfl_xor(pcorr, 32);
+    const size_t row0 = (size_t)b * p.n_q + (size_t)h * G;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int head = 4 * g + r;
+        const float lr = __shfl(lsum, head & 15);
+        const float add = __shfl(pz, head & 15) - 128.0f * __shfl(pcorr, head & 15);
+        if (head < G) {
+            const float inv = 1.0f / lr;
+            f32x4_t o0, o1;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                o0[t] = (st.acc[t][r] + add) * inv;
+                o1[t] = (st.acc[t + 4][r] + add) * inv;
+            }
+            float* dst = (n_seg == 1)
+                             ? p.out + (row0 + head) * kHeadDim + 8 * j
+                             : p.part_o + ((row0 + head) * p.max_parts + seg) * kHeadDim + 8 * j;
+            *(f32x4_t*)dst = o0;
+            *(f32x4_t*)(dst + 4) = o1;
+        }
+    }
+    if (g == 0 && j < G) {
+        const float l2 = st.m_used + __log2f(lsum);
+        if (n_seg == 1) {
+            if (p.lse) p.lse[row0 + j] = l2 * kLn2;
+        } else {
+            p.part_lse[(row0 + j) * p.max_parts + seg] = l2;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void kivi_split_kernel(KiviSplitParams kp) {
+    for_each_segment<kKiviGroup>(kp.s, [&](int b, int h, int page0, int page1, int seg, int n_seg, int lane) {
+        kivi_segment(kp, b, h, page0, page1, seg, n_seg, lane);
+    });
+}
+
+hipError_t kivi_split_occupancy(size_t lds_bytes, int* blocks_per_cu) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)&kivi_split_kernel,
+                                                        kSplitThreads, lds_bytes);
+}
+
+hipError_t launch_kivi_split(const KiviSplitParams& p, int grid, size_t lds_bytes, hipStream_t stream) {
+    if (grid <= 0) return hipSuccess;
+    KiviSplitParams args = p;
+    void* kargs[] = {&args};
+    return hipLaunchKernel((const void*)&kivi_split_kernel, dim3(grid), dim3(kSplitThreads), kargs,
+                           lds_bytes, stream);
+}
+
+}  // namespace kvq

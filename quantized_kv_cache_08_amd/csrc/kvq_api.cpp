@@ -39,21 +39,30 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool valid_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
-// Common descriptor checks for the FP8 / INT8 paths.
-kvq_status check_cache(const kvq_cache* c) {
+// Descriptor checks.  kivi: whether the INT4 window layout is accepted (the
+// decode entry points) or refused as unsupported (the slot-based append).
+kvq_status check_cache(const kvq_cache* c, bool kivi) {
     if (!c) return KVQ_ERR_INVALID;
-    if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_INT8_ASYM) {
-        return c->dtype == KVQ_INT4_KIVI ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
-    }
+    if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_INT8_ASYM && c->dtype != KVQ_INT4_KIVI)
+        return KVQ_ERR_INVALID;
     if (c->scale_mode < KVQ_SCALE_PER_TENSOR || c->scale_mode > KVQ_SCALE_PER_TOKEN_HEAD)
         return KVQ_ERR_INVALID;
-    if (c->dtype == KVQ_INT8_ASYM && c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD)
-        return KVQ_ERR_UNSUPPORTED;
     if (c->num_pages <= 0 || c->num_kv_heads <= 0 || c->page_size <= 0 || c->head_dim <= 0)
         return KVQ_ERR_INVALID;
-    if (c->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
-    if (c->page_size != 16 && c->page_size != 32) return KVQ_ERR_UNSUPPORTED;
     if (!c->k_pages || !c->v_pages) return KVQ_ERR_INVALID;
+    if (c->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
+    if (c->dtype == KVQ_INT4_KIVI) {
+        if (!kivi) return KVQ_ERR_UNSUPPORTED;
+        if (c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD || c->page_size != kKiviGroup)
+            return KVQ_ERR_UNSUPPORTED;
+        if (!c->k_window || !c->v_window || c->max_seqs <= 0 || c->residual < 0 ||
+            c->window_tokens < c->residual + kKiviGroup)
+            return KVQ_ERR_INVALID;
+        return KVQ_OK;
+    }
+    if (c->dtype == KVQ_INT8_ASYM && c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD)
+        return KVQ_ERR_UNSUPPORTED;
+    if (c->page_size != 16 && c->page_size != 32) return KVQ_ERR_UNSUPPORTED;
     if (c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD && !c->static_scales) return KVQ_ERR_INVALID;
     return KVQ_OK;
 }
@@ -96,7 +105,7 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
                         const int32_t* context_lens, int32_t max_context_len,
                         int32_t partition_pages, void* workspace, size_t workspace_bytes,
                         float* out, Plan* plan) {
-    kvq_status st = check_cache(c);
+    kvq_status st = check_cache(c, true);
     if (st != KVQ_OK) return st;
     if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_pages_per_seq < 0 ||
         partition_pages < 0)
@@ -106,6 +115,7 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
     if ((long long)max_context_len > (long long)max_pages_per_seq * c->page_size)
         return KVQ_ERR_INVALID;
     if (num_seqs > 16383) return KVQ_ERR_UNSUPPORTED;   // prefix table lives in LDS
+    if (c->dtype == KVQ_INT4_KIVI && num_seqs > c->max_seqs) return KVQ_ERR_INVALID;
     if (num_seqs == 0) return KVQ_OK;
     if (!q || !block_table || !context_lens || !out || !workspace) return KVQ_ERR_INVALID;
     *plan = make_plan(c->page_size, num_seqs, num_q_heads, max_context_len, partition_pages);
@@ -150,16 +160,27 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     p.score_scale = softmax_scale * 1.4426950408889634f;
 
     const size_t lds = ((size_t)num_seqs + 1) * sizeof(int32_t);
+    const bool kivi = c->dtype == KVQ_INT4_KIVI;
     int per_cu = 0;
-    if (split_occupancy(c->dtype, is_static, c->page_size, lds, &per_cu) != hipSuccess)
-        return KVQ_ERR_HIP;
+    hipError_t e = kivi ? kivi_split_occupancy(lds, &per_cu)
+                        : split_occupancy(c->dtype, is_static, c->page_size, lds, &per_cu);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
     const int cus = device_cus();
     if (cus <= 0 || per_cu <= 0) return KVQ_ERR_HIP;
     const int grid = per_cu * cus;
     p.total_waves = grid * (kSplitThreads / 64);
-    if (launch_split(c->dtype, is_static, c->page_size, p, grid, lds, stream) != hipSuccess)
-        return KVQ_ERR_HIP;
-    return KVQ_OK;
+    if (kivi) {
+        KiviSplitParams kp{};
+        kp.s = p;
+        kp.k_window = (const uint16_t*)c->k_window;
+        kp.v_window = (const uint16_t*)c->v_window;
+        kp.window = c->window_tokens;
+        kp.residual = c->residual;
+        e = launch_kivi_split(kp, grid, lds, stream);
+    } else {
+        e = launch_split(c->dtype, is_static, c->page_size, p, grid, lds, stream);
+    }
+    return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 kvq_status run_reduce(const kvq_cache* c, int32_t num_seqs, int32_t num_q_heads, const Plan& pl,
@@ -208,7 +229,7 @@ size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size, in
 
 kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,
                       const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream) {
-    kvq_status st = check_cache(cache);
+    kvq_status st = check_cache(cache, false);
     if (st != KVQ_OK) return st;
     if (num_tokens < 0) return KVQ_ERR_INVALID;
     if (num_tokens == 0) return KVQ_OK;
@@ -233,6 +254,45 @@ kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,
     if (launch_append(cache->dtype, is_static, cache->page_size, p, stream) != hipSuccess)
         return KVQ_ERR_HIP;
     return KVQ_OK;
+}
+
+kvq_status kvq_kivi_append(const kvq_cache* cache, const void* k, const void* v,
+                           const int32_t* token_offsets, const int32_t* context_lens,
+                           const int32_t* block_table, int32_t max_pages_per_seq, int32_t num_seqs,
+                           int32_t max_new_tokens, hipStream_t stream) {
+    if (!cache) return KVQ_ERR_INVALID;
+    if (cache->dtype != KVQ_INT4_KIVI) return check_cache(cache, false) == KVQ_OK
+                                                  ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
+    kvq_status st = check_cache(cache, true);
+    if (st != KVQ_OK) return st;
+    if (num_seqs < 0 || max_new_tokens < 0 || max_pages_per_seq < 0) return KVQ_ERR_INVALID;
+    if (num_seqs > cache->max_seqs) return KVQ_ERR_INVALID;
+    if (num_seqs > 65535 || cache->num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || max_new_tokens == 0) return KVQ_OK;
+    if (!k || !v || !token_offsets || !context_lens || !block_table || max_pages_per_seq == 0)
+        return KVQ_ERR_INVALID;
+    KiviAppendParams p{};
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.offsets = token_offsets;
+    p.context_lens = context_lens;
+    p.block_table = block_table;
+    p.k_pages = (uint8_t*)cache->k_pages;
+    p.v_pages = (uint8_t*)cache->v_pages;
+    p.k_window = (uint16_t*)cache->k_window;
+    p.v_window = (uint16_t*)cache->v_window;
+    p.rec_k = (long long)kvq_record_bytes(cache->dtype, cache->scale_mode, cache->page_size,
+                                          cache->head_dim, 0);
+    p.rec_v = (long long)kvq_record_bytes(cache->dtype, cache->scale_mode, cache->page_size,
+                                          cache->head_dim, 1);
+    p.num_seqs = num_seqs;
+    p.n_kv = cache->num_kv_heads;
+    p.max_pages_per_seq = max_pages_per_seq;
+    p.window = cache->window_tokens;
+    p.residual = cache->residual;
+    p.max_new = max_new_tokens;
+    p.num_pages = cache->num_pages;
+    return launch_kivi_append(p, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,

@@ -12,6 +12,7 @@ constexpr int kHeadDim = 128;
 constexpr int kMaxParts = 32;      // partial results kept per (sequence, query head)
 constexpr int kMinChunkPages = 4;  // smallest automatic work range per wave
 constexpr int kSplitThreads = 256; // 4 waves per workgroup
+constexpr int kKiviGroup = 32;     // INT4 path: tokens per K group = page size
 
 struct AppendParams {
     const uint16_t* k;             // bf16 [T][n_kv][128]

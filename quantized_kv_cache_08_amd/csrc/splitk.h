@@ -1,0 +1,106 @@
+// splitk.h -- work distribution shared by the split-K decode kernels.
+//
+// Flash-decoding over context partitions, balanced across the whole batch:
+// each (sequence, KV head) is an "item" of pages (32-token chunks for the
+// INT4 window path, which counts its fp16 tail as trailing chunks); the items
+// are laid end to end and the resulting page space is cut into equal ranges,
+// one per resident wave.  A wave walks its range item by item and calls the
+// segment processor once per (item, sub-range).  A segment that covers a
+// whole item writes the final result; otherwise it writes partial results that
+// the reduce kernel merges with log-sum-exp weights.
+#pragma once
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+// Pages of context a sequence of `len` tokens occupies (len clamped to max_ctx).
+__device__ __forceinline__ int pages_of(int len, int max_ctx, int ps) {
+    len = len < 0 ? 0 : (len > max_ctx ? max_ctx : len);
+    return (len + ps - 1) / ps;
+}
+
+// Calls seg(b, h, page0, page1, seg_index, n_segments, lane) for every
+// segment of this wave's ranges.  Must be called by every thread of a
+// workgroup of kSplitThreads threads (it synchronises once); the dynamic LDS
+// holds num_seqs + 1 ints.
+template <int PS, typename Seg>
+__device__ __forceinline__ void for_each_segment(const SplitParams& p, Seg&& seg) {
+    extern __shared__ int s_pfx[];   // [num_seqs + 1]
+    __shared__ int s_wsum[kSplitThreads / 64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    const int B = p.num_seqs;
+
+    // pages per sequence and their exclusive prefix sum (every workgroup)
+    const int per = (B + kSplitThreads - 1) / kSplitThreads;
+    const int beg = min(tid * per, B);
+    const int end = min(beg + per, B);
+    int local = 0;
+    for (int i = beg; i < end; ++i) local += pages_of(p.context_lens[i], p.max_ctx, PS);
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_wsum[wid] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wid; ++w) run += s_wsum[w];
+    for (int i = beg; i < end; ++i) {
+        s_pfx[i] = run;
+        run += pages_of(p.context_lens[i], p.max_ctx, PS);
+    }
+    if (tid == 0) {
+        int tot = 0;
+        for (int w = 0; w < kSplitThreads / 64; ++w) tot += s_wsum[w];
+        s_pfx[B] = tot;
+    }
+    __syncthreads();
+
+    const long long W = (long long)s_pfx[B] * p.n_kv;
+    long long chunk;
+    if (p.forced_chunk > 0) {
+        chunk = p.forced_chunk;
+    } else {
+        chunk = (W + p.total_waves - 1) / p.total_waves;
+        if (chunk < p.min_chunk) chunk = p.min_chunk;
+    }
+    if (blockIdx.x == 0) {
+        if (tid == 0) p.ws_header[0] = (int)chunk;
+        for (int i = tid; i <= B; i += kSplitThreads) p.ws_pfx[i] = s_pfx[i];
+    }
+
+    const long long waves = (long long)gridDim.x * (kSplitThreads / 64);
+    for (long long k = (long long)blockIdx.x * (kSplitThreads / 64) + wid; k * chunk < W; k += waves) {
+        long long x = k * chunk;
+        const long long xend = min(x + chunk, W);
+        while (x < xend) {
+            int lo = 0, hi = B - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((long long)s_pfx[mid] * p.n_kv <= x) lo = mid;
+                else hi = mid - 1;
+            }
+            const int b = uniform(lo);
+            const int pb = uniform(s_pfx[b + 1] - s_pfx[b]);
+            const long long start_b = (long long)s_pfx[b] * p.n_kv;
+            const int h = uniform((int)((x - start_b) / pb));
+            const long long item_start = start_b + (long long)h * pb;
+            const long long item_end = item_start + pb;
+            const long long seg_end = min(xend, item_end);
+            const int page0 = uniform((int)(x - item_start));
+            const int page1 = uniform((int)(seg_end - item_start));
+            const long long first_seg = item_start / chunk;
+            const int n_seg = uniform((int)((item_end - 1) / chunk - first_seg + 1));
+            const int segi = uniform((int)(x / chunk - first_seg));
+            seg(b, h, page0, page1, segi, n_seg, lane);
+            x = seg_end;
+        }
+    }
+}
+
+}  // namespace kvq

@@ -117,3 +117,129 @@ def allclose_report(got: np.ndarray, ref: np.ndarray, atol=2e-3, rtol=1e-2):
     ok = bool(np.all(diff <= atol + rtol * np.abs(ref)))
     rel = diff / np.maximum(np.abs(ref), 1e-30)
     return ok, float(diff.max()) if diff.size else 0.0, float(rel.max()) if rel.size else 0.0
+
+
+# ------------------------------------------------------------------ KIVI (INT4 + fp16 window)
+@dataclass
+class BuiltKivi:
+    w: synthetic.Workload
+    cache: kvq.Cache
+    lens: np.ndarray
+    layout: synthetic.PageLayout
+    block_table: torch.Tensor
+    context_lens: torch.Tensor
+    q: torch.Tensor
+    max_ctx: int
+
+
+def kivi_plan(lens: np.ndarray, singles: int = 37, bulk_frac: float = 0.6) -> List[np.ndarray]:
+    """Per-call new-token counts: one bulk call, then `singles` one-token steps, then the rest."""
+    lens = np.asarray(lens, dtype=np.int64)
+    bulk = (lens * bulk_frac).astype(np.int64)
+    single = np.minimum(lens - bulk, singles)
+    rest = lens - bulk - single
+    calls = [bulk]
+    for i in range(singles):
+        calls.append((single > i).astype(np.int64))
+    calls.append(rest)
+    return [c for c in calls if c.sum() > 0]
+
+
+def build_kivi(w: synthetic.Workload, lens: Optional[np.ndarray] = None, plan=None, shuffle: Optional[bool] = None,
+               device="cuda", fill: int = SENTINEL, max_chunk: int = 1 << 14) -> BuiltKivi:
+    """Fill a KIVI cache through kvq_kivi_append following `plan` (list of per-call counts)."""
+    lens = synthetic.seq_lens(w) if lens is None else np.asarray(lens, dtype=np.int64)
+    B = len(lens)
+    layout = synthetic.page_layout(w, lens, w.page_size, shuffle)
+    cache = kvq.Cache(kvq.KVQ_INT4_KIVI, max(1, layout.num_pages), w.num_kv_heads, w.page_size, w.head_dim,
+                      kvq.KVQ_SCALE_PER_TOKEN_HEAD, device=device, fill=fill, max_seqs=B, residual=w.resid)
+    bt = torch.from_numpy(layout.block_table).to(device)
+    plan = kivi_plan(lens) if plan is None else plan
+    held = np.zeros(B, dtype=np.int64)
+    for counts in plan:
+        counts = np.asarray(counts, dtype=np.int64)
+        # long calls are split so that the generated tensors stay small
+        while counts.sum() > 0:
+            step = np.minimum(counts, max_chunk)
+            ks, vs = [], []
+            for b in range(B):
+                if step[b]:
+                    k, v = synthetic.gen_kv(w, b, int(held[b]), int(step[b]), device)
+                    ks.append(k)
+                    vs.append(v)
+            k = torch.cat(ks).contiguous()
+            v = torch.cat(vs).contiguous()
+            offs = torch.from_numpy(np.concatenate([[0], np.cumsum(step)]).astype(np.int32)).to(device)
+            cl = torch.from_numpy(held.astype(np.int32)).to(device)
+            kvq.kivi_append(cache, k, v, offs, cl, bt, int(step.max()))
+            held += step
+            counts = counts - step
+    assert np.array_equal(held, lens)
+    cl = torch.from_numpy(lens.astype(np.int32)).to(device)
+    q = synthetic.gen_q(w, device, batch=B)
+    return BuiltKivi(w, cache, lens, layout, bt, cl, q, int(lens.max()) if B else 0)
+
+
+def kivi_oracle_seq(bt: BuiltKivi, b: int, softmax_scale=None):
+    """Oracle KIVI state of every KV head of sequence b plus its fp64 attention."""
+    w = bt.w
+    T = int(bt.lens[b])
+    k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
+    k16 = O.bf16_to_f16_bits(u16(k))          # [T][n_kv][d]
+    v16 = O.bf16_to_f16_bits(u16(v))
+    heads = [O.kivi_stream(k16[:, h], v16[:, h], w.resid, w.page_size) for h in range(w.num_kv_heads)]
+    kd = np.zeros((T, w.num_kv_heads, w.head_dim))
+    vd = np.zeros((T, w.num_kv_heads, w.head_dim))
+    for h, st in enumerate(heads):
+        kd[:, h], vd[:, h] = O.kivi_dequant(st, w.page_size)
+    q = O.bf16_value(u16(synthetic.gen_q(w, "cpu", batch=len(bt.lens))[b])).astype(np.float64)
+    scale = 1.0 / math.sqrt(w.head_dim) if softmax_scale is None else softmax_scale
+    out, lse = O.attention(q, kd, vd, scale)
+    return dict(heads=heads, out=out, lse=lse, k_hat=kd, v_hat=vd)
+
+
+def kivi_read_seq(bt: BuiltKivi, b: int):
+    """Device state of sequence b read through the documented layout: per KV head
+    K codes [nq][d] (one code per byte), K s/z [nq/32][d], V codes [nq][d], V s/z [nq],
+    and the fp16 window rows of tokens [nq, T) (bits)."""
+    w = bt.w
+    ps, d, R = w.page_size, w.head_dim, w.resid
+    T = int(bt.lens[b])
+    nq = O.kivi_quantized_count(T, R, ps)
+    npg = nq // ps
+    pages = torch.from_numpy(bt.layout.block_table[b, :npg].astype(np.int64)).to(bt.q.device)
+    krec = bt.cache.records(0)[pages].cpu().numpy()            # [npg][n_kv][2560]
+    vrec = bt.cache.records(1)[pages].cpu().numpy()            # [npg][n_kv][2176]
+    W = bt.cache.window_tokens
+    rows = np.arange(nq, T) % W
+    kwin = bt.cache.k_window[b].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)[:, rows]
+    vwin = bt.cache.v_window[b].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)[:, rows]
+    res = []
+    for h in range(w.num_kv_heads):
+        def unpack(rec):
+            packed = rec[:, h, :ps * d // 2].reshape(npg * ps, d // 2)
+            codes = np.empty((npg * ps, d), dtype=np.uint8)
+            codes[:, 0::2] = packed & 0x0F
+            codes[:, 1::2] = packed >> 4
+            return codes
+        off = ps * d // 2
+        k_s = krec[:, h, off:off + 2 * d].copy().view(np.uint16)
+        k_z = krec[:, h, off + 2 * d:off + 4 * d].copy().view(np.uint16)
+        v_s = vrec[:, h, off:off + 2 * ps].copy().view(np.uint16).reshape(-1)
+        v_z = vrec[:, h, off + 2 * ps:off + 4 * ps].copy().view(np.uint16).reshape(-1)
+        res.append(dict(nq=nq, k_codes=unpack(krec), k_s=k_s, k_z=k_z, v_codes=unpack(vrec), v_s=v_s, v_z=v_z,
+                        k_res=kwin[h], v_res=vwin[h]))
+    return res
+
+
+def run_decode_kivi(bt: BuiltKivi, partition_pages: int = 0, softmax_scale=None):
+    B, Hq = bt.q.shape[0], bt.q.shape[1]
+    scale = 1.0 / math.sqrt(bt.w.head_dim) if softmax_scale is None else softmax_scale
+    ws = torch.empty(kvq.decode_workspace_bytes(bt.cache, B, Hq, bt.max_ctx, partition_pages),
+                     dtype=torch.uint8, device=bt.q.device)
+    out = torch.full((B, Hq, bt.w.head_dim), float("nan"), dtype=torch.float32, device=bt.q.device)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=bt.q.device)
+    kvq.decode_attention(bt.cache, bt.q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws, out, lse,
+                         partition_pages)
+    torch.cuda.synchronize()
+    return out, lse

@@ -55,10 +55,19 @@ def test_record_bytes(L):
 
 def _desc(**kw):
     d = dict(dtype=1, scale_mode=2, num_pages=4, page_size=16, num_kv_heads=2, head_dim=128,
-             k_pages=0x2000, v_pages=0x3000, static_scales=None)
+             k_pages=0x2000, v_pages=0x3000, static_scales=None, k_window=None, v_window=None,
+             max_seqs=0, window_tokens=0, residual=0)
     d.update(kw)
     return kvq.CacheDesc(d["dtype"], d["scale_mode"], d["num_pages"], d["page_size"], d["num_kv_heads"],
-                         d["head_dim"], d["k_pages"], d["v_pages"], d["static_scales"], None, None, 0, 0, 0, 0)
+                         d["head_dim"], d["k_pages"], d["v_pages"], d["static_scales"], d["k_window"],
+                         d["v_window"], d["max_seqs"], d["window_tokens"], d["residual"], 0)
+
+
+def _kivi_desc(**kw):
+    d = dict(dtype=3, page_size=32, k_window=0x4000, v_window=0x5000, max_seqs=4, window_tokens=160,
+             residual=128)
+    d.update(kw)
+    return _desc(**d)
 
 
 def _append(L, desc, n=4, k=FAKE, v=FAKE, slots=FAKE):
@@ -104,6 +113,37 @@ def test_decode_validation(L):
         assert _decode(L, _desc(head_dim=96), fn) == UNSUPPORTED
     assert L.kvq_decode_reduce(ctypes.byref(d), 2, 8, 64, 0, FAKE, 0, FAKE, None, None) == WORKSPACE
     assert L.kvq_decode_reduce(ctypes.byref(d), 2, 7, 64, 0, FAKE, 1 << 30, FAKE, None, None) == INVALID
+
+
+def _kivi_append(L, desc, num_seqs=2, max_new=8, maxp=4, k=FAKE, offs=FAKE, lens=FAKE, bt=FAKE):
+    return L.kvq_kivi_append(None if desc is None else ctypes.byref(desc), k, FAKE, offs, lens, bt, maxp,
+                             num_seqs, max_new, None)
+
+
+def test_kivi_validation(L):
+    d = _kivi_desc()
+    assert _kivi_append(L, None) == INVALID
+    assert _kivi_append(L, _desc()) == UNSUPPORTED                        # FP8 cache: use kvq_append
+    assert _kivi_append(L, _desc(num_pages=0)) == INVALID
+    assert _kivi_append(L, _kivi_desc(page_size=16)) == UNSUPPORTED       # group = page = 32 tokens
+    assert _kivi_append(L, _kivi_desc(scale_mode=0)) == UNSUPPORTED
+    assert _kivi_append(L, _kivi_desc(k_window=None)) == INVALID
+    assert _kivi_append(L, _kivi_desc(window_tokens=159)) == INVALID      # ring must hold residual + 32
+    assert _kivi_append(L, _kivi_desc(residual=-1)) == INVALID
+    assert _kivi_append(L, d, num_seqs=5) == INVALID                      # beyond the window slots
+    assert _kivi_append(L, d, num_seqs=-1) == INVALID
+    assert _kivi_append(L, d, max_new=-1) == INVALID
+    assert _kivi_append(L, d, k=None) == INVALID
+    assert _kivi_append(L, d, offs=None) == INVALID
+    assert _kivi_append(L, d, maxp=0) == INVALID
+    assert _kivi_append(L, d, num_seqs=0) == OK
+    assert _kivi_append(L, d, max_new=0) == OK
+    # decode on a KIVI cache: same checks as FP8 / INT8 plus the window slots
+    assert _decode(L, d, num_seqs=5, hq=16, maxp=4, max_ctx=128) == INVALID
+    assert _decode(L, d, hq=16, maxp=1, max_ctx=64) == INVALID            # 2 pages of 32 needed
+    assert _decode(L, _kivi_desc(v_window=None), hq=16, maxp=4, max_ctx=128) == INVALID
+    assert _decode(L, d, num_seqs=0, hq=16, maxp=4, max_ctx=128) == OK
+    assert _decode(L, d, hq=16, maxp=4, max_ctx=128, ws_bytes=0) == WORKSPACE
 
 
 def test_workspace_bytes(L):

@@ -1,0 +1,146 @@
+"""GPU parity of the KIVI-style INT4 path (kvq_kivi_append + kvq_decode_attention
+on a KVQ_INT4_KIVI cache) against the CPU oracle.
+
+Quantized bytes (4-bit codes, per-channel K and per-token V BF16 scales and
+zero-points) and the fp16 window rows must match bit for bit; attention must
+satisfy |gpu - oracle| <= 2e-3 + 1e-2 |oracle| elementwise against fp64
+attention over the oracle's own dequantized INT4 tokens plus fp16 window.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from tests.conftest import gpu_available
+
+pytestmark = pytest.mark.gpu
+
+if not gpu_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import synthetic  # noqa: E402
+from tests import kvq_harness as H  # noqa: E402
+
+ATOL, RTOL = 2e-3, 1e-2
+LSE_ATOL = 1e-3
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def small(**kw) -> synthetic.Workload:
+    w = synthetic.WORKLOADS["kivi"]
+    d = dict(w.__dict__)
+    d.update(dict(batch=3, num_q_heads=8, num_kv_heads=2, context=1024))
+    d.update(kw)
+    return synthetic.Workload(**d)
+
+
+def check_state(bt, b, ref):
+    got = H.kivi_read_seq(bt, b)
+    for h, (g, r) in enumerate(zip(got, ref["heads"])):
+        assert g["nq"] == r["nq"]
+        for key in ("k_codes", "k_s", "k_z", "v_codes", "v_s", "v_z", "k_res", "v_res"):
+            a, e = np.asarray(g[key]), np.asarray(r[key])
+            assert a.shape == e.shape, (key, a.shape, e.shape)
+            if not np.array_equal(a, e):
+                idx = np.argwhere(a != e)[0]
+                raise AssertionError(f"seq {b} head {h} {key} differs at {tuple(idx)}: {a[tuple(idx)]} vs {e[tuple(idx)]}")
+
+
+def check_out(bt, out, lse, b, ref):
+    ok, mabs, mrel = H.allclose_report(out[b].cpu().numpy(), ref["out"], ATOL, RTOL)
+    assert ok, f"seq {b}: max abs {mabs:.3e} max rel {mrel:.3e}"
+    dl = np.abs(lse[b].cpu().numpy().astype(np.float64) - ref["lse"])
+    assert dl.max() <= LSE_ATOL, f"seq {b}: lse diff {dl.max():.3e}"
+    return mabs
+
+
+def test_kivi_append_and_decode_small():
+    """Window-only, one group, several groups; groups flushed from the window,
+    from new rows and from both (bulk call, one-token steps, remainder)."""
+    w = small()
+    lens = np.array([100, 200, 333])
+    say("kivi small build")
+    bt = H.build_kivi(w, lens)
+    out, lse = H.run_decode_kivi(bt)
+    for b in range(len(lens)):
+        say("kivi small check seq", b)
+        ref = H.kivi_oracle_seq(bt, b)
+        check_state(bt, b, ref)
+        check_out(bt, out, lse, b, ref)
+
+
+def test_kivi_group_boundaries_one_token_at_a_time():
+    """Appending one token per call across the 160/192-token boundaries flushes a
+    group from the window exactly when the window would exceed 128 + 31 tokens."""
+    w = small(batch=2)
+    lens = np.array([161, 197])
+    plan = [np.array([120, 120])] + [np.array([1 if 120 + i < n else 0 for n in lens]) for i in range(80)]
+    say("kivi one-token build")
+    bt = H.build_kivi(w, lens, plan=plan)
+    out, lse = H.run_decode_kivi(bt)
+    for b in range(2):
+        ref = H.kivi_oracle_seq(bt, b)
+        check_state(bt, b, ref)
+        check_out(bt, out, lse, b, ref)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_kivi_gqa_group_sizes(G):
+    w = small(batch=2, num_q_heads=2 * G, num_kv_heads=2)
+    lens = np.array([290, 77])
+    say("kivi gqa", G)
+    bt = H.build_kivi(w, lens)
+    out, lse = H.run_decode_kivi(bt)
+    for b in range(2):
+        check_out(bt, out, lse, b, H.kivi_oracle_seq(bt, b))
+
+
+def test_kivi_partition_sweep_and_shuffled_pages():
+    w = small(batch=4, num_q_heads=16, num_kv_heads=2)
+    lens = np.array([1000, 1, 450, 161])
+    say("kivi partitions build")
+    bt = H.build_kivi(w, lens, shuffle=True)
+    refs = [H.kivi_oracle_seq(bt, b) for b in range(len(lens))]
+    outs = []
+    for part in (0, 1, 2, 3, 7, 64):
+        say("kivi partitions decode", part)
+        out, lse = H.run_decode_kivi(bt, part)
+        for b in range(len(lens)):
+            check_out(bt, out, lse, b, refs[b])
+        outs.append(out.cpu())
+    # V codes enter the MFMA as 128 + n and the offset is removed at the end, so
+    # fp32 rounding of the accumulator is amplified by about (128 + 7.5) / 7.5;
+    # different partitionings round differently by up to ~1e-4 (the oracle bar
+    # above is 2e-3 + 1e-2 |ref|)
+    for o in outs[1:]:
+        assert torch.allclose(o, outs[0], atol=5e-4, rtol=1e-4)
+
+
+def test_kivi_context_length_one_is_exact():
+    """One token, still in the fp16 window: the output is its fp16 value row exactly."""
+    w = small(batch=2)
+    bt = H.build_kivi(w, np.array([1, 1]))
+    out, lse = H.run_decode_kivi(bt)
+    for b in range(2):
+        ref = H.kivi_oracle_seq(bt, b)
+        vrow = np.repeat(ref["v_hat"][0], w.group_size, axis=0)
+        assert np.array_equal(out[b].cpu().numpy().astype(np.float64), vrow)
+
+
+def test_kivi_full_size():
+    """B 4, 64 q / 8 KV heads, context 131072 (130944 INT4 tokens + 128 fp16)."""
+    w = synthetic.WORKLOADS["kivi"]
+    say("kivi full build")
+    bt = H.build_kivi(w, plan=[synthetic.seq_lens(w) - 5, np.ones(w.batch, dtype=np.int64) * 5])
+    say("kivi full decode")
+    out, lse = H.run_decode_kivi(bt)
+    for b in (0, 3):
+        say("kivi full check seq", b)
+        ref = H.kivi_oracle_seq(bt, b)
+        check_state(bt, b, ref)
+        check_out(bt, out, lse, b, ref)
