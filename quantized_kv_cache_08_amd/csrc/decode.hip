@@ -408,14 +408,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const int hq = (int)(idx - (long long)b * p.n_q);
     const int h = hq / p.group;
     const long long chunk = p.ws_header[0];
-    const int pb = p.ws_pfx[b + 1] - p.ws_pfx[b];
+    const int cb = p.ws_pfx[b + 1] - p.ws_pfx[b];      // item weight: pages + start-up weight
     float* out = p.out + idx * kHeadDim + 2 * lane;
-    if (pb == 0) {
+    if (cb == 0) {
         *(float2*)out = make_float2(0.0f, 0.0f);
         if (p.lse && lane == 0) p.lse[idx] = -INFINITY;
         return;
     }
-    const long long item_start = (long long)p.ws_pfx[b] * p.n_kv + (long long)h * pb;
+    const int pb = cb - p.ws_header[1];
+    const long long item_start = (long long)p.ws_pfx[b] * p.n_kv + (long long)h * cb;
     const int n_seg = (int)((item_start + pb - 1) / chunk - item_start / chunk + 1);
     if (n_seg == 1) return;   // written by the split kernel
     const float* pl = p.part_lse + idx * p.max_parts;

@@ -11,6 +11,7 @@ namespace kvq {
 constexpr int kHeadDim = 128;
 constexpr int kMaxParts = 32;      // partial results kept per (sequence, query head)
 constexpr int kMinChunkPages = 4;  // smallest automatic work range per wave
+constexpr int kSegmentCost = 8;    // start-up of a segment, in pages, for ragged batches (measured best on the mixed workload)
 constexpr int kSplitThreads = 256; // 4 waves per workgroup
 constexpr int kKiviGroup = 32;     // INT4 path: tokens per K group = page size
 
@@ -37,7 +38,7 @@ struct SplitParams {
     float* lse;                    // fp32 [B][Hq] or null
     float* part_o;                 // fp32 [B][Hq][max_parts][128]
     float* part_lse;               // fp32 [B][Hq][max_parts] (log2 domain)
-    int32_t* ws_header;            // [0] = chunk pages
+    int32_t* ws_header;            // [0] = range length, [1] = per-item start-up weight
     int32_t* ws_pfx;               // [B + 1] exclusive prefix of pages per sequence
     long long rec_k, rec_v;
     int num_seqs, n_q, n_kv, group, num_pages;

@@ -25,21 +25,60 @@ __device__ __forceinline__ int pages_of(int len, int max_ctx, int ps) {
 // segment of this wave's ranges.  Must be called by every thread of a
 // workgroup of kSplitThreads threads (it synchronises once); the dynamic LDS
 // holds num_seqs + 1 ints.
+//
+// Balancing.  A segment costs its pages plus a fixed start-up (loading q,
+// filling the load pipeline, writing its result), which is worth about
+// kSegmentCost pages.  In a batch of unequal lengths each item is therefore
+// weighted as pages + kSegmentCost and the weight space, not the page space,
+// is cut into equal ranges, so that a wave whose range holds many short items
+// gets fewer pages.  The trailing kSegmentCost units of an item hold no pages
+// (a range that covers only those is skipped); 8 pages measured best on a
+// lognormal-length batch.  When every sequence has the
+// same length the weight is 0 and ranges stay aligned with items.  Layout of
+// the shared header: [0] = range length (weight units), [1] = the weight.
 template <int PS, typename Seg>
 __device__ __forceinline__ void for_each_segment(const SplitParams& p, Seg&& seg) {
     extern __shared__ int s_pfx[];   // [num_seqs + 1]
     __shared__ int s_wsum[kSplitThreads / 64];
+    __shared__ int s_wmin[kSplitThreads / 64], s_wmax[kSplitThreads / 64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int B = p.num_seqs;
 
-    // pages per sequence and their exclusive prefix sum (every workgroup)
+    // pages per sequence, their extremes (is the batch uniform?)
     const int per = (B + kSplitThreads - 1) / kSplitThreads;
     const int beg = min(tid * per, B);
     const int end = min(beg + per, B);
+    int pmin = 0x7FFFFFFF, pmax = 0;
+    for (int i = beg; i < end; ++i) {
+        const int pg = pages_of(p.context_lens[i], p.max_ctx, PS);
+        pmin = min(pmin, pg);
+        pmax = max(pmax, pg);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        pmin = min(pmin, __shfl_xor(pmin, o));
+        pmax = max(pmax, __shfl_xor(pmax, o));
+    }
+    if (lane == 0) {
+        s_wmin[wid] = pmin;
+        s_wmax[wid] = pmax;
+    }
+    __syncthreads();
+    for (int w = 0; w < kSplitThreads / 64; ++w) {
+        pmin = min(pmin, s_wmin[w]);
+        pmax = max(pmax, s_wmax[w]);
+    }
+    const int K = (pmin == pmax) ? 0 : kSegmentCost;
+    auto weight = [&](int i) {
+        const int pg = pages_of(p.context_lens[i], p.max_ctx, PS);
+        return pg > 0 ? pg + K : 0;
+    };
+
+    // exclusive prefix sum of the per-sequence item weights
     int local = 0;
-    for (int i = beg; i < end; ++i) local += pages_of(p.context_lens[i], p.max_ctx, PS);
+    for (int i = beg; i < end; ++i) local += weight(i);
     int incl = local;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -52,7 +91,7 @@ __device__ __forceinline__ void for_each_segment(const SplitParams& p, Seg&& seg
     for (int w = 0; w < wid; ++w) run += s_wsum[w];
     for (int i = beg; i < end; ++i) {
         s_pfx[i] = run;
-        run += pages_of(p.context_lens[i], p.max_ctx, PS);
+        run += weight(i);
     }
     if (tid == 0) {
         int tot = 0;
@@ -70,7 +109,10 @@ __device__ __forceinline__ void for_each_segment(const SplitParams& p, Seg&& seg
         if (chunk < p.min_chunk) chunk = p.min_chunk;
     }
     if (blockIdx.x == 0) {
-        if (tid == 0) p.ws_header[0] = (int)chunk;
+        if (tid == 0) {
+            p.ws_header[0] = (int)chunk;
+            p.ws_header[1] = K;
+        }
         for (int i = tid; i <= B; i += kSplitThreads) p.ws_pfx[i] = s_pfx[i];
     }
 
@@ -86,19 +128,25 @@ __device__ __forceinline__ void for_each_segment(const SplitParams& p, Seg&& seg
                 else hi = mid - 1;
             }
             const int b = uniform(lo);
-            const int pb = uniform(s_pfx[b + 1] - s_pfx[b]);
+            const int cb = uniform(s_pfx[b + 1] - s_pfx[b]);   // item weight (> 0 here)
+            const int pb = cb - K;                              // item pages
             const long long start_b = (long long)s_pfx[b] * p.n_kv;
-            const int h = uniform((int)((x - start_b) / pb));
-            const long long item_start = start_b + (long long)h * pb;
-            const long long item_end = item_start + pb;
-            const long long seg_end = min(xend, item_end);
-            const int page0 = uniform((int)(x - item_start));
-            const int page1 = uniform((int)(seg_end - item_start));
-            const long long first_seg = item_start / chunk;
-            const int n_seg = uniform((int)((item_end - 1) / chunk - first_seg + 1));
-            const int segi = uniform((int)(x / chunk - first_seg));
-            seg(b, h, page0, page1, segi, n_seg, lane);
-            x = seg_end;
+            const int h = uniform((int)((x - start_b) / cb));
+            const long long item_start = start_b + (long long)h * cb;
+            const long long item_pend = item_start + pb;        // end of the page part
+            const long long item_end = item_start + cb;
+            if (x < item_pend) {
+                const long long seg_end = min(xend, item_pend);
+                const int page0 = uniform((int)(x - item_start));
+                const int page1 = uniform((int)(seg_end - item_start));
+                const long long first_seg = item_start / chunk;
+                const int n_seg = uniform((int)((item_pend - 1) / chunk - first_seg + 1));
+                const int segi = uniform((int)(x / chunk - first_seg));
+                seg(b, h, page0, page1, segi, n_seg, lane);
+                x = (seg_end < item_pend) ? seg_end : min(xend, item_end);
+            } else {
+                x = min(xend, item_end);
+            }
         }
     }
 }
