@@ -191,14 +191,22 @@ hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream) {
 }
 
 // ============================================================== decode
+// Per-page loads into registers: the 4-bit codes, and the page's scales and
+// zero-points as three words per lane (the whole 640-byte metadata block of
+// the K and V records), which the wave spreads through its LDS slot when it
+// computes the page.  A pipeline stage is 19 VGPRs.
 struct KiviBuf {
     u32x4_t kc[2];     // [half]: K codes of token 16 hp + j, channels [32g, 32g+32)
-    u32x4_t ks[4];     // bf16 K scales of channels 32g + 8kb + [0, 8)
-    u32x4_t kz[4];     // bias operand: lane j = 0 zero-points, j = 1 scales, else 0
     uint32_t vc[2][4]; // [half][r]: V codes of token 16 hp + 4g + r, channels [8j, 8j+8)
-    u32x2_t vs[2];     // bf16 V scales of tokens 16 hp + 4g + [0, 4)
-    u32x2_t vz[2];
+    uint32_t km[2];    // K record bytes 2048 + 4 lane and 2304 + 4 lane (scales, zero-points)
+    uint32_t vm;       // V record bytes 2048 + 4 lane (scales, zero-points; 0 past the record)
 };
+
+// LDS slot of one wave: [0, 256) K scales (128 bf16), [256, 512) K
+// zero-points, [512, 576) V scales (32 bf16), [576, 640) V zero-points,
+// [640, 768) zeros.
+constexpr int kKiviMetaBytes = 768;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 struct KiviState {
     f32x4_t acc[8];
@@ -243,7 +251,8 @@ __device__ __forceinline__ void kivi_softmax(KiviState& st, float (&sc)[2][4], f
 
 __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const int b, const int h,
                                              const int page0, const int page1, const int seg,
-                                             const int n_seg, const int lane) {
+                                             const int n_seg, const int lane, lds_u8* smeta,
+                                             const lds_u8* szero) {
     const SplitParams& p = kp.s;
     const int j = lane & 15;
     const int g = lane >> 4;
@@ -264,6 +273,16 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         for (int kb = 0; kb < 4; ++kb) qb[kb] = u32x4_t{0u, 0u, 0u, 0u};
     }
 
+    // q pairs with one half cleared: dot2(qlo, s) = q_even s_even, dot2(qhi, s) = q_odd s_odd
+    u32x4_t qlo[4], qhi[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qlo[kb][i] = qb[kb][i] & 0x0000FFFFu;
+            qhi[kb][i] = qb[kb][i] & 0xFFFF0000u;
+        }
+
     KiviState st;
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -272,16 +291,17 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     st.pz = 0.0f;
     st.pcorr = 0.0f;
 
-    const int* bt = p.block_table + (size_t)b * p.max_pages_per_seq;
+    // read-only block table through the constant address space: page-id loads
+    // are scalar and never wait for the K/V vector loads in flight
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(p.block_table) + (size_t)b * p.max_pages_per_seq;
     const int qend = min(page1, pq);            // quantized pages of this segment: [page0, qend)
     const int n_q = qend - page0;
     const uint32_t kC = 0x43434343u;           // bf16 high byte of 128 + n
 
     const int off_kc = j * (kHeadDim / 2) + 16 * g;
-    const int off_ks = kKiviGroup * kHeadDim / 2 + 64 * g;
-    const int off_kz = (j == 0) ? off_ks + 2 * kHeadDim : (j == 1 ? off_ks : (int)p.rec_k);
     const int off_vc = 4 * g * (kHeadDim / 2) + 4 * j;
-    const int off_vs = kKiviGroup * kHeadDim / 2 + 8 * g;
+    constexpr int kMetaOff = kKiviGroup * kHeadDim / 2;          // metadata after the codes
 
     auto load = [&](KiviBuf& cb, const int c) {
         const bool live = c < n_q;
@@ -298,45 +318,64 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         for (int hp = 0; hp < 2; ++hp)
             cb.kc[hp] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_kc + hp * 16 * (kHeadDim / 2), 0, 0);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            cb.ks[kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_ks + 16 * kb, 0, 0);
-            cb.kz[kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_kz + 16 * kb, 0, 0);
-        }
-#pragma unroll
-        for (int hp = 0; hp < 2; ++hp) {
+        for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 cb.vc[hp][r] = __builtin_amdgcn_raw_buffer_load_b32(
                     rv, off_vc + (16 * hp + r) * (kHeadDim / 2), 0, 0);
-            cb.vs[hp] = __builtin_amdgcn_raw_buffer_load_b64(rv, off_vs + 32 * hp, 0, 0);
-            cb.vz[hp] = __builtin_amdgcn_raw_buffer_load_b64(rv, off_vs + 2 * kKiviGroup + 32 * hp, 0, 0);
-        }
+        cb.km[0] = __builtin_amdgcn_raw_buffer_load_b32(rk, kMetaOff + 4 * lane, 0, 0);
+        cb.km[1] = __builtin_amdgcn_raw_buffer_load_b32(rk, kMetaOff + 256 + 4 * lane, 0, 0);
+        cb.vm = __builtin_amdgcn_raw_buffer_load_b32(rv, kMetaOff + 4 * lane, 0, 0);
     };
 
     auto compute_quant = [&](KiviBuf& cb) {
+        // spread the page's metadata through the wave's LDS slot (the wave's LDS
+        // operations execute in order: the reads below see these writes, and the
+        // previous page's reads were issued before them)
+        *(__attribute__((address_space(3))) uint32_t*)(smeta + 4 * lane) = cb.km[0];
+        *(__attribute__((address_space(3))) uint32_t*)(smeta + 256 + 4 * lane) = cb.km[1];
+        *(__attribute__((address_space(3))) uint32_t*)(smeta + 512 + 4 * lane) = cb.vm;
+        const lds_u8* m = smeta;
+        u32x4_t ks[4], kz[4];
+        const lds_u8* zsrc = (j == 0) ? m + 256 + 64 * g : (j == 1 ? m + 64 * g : szero);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            ks[kb] = *(const __attribute__((address_space(3))) u32x4_t*)(m + 64 * g + 16 * kb);
+            kz[kb] = *(const __attribute__((address_space(3))) u32x4_t*)(zsrc + 16 * kb);
+        }
+        u32x2_t vs[2], vz[2];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+            vs[hp] = *(const __attribute__((address_space(3))) u32x2_t*)(m + 512 + 32 * hp + 8 * g);
+            vz[hp] = *(const __attribute__((address_space(3))) u32x2_t*)(m + 576 + 32 * hp + 8 * g);
+        }
+
         // bias = sum_c q_c z_c - 128 sum_c q_c s_c for head j (rows 0, 1 of an MFMA)
         f32x4_t d2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) d2 = mfma_16x16x32_bf16(cb.kz[kb], qb[kb], d2);
+        for (int kb = 0; kb < 4; ++kb) d2 = mfma_16x16x32_bf16(kz[kb], qb[kb], d2);
         const float bias = __shfl(d2[0] - 128.0f * d2[1], j);
 
-        // q' = q s (exact as bf16 hi + lo), slots ordered like the code bytes
+        // q' = q s, at most 16 significant bits: its truncation to bf16 and the
+        // remainder are both exact bf16 values; slots ordered like the code bytes
         u32x4_t bh[4], bl[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             float qs[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                qs[2 * i] = bf16lo(qb[kb][i]) * bf16lo(cb.ks[kb][i]);
-                qs[2 * i + 1] = bf16hi(qb[kb][i]) * bf16hi(cb.ks[kb][i]);
+                qs[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qlo[kb][i]), as_bf16x2(ks[kb][i]),
+                                                            0.0f, false);
+                qs[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qhi[kb][i]), as_bf16x2(ks[kb][i]),
+                                                                0.0f, false);
             }
             const int ord[8] = {0, 2, 1, 3, 4, 6, 5, 7};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float a0 = qs[ord[2 * e]], a1 = qs[ord[2 * e + 1]];
-                const uint32_t hw = pack_bf16_rne(a0, a1);
-                bh[kb][e] = hw;
-                bl[kb][e] = pack_bf16_rne(a0 - bf16lo(hw), a1 - bf16hi(hw));
+                const uint32_t u0 = f32_to_bits(a0), u1 = f32_to_bits(a1);
+                bh[kb][e] = perm(u1, u0, 0x07060302u);
+                bl[kb][e] = pack_bf16_rne(a0 - bits_to_f32(u0 & 0xFFFF0000u), a1 - bits_to_f32(u1 & 0xFFFF0000u));
             }
         }
 
@@ -367,8 +406,8 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         for (int hp = 0; hp < 2; ++hp) {
 #pragma unroll
             for (int rp = 0; rp < 2; ++rp) {
-                const uint32_t sw = cb.vs[hp][rp];
-                const uint32_t zw = cb.vz[hp][rp];
+                const uint32_t sw = vs[hp][rp];
+                const uint32_t zw = vz[hp][rp];
                 const float p0 = pp[hp][2 * rp], p1 = pp[hp][2 * rp + 1];
                 const float a0 = p0 * bf16lo(sw), a1 = p1 * bf16hi(sw);
                 st.pz += p0 * bf16lo(zw) + p1 * bf16hi(zw);
@@ -407,15 +446,20 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         }
     };
 
-    // ---- quantized pages, loads of the next page in flight during compute
+    // ---- quantized pages: the loads of the next page are in flight while a
+    // page is computed.  The scheduling barriers keep those loads issued
+    // before the compute, whose first step (the LDS writes) would otherwise be
+    // hoisted above them and wait with nothing in flight.
     if (n_q > 0) {
         KiviBuf b0, b1;
         load(b0, 0);
         for (int c = 0;;) {
             load(b1, c + 1);
+            __builtin_amdgcn_sched_barrier(0);
             compute_quant(b0);
             if (++c >= n_q) break;
             load(b0, c + 1);
+            __builtin_amdgcn_sched_barrier(0);
             compute_quant(b1);
             if (++c >= n_q) break;
         }
@@ -530,8 +574,14 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
 }
 
 __global__ __launch_bounds__(256) void kivi_split_kernel(KiviSplitParams kp) {
+    __shared__ __attribute__((aligned(16))) uint8_t s_meta[kSplitThreads / 64][kKiviMetaBytes];
+    __shared__ __attribute__((aligned(16))) uint32_t s_zero[64];
+    if (threadIdx.x < 64) s_zero[threadIdx.x] = 0u;   // visible after the first barrier below
+    const int wid = threadIdx.x >> 6;
+    lds_u8* smeta = (lds_u8*)&s_meta[wid][0];
+    const lds_u8* szero = (const lds_u8*)&s_zero[0];
     for_each_segment<kKiviGroup>(kp.s, [&](int b, int h, int page0, int page1, int seg, int n_seg, int lane) {
-        kivi_segment(kp, b, h, page0, page1, seg, n_seg, lane);
+        kivi_segment(kp, b, h, page0, page1, seg, n_seg, lane, smeta, szero);
     });
 }
 

@@ -20,6 +20,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float bits_to_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+// Pair of bf16 from its 32 bits.  Takes the word by value: this compiler's
+// __builtin_bit_cast of a vector-element lvalue (v[i]) reads element 0 for
+// every i, so element accesses are always passed through a function argument.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
 __device__ __forceinline__ uint32_t f32_to_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
 // bf16 bits (low 16 of u) -> fp32, exact.
