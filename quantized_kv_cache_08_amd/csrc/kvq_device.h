@@ -100,6 +100,24 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32_bf16(u32x4_t a, u32x4_t b, f32x
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+
+__device__ __forceinline__ float f16_value(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
+    f16x2_t v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
 template <typename T>
 __device__ __forceinline__ T uniform(T v) {
     return (T)__builtin_amdgcn_readfirstlane((int)v);
