@@ -43,8 +43,11 @@
  * Page records.  A pool holds num_pages x num_kv_heads records; record
  * (page p, head h) starts at byte (p * num_kv_heads + h) * kvq_record_bytes().
  * A record stores, in order:
- *   page_size rows of head_dim code bytes (token-major; INT4: head_dim/2 bytes
- *   per row, low nibble = even channel), then
+ *   page_size rows of head_dim code bytes (token-major; INT4 K: head_dim/2
+ *   bytes per row, low nibble = even channel; INT4 V: the rows of tokens 2m and
+ *   2m + 1 interleaved in 16-bit units, i.e. 32-bit word q of pair row m holds
+ *   channels 4q..4q+3 of token 2m in bits 0-15 and of token 2m + 1 in bits
+ *   16-31, channel 4q + i in bits 4i..4i+3 of each half), then
  *   per-(token,head) modes: page_size bf16 scales, then (INT8) page_size bf16
  *   zero-points;  KIVI K: head_dim bf16 scales then head_dim bf16 zero-points
  *   (one per channel for the page's 32-token group);  KIVI V: page_size bf16

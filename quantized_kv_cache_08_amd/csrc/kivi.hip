@@ -17,17 +17,22 @@
 //   x^ = code * s + z, every "/" one IEEE float32 division.  The inputs are
 //   the fp16 values (bf16 input rounded to nearest-even fp16).
 //
+// V records store each token pair's code rows interleaved in 16-bit units:
+// word q of pair row m holds channels 4q..4q+3 of token 2m (bits 0-15) and of
+// token 2m + 1 (bits 16-31), channel 4q + i in bits 4i..4i+3 of each half.
+//
 // Decode of one 32-token page, per wave (lane l: j = l % 16, g = l / 16):
 //   score_t = sum_c q_c (n_tc s_c + z_c) = sum_c n_tc (q_c s_c) + sum_c q_c z_c.
 //   q'_c = q_c s_c is the product of two bf16 values, at most 16 significant
 //   bits, so it splits exactly into bf16 hi + lo; codes enter the MFMA as the
 //   bf16 value 128 + n (one byte permute per pair), and the offset
-//   128 sum_c q'_c is removed, together with the zero-point term, through the
-//   accumulator's initial value: bias = sum_c q_c z_c - 128 sum_c q_c s_c,
-//   computed by one more small MFMA (rows z and s against q).
-//   PV: O += P'.(128 + n_v) with P' = p * s_t split into bf16 hi + lo; the
-//   offset 128 sum_t P'_t and the zero-point term sum_t p_t z_t are removed
-//   at the end.  fp16 window chunks use fp16 MFMAs on the exact fp16 values.
+//   128 sum_c q'_c is removed, together with the zero-point term, by
+//   bias = sum_c q_c z_c - 128 sum_c q_c s_c from one more small MFMA (rows z
+//   and s against q), added where the scores are scaled.
+//   PV: O += P'.(128 + n_v) (128 + 8 n_v on odd channels) with P' = p * s_t
+//   split into bf16 hi + lo; the offset 128 sum_t P'_t (summed by MFMAs over
+//   the same P') and the zero-point term sum_t p_t z_t are removed at the end.
+//   fp16 window chunks use fp16 MFMAs on the exact fp16 values.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "splitk.h"
@@ -128,7 +133,8 @@ __global__ __launch_bounds__(128) void kivi_flush_kernel(KiviAppendParams p) {
             const float sf = bf16lo(sb);
             const uint32_t c0 = kivi_code(x0, zf, sf);
             const uint32_t c1 = kivi_code(x1, zf, sf);
-            vrec[t * (kHeadDim / 2) + l] = (uint8_t)(c0 | (c1 << 4));
+            // token pairs interleaved in 16-bit units: pair t / 2, channel quad l / 2
+            vrec[(t >> 1) * kHeadDim + 4 * (l >> 1) + 2 * (t & 1) + (l & 1)] = (uint8_t)(c0 | (c1 << 4));
             if (l == 0) {
                 *(uint16_t*)(vrec + kKiviGroup * kHeadDim / 2 + 2 * t) = (uint16_t)sb;
                 *(uint16_t*)(vrec + kKiviGroup * kHeadDim / 2 + 2 * kKiviGroup + 2 * t) = (uint16_t)zb;
@@ -180,20 +186,26 @@ hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream) {
 // computes the page.  A pipeline stage is 19 VGPRs.
 struct KiviBuf {
     u32x4_t kc[2];     // [half]: K codes of token 16 hp + j, channels [32g, 32g+32)
-    uint32_t vc[2][4]; // [half][r]: V codes of token 16 hp + 4g + r, channels [8j, 8j+8)
+    u32x2_t vc[2][2];  // [half][rp]: V token pair 8 hp + 2g + rp, channels [8j, 8j+8)
     uint32_t km[2];    // K record bytes 2048 + 4 lane and 2304 + 4 lane (scales, zero-points)
     uint32_t vm;       // V record bytes 2048 + 4 lane (scales, zero-points; 0 past the record)
 };
 
 // LDS slot of one wave: [0, 256) K scales (128 bf16), [256, 512) K
-// zero-points, [512, 576) V scales (32 bf16), [576, 640) V zero-points,
-// [640, 768) zeros.
-constexpr int kKiviMetaBytes = 768;
+// zero-points (bf16), [512, 1024) K scales as fp32, [1024, 1152) V scales as
+// fp32 (32 tokens), [1152, 1280) V zero-points as fp32, [1280, 1536) unused
+// (written with the zeros that lanes 32-63 load past the V record).
+constexpr int kKiviMetaBytes = 1536;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4;
 
 struct KiviState {
-    f32x4_t acc[8];
-    float m_used, lsum, pz, pcorr;
+    f32x4_t acc[8];    // O rows (heads 4g + r) x channel 8j + t; odd t carry codes x 8
+    f32x4_t pc;        // sum of the P' values the PV products consumed, rows 4g + r
+    float m_used, lsum, pz;
 };
 
 // Online-softmax update with the scores of one 32-token chunk (exp2 domain);
@@ -205,19 +217,18 @@ __device__ __forceinline__ void kivi_softmax(KiviState& st, float (&sc)[2][4], f
     for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[hp][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_over_groups(mx);
     if (__builtin_expect(__any(mx > st.m_used + kKiviHeadroom), 0)) {
         __asm__ volatile("");   // keep the rare rescale a branch, not straight-line code
         const float m_new = fmaxf(st.m_used, mx);
         const float alpha = __builtin_amdgcn_exp2f(st.m_used - m_new);
         st.lsum *= alpha;
         st.pz *= alpha;
-        st.pcorr *= alpha;
         st.m_used = m_new;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float ar = __shfl(alpha, 4 * g + r);
+            st.pc[r] *= ar;
 #pragma unroll
             for (int t = 0; t < 8; ++t) st.acc[t][r] *= ar;
         }
@@ -232,6 +243,37 @@ __device__ __forceinline__ void kivi_softmax(KiviState& st, float (&sc)[2][4], f
         }
 }
 
+// Lane j of each row of 16 takes the word of lane (j + 8) mod 16.
+__device__ __forceinline__ uint32_t row_swap8(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);   // row_ror:8
+}
+
+// (w & mask) | c in one instruction: the masks stay in VGPRs so that the
+// constant c can come from an SGPR (a VOP3 instruction takes no literal here).
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t vmask, uint32_t c) {
+    uint32_t o;
+    __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(o) : "v"(w), "v"(vmask), "s"(c));
+    return o;
+}
+
+// V code pairs -> bf16 operand words.  Word w holds a token pair's codes of
+// four channels, the pair's first token in bits [0, 16), the second in
+// [16, 32), channel 4q + i in bits [4i, 4i + 4) of each half.  Channel
+// positions 0 and 2 become bf16 128 + n, positions 1 and 3 bf16 128 + 8n.
+// m0 = 0x000F000F, m1 = 0x00780078 (held in VGPRs).
+template <int POS>
+__device__ __forceinline__ uint32_t v_pair(uint32_t w, uint32_t m0, uint32_t m1) {
+    constexpr uint32_t kC = 0x43004300u;
+    if constexpr (POS == 0) return and_or(w, m0, kC);
+    if constexpr (POS == 1) return and_or(w >> 1, m1, kC);
+    if constexpr (POS == 2) return and_or(w >> 8, m0, kC);
+    return and_or(w >> 9, m1, kC);
+}
+
+// SHARE (query group <= 8): lanes j and j + 8 hold the same head and each
+// forms q' = q s for half of the channel blocks; lane j receives the other
+// half from lane j + 8.  Columns 8-15 of the score tile are then unused.
+template <bool SHARE>
 __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const int b, const int h,
                                              const int page0, const int page1, const int seg,
                                              const int n_seg, const int lane, lds_u8* smeta,
@@ -240,15 +282,16 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     const int j = lane & 15;
     const int g = lane >> 4;
     const int G = p.group;
+    const int hj = SHARE ? (j & 7) : j;          // head of this lane's query
     const int len = min(max(p.context_lens[b], 0), p.max_ctx);
     const int nq = kivi_nq(len, kp.residual);
     const int pq = nq / kKiviGroup;
 
-    // query (B operand): head j, channels 32g + 8kb + [0, 8)
+    // query (B operand): head hj, channels 32g + 8kb + [0, 8)
     u32x4_t qb[4];
-    if (j < G) {
+    if (hj < G) {
         const u32x4_t* qp =
-            (const u32x4_t*)(p.q + ((size_t)b * p.n_q + (size_t)h * G + j) * kHeadDim + 32 * g);
+            (const u32x4_t*)(p.q + ((size_t)b * p.n_q + (size_t)h * G + hj) * kHeadDim + 32 * g);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qb[kb] = qp[kb];
     } else {
@@ -256,23 +299,28 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         for (int kb = 0; kb < 4; ++kb) qb[kb] = u32x4_t{0u, 0u, 0u, 0u};
     }
 
-    // q pairs with one half cleared: dot2(qlo, s) = q_even s_even, dot2(qhi, s) = q_odd s_odd
-    u32x4_t qlo[4], qhi[4];
+    // fp32 query values of the channel blocks whose q' this lane forms:
+    // blocks kb0 + kk (kb0 = 0, or 2 on lanes 8-15 when sharing)
+    constexpr int NKB = SHARE ? 2 : 4;
+    const int kb0 = SHARE ? 2 * (j >> 3) : 0;
+    float qf[NKB][8];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            qlo[kb][i] = qb[kb][i] & 0x0000FFFFu;
-            qhi[kb][i] = qb[kb][i] & 0xFFFF0000u;
+            uint32_t w = qb[kk][i];
+            if constexpr (SHARE) w = (j >= 8) ? qb[kk + 2][i] : w;
+            qf[kk][2 * i] = bf16lo(w);
+            qf[kk][2 * i + 1] = bf16hi(w);
         }
 
     KiviState st;
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.pc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     st.m_used = -INFINITY;
     st.lsum = 0.0f;
     st.pz = 0.0f;
-    st.pcorr = 0.0f;
 
     // read-only block table through the constant address space: page-id loads
     // are scalar and never wait for the K/V vector loads in flight
@@ -281,9 +329,17 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     const int qend = min(page1, pq);            // quantized pages of this segment: [page0, qend)
     const int n_q = qend - page0;
     const uint32_t kC = 0x43434343u;           // bf16 high byte of 128 + n
+    const u32x4_t kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const uint32_t neg_lo = opaque_sgpr(0x0000BF80u), neg_hi = opaque_sgpr(0xBF800000u);   // bf16 (-1, 0), (0, -1)
+    // V nibble masks, opaque to the compiler so that they stay in two VGPRs
+    // instead of being rematerialised before every and_or
+    uint32_t vm0 = 0x000F000Fu, vm1 = 0x00780078u;
+    __asm__("" : "+v"(vm0));
+    __asm__("" : "+v"(vm1));
 
     const int off_kc = j * (kHeadDim / 2) + 16 * g;
-    const int off_vc = 4 * g * (kHeadDim / 2) + 4 * j;
+    const int off_vc = (2 * g) * (2 * kHeadDim / 2) + 8 * j;
+    constexpr int kPairBytes = 2 * kHeadDim / 2;                   // one V token pair
     constexpr int kMetaOff = kKiviGroup * kHeadDim / 2;          // metadata after the codes
 
     auto load = [&](KiviBuf& cb, const int c) {
@@ -303,9 +359,9 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                cb.vc[hp][r] = __builtin_amdgcn_raw_buffer_load_b32(
-                    rv, off_vc + (16 * hp + r) * (kHeadDim / 2), 0, 0);
+            for (int rp = 0; rp < 2; ++rp)
+                cb.vc[hp][rp] = __builtin_amdgcn_raw_buffer_load_b64(
+                    rv, off_vc + (8 * hp + rp) * kPairBytes, 0, 0);
         cb.km[0] = __builtin_amdgcn_raw_buffer_load_b32(rk, kMetaOff + 4 * lane, 0, 0);
         cb.km[1] = __builtin_amdgcn_raw_buffer_load_b32(rk, kMetaOff + 256 + 4 * lane, 0, 0);
         cb.vm = __builtin_amdgcn_raw_buffer_load_b32(rv, kMetaOff + 4 * lane, 0, 0);
@@ -315,57 +371,75 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         // spread the page's metadata through the wave's LDS slot (the wave's LDS
         // operations execute in order: the reads below see these writes, and the
         // previous page's reads were issued before them)
-        *(__attribute__((address_space(3))) uint32_t*)(smeta + 4 * lane) = cb.km[0];
-        *(__attribute__((address_space(3))) uint32_t*)(smeta + 256 + 4 * lane) = cb.km[1];
-        *(__attribute__((address_space(3))) uint32_t*)(smeta + 512 + 4 * lane) = cb.vm;
+        *(lds_u32*)(smeta + 4 * lane) = cb.km[0];
+        *(lds_u32*)(smeta + 256 + 4 * lane) = cb.km[1];
+        *(lds_u32x2*)(smeta + 512 + 8 * lane) = u32x2_t{cb.km[0] << 16, cb.km[0] & 0xFFFF0000u};
+        *(lds_u32x2*)(smeta + 1024 + 8 * lane) = u32x2_t{cb.vm << 16, cb.vm & 0xFFFF0000u};
         const lds_u8* m = smeta;
-        u32x4_t ks[4], kz[4];
-        const lds_u8* zsrc = (j == 0) ? m + 256 + 64 * g : (j == 1 ? m + 64 * g : szero);
+        u32x4_t kz[4];
+        // rows 4i of the bias tile are the zero-points, rows 4i + 1 the scales, so
+        // that every lane group finds its column's two sums in d2[0], d2[1]
+        const lds_u8* zsrc = ((j & 3) == 0) ? m + 256 + 64 * g : ((j & 3) == 1 ? m + 64 * g : szero);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            ks[kb] = *(const __attribute__((address_space(3))) u32x4_t*)(m + 64 * g + 16 * kb);
-            kz[kb] = *(const __attribute__((address_space(3))) u32x4_t*)(zsrc + 16 * kb);
-        }
-        u32x2_t vs[2], vz[2];
+        for (int kb = 0; kb < 4; ++kb) kz[kb] = *(const lds_u32x4*)(zsrc + 16 * kb);
+        f32x4_t sf[NKB][2];
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                sf[kk][x] = *(const lds_f32x4*)(m + 512 + 4 * (32 * g + 8 * (kb0 + kk) + 4 * x));
+        f32x4_t vsf[2], vzf[2];
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
-            vs[hp] = *(const __attribute__((address_space(3))) u32x2_t*)(m + 512 + 32 * hp + 8 * g);
-            vz[hp] = *(const __attribute__((address_space(3))) u32x2_t*)(m + 576 + 32 * hp + 8 * g);
+            vsf[hp] = *(const lds_f32x4*)(m + 1024 + 4 * (16 * hp + 4 * g));
+            vzf[hp] = *(const lds_f32x4*)(m + 1152 + 4 * (16 * hp + 4 * g));
         }
 
-        // bias = sum_c q_c z_c - 128 sum_c q_c s_c for head j (rows 0, 1 of an MFMA)
+        // bias = sum_c q_c z_c - 128 sum_c q_c s_c for head j, added to the
+        // scaled scores (not used as the accumulators' start, so that the QK
+        // products do not wait for it)
         f32x4_t d2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) d2 = mfma_16x16x32_bf16(kz[kb], qb[kb], d2);
-        const float bias = __shfl(d2[0] - 128.0f * d2[1], j);
+        const float bias_s = (d2[0] - 128.0f * d2[1]) * p.score_scale;
 
-        // q' = q s, at most 16 significant bits: its truncation to bf16 and the
-        // remainder are both exact bf16 values; slots ordered like the code bytes
-        u32x4_t bh[4], bl[4];
+        // q' = q s, exact in fp32 (at most 16 significant bits): its bf16
+        // rounding and the remainder are both exact bf16 values; slots ordered
+        // like the code bytes (channel pairs (0,2), (1,3), (4,6), (5,7) of a block)
+        u32x4_t bh[NKB], bl[NKB];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            float qs[8];
+        for (int kk = 0; kk < NKB; ++kk) {
+            float a[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                qs[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qlo[kb][i]), as_bf16x2(ks[kb][i]),
-                                                            0.0f, false);
-                qs[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qhi[kb][i]), as_bf16x2(ks[kb][i]),
-                                                                0.0f, false);
-            }
+            for (int c = 0; c < 8; ++c) a[c] = qf[kk][c] * sf[kk][c >> 2][c & 3];
             const int ord[8] = {0, 2, 1, 3, 4, 6, 5, 7};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float a0 = qs[ord[2 * e]], a1 = qs[ord[2 * e + 1]];
-                const uint32_t u0 = f32_to_bits(a0), u1 = f32_to_bits(a1);
-                bh[kb][e] = perm(u1, u0, 0x07060302u);
-                bl[kb][e] = pack_bf16_rne(a0 - bits_to_f32(u0 & 0xFFFF0000u), a1 - bits_to_f32(u1 & 0xFFFF0000u));
+                const u32x2_t hl = split_bf16(a[ord[2 * e]], a[ord[2 * e + 1]], neg_lo, neg_hi);
+                bh[kk][e] = hl[0];
+                bl[kk][e] = hl[1];
             }
+        }
+        u32x4_t BH[4], BL[4];
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) {
+            BH[kk] = bh[kk];
+            BL[kk] = bl[kk];
+        }
+        if constexpr (SHARE) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    BH[2 + kk][e] = row_swap8(bh[kk][e]);
+                    BL[2 + kk][e] = row_swap8(bl[kk][e]);
+                }
         }
 
         float sc[2][4];
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
-            f32x4_t d = {bias, bias, bias, bias};
+            f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const uint32_t w = cb.kc[hp][kb];
@@ -373,56 +447,51 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 const uint32_t y = (w >> 4) & 0x0F0F0F0Fu;
                 const u32x4_t a = {perm(kC, x, 0x04010400u), perm(kC, y, 0x04010400u),
                                    perm(kC, x, 0x04030402u), perm(kC, y, 0x04030402u)};
-                d = mfma_16x16x32_bf16(a, bh[kb], d);
-                d = mfma_16x16x32_bf16(a, bl[kb], d);
+                d = mfma_16x16x32_bf16(a, BH[kb], d);
+                d = mfma_16x16x32_bf16(a, BL[kb], d);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sc[hp][r] = d[r] * p.score_scale;
+            for (int r = 0; r < 4; ++r) sc[hp][r] = __builtin_fmaf(d[r], p.score_scale, bias_s);
         }
 
         float pp[2][4];
         kivi_softmax(st, sc, pp, g);
 
-        // P' = p s_t as bf16 hi + lo; offset and zero-point sums
+        // P' = p s_t as bf16 hi + lo, and the zero-point sum
         u32x4_t ahi, alo;
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
 #pragma unroll
             for (int rp = 0; rp < 2; ++rp) {
-                const uint32_t sw = vs[hp][rp];
-                const uint32_t zw = vz[hp][rp];
                 const float p0 = pp[hp][2 * rp], p1 = pp[hp][2 * rp + 1];
-                const float a0 = p0 * bf16lo(sw), a1 = p1 * bf16hi(sw);
-                st.pz += p0 * bf16lo(zw) + p1 * bf16hi(zw);
-                const uint32_t hw = pack_bf16_rne(a0, a1);
-                const uint32_t lw = pack_bf16_rne(a0 - bf16lo(hw), a1 - bf16hi(hw));
-                ahi[2 * hp + rp] = hw;
-                alo[2 * hp + rp] = lw;
-                st.pcorr += (bf16lo(hw) + bf16hi(hw)) + (bf16lo(lw) + bf16hi(lw));
+                st.pz += p0 * vzf[hp][2 * rp] + p1 * vzf[hp][2 * rp + 1];
+                const u32x2_t hl = split_bf16(p0 * vsf[hp][2 * rp], p1 * vsf[hp][2 * rp + 1], neg_lo, neg_hi);
+                ahi[2 * hp + rp] = hl[0];
+                alo[2 * hp + rp] = hl[1];
             }
         }
+        // the code offset 128 multiplies exactly the P' the MFMAs consume: sum them
+        // with the same MFMAs against ones
+        st.pc = mfma_16x16x32_bf16(ahi, kOnes, st.pc);
+        st.pc = mfma_16x16x32_bf16(alo, kOnes, st.pc);
 
-        // V codes: channel 8j + t, tokens 16 hp + 4g + r
-        uint32_t xs[2][4], ys[2][4];
-#pragma unroll
-        for (int hp = 0; hp < 2; ++hp)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                xs[hp][r] = cb.vc[hp][r] & 0x0F0F0F0Fu;
-                ys[hp][r] = (cb.vc[hp][r] >> 4) & 0x0F0F0F0Fu;
-            }
+        // V: channel 8j + t, tokens 16 hp + 4g + [0, 4) in slots 2 hp + [0, 2)
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const uint32_t by = (uint32_t)(t >> 1);
-            const uint32_t sel = by | (0x0Cu << 8) | ((4u + by) << 16) | (0x0Cu << 24);
             u32x4_t bv;
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
                 for (int rp = 0; rp < 2; ++rp) {
-                    const uint32_t s0 = (t & 1) ? ys[hp][2 * rp] : xs[hp][2 * rp];
-                    const uint32_t s1 = (t & 1) ? ys[hp][2 * rp + 1] : xs[hp][2 * rp + 1];
-                    bv[2 * hp + rp] = perm(s1, s0, sel) | 0x43004300u;
+                    const uint32_t w = cb.vc[hp][rp][t >> 2];
+                    uint32_t o;
+                    switch (t & 3) {
+                        case 0: o = v_pair<0>(w, vm0, vm1); break;
+                        case 1: o = v_pair<1>(w, vm0, vm1); break;
+                        case 2: o = v_pair<2>(w, vm0, vm1); break;
+                        default: o = v_pair<3>(w, vm0, vm1); break;
+                    }
+                    bv[2 * hp + rp] = o;
                 }
             st.acc[t] = mfma_16x16x32_bf16(ahi, bv, st.acc[t]);
             st.acc[t] = mfma_16x16x32_bf16(alo, bv, st.acc[t]);
@@ -448,7 +517,9 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         }
     }
 
-    // ---- fp16 window chunks: tokens nq + 32 (c - pq) + [0, 32)
+    // ---- fp16 window chunks: tokens nq + 32 (c - pq) + [0, 32).  The odd
+    // channels t of the accumulators hold 8x their value (code positions 1 and
+    // 3 above), so the window adds 8 p v there.
     const int rfirst = max(page0, pq);
     if (rfirst < page1) {
         u32x4_t qh[4];
@@ -482,7 +553,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
             }
             float pp[2][4];
             kivi_softmax(st, sc, pp, g);
-            u32x4_t ahi, alo;
+            u32x4_t ahi, alo, ahi8, alo8;
             u32x4_t vr[2][4];
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
@@ -500,6 +571,10 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                     const uint32_t hw = pack_f16_rne(a0, a1);
                     ahi[2 * hp + rp] = hw;
                     alo[2 * hp + rp] = pack_f16_rne(a0 - f16_value(hw & 0xFFFFu), a1 - f16_value(hw >> 16));
+                    const float b0 = 8.0f * a0, b1 = 8.0f * a1;
+                    const uint32_t h8 = pack_f16_rne(b0, b1);
+                    ahi8[2 * hp + rp] = h8;
+                    alo8[2 * hp + rp] = pack_f16_rne(b0 - f16_value(h8 & 0xFFFFu), b1 - f16_value(h8 >> 16));
                 }
             }
 #pragma unroll
@@ -511,33 +586,34 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
 #pragma unroll
                     for (int rp = 0; rp < 2; ++rp)
                         bv[2 * hp + rp] = perm(vr[hp][2 * rp + 1][t >> 1], vr[hp][2 * rp][t >> 1], sel);
-                st.acc[t] = mfma_16x16x32_f16(ahi, bv, st.acc[t]);
-                st.acc[t] = mfma_16x16x32_f16(alo, bv, st.acc[t]);
+                st.acc[t] = mfma_16x16x32_f16((t & 1) ? ahi8 : ahi, bv, st.acc[t]);
+                st.acc[t] = mfma_16x16x32_f16((t & 1) ? alo8 : alo, bv, st.acc[t]);
             }
         }
     }
 
-    // ---- epilogue (same output format as the FP8 / INT8 kernel)
-    float lsum = st.lsum, pz = st.pz, pcorr = st.pcorr;
+    // ---- epilogue (same output format as the FP8 / INT8 kernel):
+    // O = ((acc - 128 pc) / (1 or 8) + sum p z) / l
+    float lsum = st.lsum, pz = st.pz;
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
     pz += __shfl_xor(pz, 16);
     pz += __shfl_xor(pz, 32);
-    pcorr += __shfl_xor(pcorr, 16);
-    pcorr += __shfl_xor(pcorr, 32);
     const size_t row0 = (size_t)b * p.n_q + (size_t)h * G;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int head = 4 * g + r;
         const float lr = __shfl(lsum, head & 15);
-        const float add = __shfl(pz, head & 15) - 128.0f * __shfl(pcorr, head & 15);
+        const float pzh = __shfl(pz, head & 15);
+        const float off = 128.0f * st.pc[r];
         if (head < G) {
             const float inv = 1.0f / lr;
             f32x4_t o0, o1;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                o0[t] = (st.acc[t][r] + add) * inv;
-                o1[t] = (st.acc[t + 4][r] + add) * inv;
+                const float f = (t & 1) ? 0.125f : 1.0f;
+                o0[t] = ((st.acc[t][r] - off) * f + pzh) * inv;
+                o1[t] = ((st.acc[t + 4][r] - off) * f + pzh) * inv;
             }
             float* dst = (n_seg == 1)
                              ? p.out + (row0 + head) * kHeadDim + 8 * j
@@ -556,6 +632,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     }
 }
 
+template <bool SHARE>
 __global__ __launch_bounds__(256) void kivi_split_kernel(KiviSplitParams kp) {
     __shared__ __attribute__((aligned(16))) uint8_t s_meta[kSplitThreads / 64][kKiviMetaBytes];
     __shared__ __attribute__((aligned(16))) uint32_t s_zero[64];
@@ -564,21 +641,25 @@ __global__ __launch_bounds__(256) void kivi_split_kernel(KiviSplitParams kp) {
     lds_u8* smeta = (lds_u8*)&s_meta[wid][0];
     const lds_u8* szero = (const lds_u8*)&s_zero[0];
     for_each_segment<kKiviGroup>(kp.s, [&](int b, int h, int page0, int page1, int seg, int n_seg, int lane) {
-        kivi_segment(kp, b, h, page0, page1, seg, n_seg, lane, smeta, szero);
+        kivi_segment<SHARE>(kp, b, h, page0, page1, seg, n_seg, lane, smeta, szero);
     });
 }
 
-hipError_t kivi_split_occupancy(size_t lds_bytes, int* blocks_per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)&kivi_split_kernel,
-                                                        kSplitThreads, lds_bytes);
+static const void* kivi_split_fn(int group) {
+    return group <= 8 ? (const void*)&kivi_split_kernel<true> : (const void*)&kivi_split_kernel<false>;
+}
+
+hipError_t kivi_split_occupancy(int group, size_t lds_bytes, int* blocks_per_cu) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kivi_split_fn(group), kSplitThreads,
+                                                        lds_bytes);
 }
 
 hipError_t launch_kivi_split(const KiviSplitParams& p, int grid, size_t lds_bytes, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     KiviSplitParams args = p;
     void* kargs[] = {&args};
-    return hipLaunchKernel((const void*)&kivi_split_kernel, dim3(grid), dim3(kSplitThreads), kargs,
-                           lds_bytes, stream);
+    return hipLaunchKernel(kivi_split_fn(p.s.group), dim3(grid), dim3(kSplitThreads), kargs, lds_bytes,
+                           stream);
 }
 
 }  // namespace kvq

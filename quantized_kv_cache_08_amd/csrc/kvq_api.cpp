@@ -162,7 +162,7 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     const size_t lds = ((size_t)num_seqs + 1) * sizeof(int32_t);
     const bool kivi = c->dtype == KVQ_INT4_KIVI;
     int per_cu = 0;
-    hipError_t e = kivi ? kivi_split_occupancy(lds, &per_cu)
+    hipError_t e = kivi ? kivi_split_occupancy(p.group, lds, &per_cu)
                         : split_occupancy(c->dtype, is_static, c->page_size, lds, &per_cu);
     if (e != hipSuccess) return KVQ_ERR_HIP;
     const int cus = device_cus();

@@ -53,6 +53,26 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two fp32 -> bf16 pairs hi = rne(a), lo = rne(a - hi) (low half = a0);
+// returns {hi, lo}.  The remainders a - hi are exact and come from one dot
+// product each, a + hi.x * m0.x + hi.y * m0.y with m0 = (-1, 0) and
+// m1 = (0, -1) as bf16 pairs.  The caller passes m0 = 0x0000BF80 and
+// m1 = 0xBF800000 from registers the compiler cannot see through (see
+// opaque_sgpr): as inline constants they are encoded as the fp32 -1.0, and
+// the remainders came out wrong.
+__device__ __forceinline__ u32x2_t split_bf16(float a0, float a1, uint32_t m0, uint32_t m1) {
+    const uint32_t hi = pack_bf16_rne(a0, a1);
+    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(hi), as_bf16x2(m0), a0, false);
+    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(hi), as_bf16x2(m1), a1, false);
+    return u32x2_t{hi, pack_bf16_rne(r0, r1)};
+}
+
+// A wave-uniform constant in an SGPR that the compiler treats as unknown.
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t c) {
+    __asm__("" : "+s"(c));
+    return c;
+}
+
 // Four fp32 -> four OCP E4M3 codes (byte i = code of the i-th argument):
 // nearest-even through the gfx950 converter after an explicit clamp to
 // +-448 (saturation); -0 keeps its sign; NaN gives 0x7F.
@@ -116,6 +136,17 @@ __device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
 __device__ __forceinline__ f32x4_t mfma_16x16x32_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of a
+// 16-column MFMA tile) with the gfx950 lane-swap instructions, in registers.
+__device__ __forceinline__ float max_over_groups(float v) {
+    const uint32_t u = f32_to_bits(v);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float m = fmaxf(bits_to_f32(s32[0]), bits_to_f32(s32[1]));
+    const uint32_t w = f32_to_bits(m);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    return fmaxf(bits_to_f32(s16[0]), bits_to_f32(s16[1]));
 }
 
 template <typename T>

@@ -216,8 +216,11 @@ def kivi_read_seq(bt: BuiltKivi, b: int):
     vwin = bt.cache.v_window[b].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)[:, rows]
     res = []
     for h in range(w.num_kv_heads):
-        def unpack(rec):
-            packed = rec[:, h, :ps * d // 2].reshape(npg * ps, d // 2)
+        def unpack(rec, pairs=False):
+            packed = rec[:, h, :ps * d // 2]
+            if pairs:   # V: the rows of a token pair interleaved in 16-bit units
+                packed = packed.reshape(npg, ps // 2, d // 4, 2, 2).transpose(0, 1, 3, 2, 4)
+            packed = packed.reshape(npg * ps, d // 2)
             codes = np.empty((npg * ps, d), dtype=np.uint8)
             codes[:, 0::2] = packed & 0x0F
             codes[:, 1::2] = packed >> 4
@@ -227,7 +230,7 @@ def kivi_read_seq(bt: BuiltKivi, b: int):
         k_z = krec[:, h, off + 2 * d:off + 4 * d].copy().view(np.uint16)
         v_s = vrec[:, h, off:off + 2 * ps].copy().view(np.uint16).reshape(-1)
         v_z = vrec[:, h, off + 2 * ps:off + 4 * ps].copy().view(np.uint16).reshape(-1)
-        res.append(dict(nq=nq, k_codes=unpack(krec), k_s=k_s, k_z=k_z, v_codes=unpack(vrec), v_s=v_s, v_z=v_z,
+        res.append(dict(nq=nq, k_codes=unpack(krec), k_s=k_s, k_z=k_z, v_codes=unpack(vrec, pairs=True), v_s=v_s, v_z=v_z,
                         k_res=kwin[h], v_res=vwin[h]))
     return res
 
