@@ -409,12 +409,8 @@ __global__ __launch_bounds__(256) void split_kernel(SplitParams p) {
     });
 }
 
-// Merge of the partial results of one (sequence, query head):
-//   L = max_i lse_i,  w_i = 2^(lse_i - L),  out = sum_i w_i o_i / sum_i w_i,
-//   lse = (L + log2 sum_i w_i) * ln 2.
-// One wave per (sequence, query head): the partial lse values are read one
-// per lane, and each lane merges two channels with eight partial rows in
-// flight at a time.
+// Merge of the partial results of each (sequence, query head), one wave per
+// row (merge_rows).
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & 63;
     const long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -424,9 +420,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const int h = hq / p.group;
     const long long chunk = p.ws_header[0];
     const int cb = p.ws_pfx[b + 1] - p.ws_pfx[b];      // item weight: pages + start-up weight
-    float* out = p.out + idx * kHeadDim + 2 * lane;
     if (cb == 0) {
-        *(float2*)out = make_float2(0.0f, 0.0f);
+        *(float2*)(p.out + idx * kHeadDim + 2 * lane) = make_float2(0.0f, 0.0f);
         if (p.lse && lane == 0) p.lse[idx] = -INFINITY;
         return;
     }
@@ -434,41 +429,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const long long item_start = (long long)p.ws_pfx[b] * p.n_kv + (long long)h * cb;
     const int n_seg = (int)((item_start + pb - 1) / chunk - item_start / chunk + 1);
     if (n_seg == 1) return;   // written by the split kernel
-    const float* pl = p.part_lse + idx * p.max_parts;
-    const float* po = p.part_o + idx * p.max_parts * kHeadDim + 2 * lane;
-    float L = -INFINITY;
-    for (int i = lane; i < n_seg; i += 64) L = fmaxf(L, pl[i]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) L = fmaxf(L, __shfl_xor(L, o));
-    float ws = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int base = 0; base < n_seg; base += 64) {
-        const int cnt = min(64, n_seg - base);
-        const float wl = lane < cnt ? __builtin_amdgcn_exp2f(pl[base + lane] - L) : 0.0f;
-        ws += wl;
-        int i = 0;
-        for (; i + 8 <= cnt; i += 8) {
-            float2 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = *(const float2*)(po + (size_t)(base + i + u) * kHeadDim);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float w = __shfl(wl, i + u);
-                o0 += w * v[u].x;
-                o1 += w * v[u].y;
-            }
-        }
-        for (; i < cnt; ++i) {
-            const float2 v = *(const float2*)(po + (size_t)(base + i) * kHeadDim);
-            const float w = __shfl(wl, i);
-            o0 += w * v.x;
-            o1 += w * v.y;
-        }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
-    const float inv = 1.0f / ws;
-    *(float2*)out = make_float2(o0 * inv, o1 * inv);
-    if (p.lse && lane == 0) p.lse[idx] = (L + __log2f(ws)) * kLn2;
+    merge_rows<1>(p.part_lse + idx * p.max_parts, p.part_o + idx * p.max_parts * kHeadDim, p.max_parts, n_seg,
+                  p.out + idx * kHeadDim, p.lse ? p.lse + idx : nullptr, lane);
 }
 
 template <int DT, bool STATIC, int PS>

@@ -15,6 +15,71 @@
 
 namespace kvq {
 
+// Merge of the partial results of NH (sequence, query head) rows:
+//   L = max_i lse_i,  w_i = 2^(lse_i - L),  out = sum_i w_i o_i / sum_i w_i,
+//   lse = (L + log2 sum_i w_i) * ln 2,
+// computed online over groups of 8 partial rows.  Called by all 64 lanes of a
+// wave; each lane merges channels 2 lane, 2 lane + 1.  Row r's partial lse
+// values are pl[r * max_parts + i] and its partial rows po[(r * max_parts + i)
+// * 128 + ..], i < n.  All loads of a group (8 lse values and 8 partial rows
+// per merged row, every lane reading the same lse words) are issued before
+// any is used, so that a merge of up to 8 partials costs one memory round
+// trip.
+template <int NH>
+__device__ __forceinline__ void merge_rows(const float* pl, const float* po, int max_parts, int n,
+                                           float* out, float* lse, int lane) {
+    float m[NH], s[NH], o0[NH], o1[NH];
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+        m[r] = -INFINITY;
+        s[r] = 0.0f;
+        o0[r] = 0.0f;
+        o1[r] = 0.0f;
+    }
+    for (int base = 0; base < n; base += 8) {
+        const int cnt = min(8, n - base);
+        float l[NH][8];
+        float2 v[NH][8];
+#pragma unroll
+        for (int r = 0; r < NH; ++r)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (u < cnt) {
+                    const float* row = po + ((size_t)r * max_parts + base + u) * kHeadDim + 2 * lane;
+                    l[r][u] = pl[(size_t)r * max_parts + base + u];
+                    v[r][u] = *(const float2*)row;
+                } else {
+                    l[r][u] = -INFINITY;
+                    v[r][u] = make_float2(0.0f, 0.0f);
+                }
+            }
+#pragma unroll
+        for (int r = 0; r < NH; ++r) {
+            float mx = m[r];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) mx = fmaxf(mx, l[r][u]);
+            const float a = __builtin_amdgcn_exp2f(m[r] - mx);    // 0 on the first group (m = -inf)
+            s[r] *= a;
+            o0[r] *= a;
+            o1[r] *= a;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float w = __builtin_amdgcn_exp2f(l[r][u] - mx);
+                s[r] += w;
+                o0[r] += w * v[r][u].x;
+                o1[r] += w * v[r][u].y;
+            }
+            m[r] = mx;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NH; ++r) {
+        const float inv = 1.0f / s[r];
+        *(float2*)(out + (size_t)r * kHeadDim + 2 * lane) = make_float2(o0[r] * inv, o1[r] * inv);
+        if (lse && lane == 0) lse[r] = (m[r] + __log2f(s[r])) * kLn2;
+    }
+}
+
 // Pages of context a sequence of `len` tokens occupies (len clamped to max_ctx).
 __device__ __forceinline__ int pages_of(int len, int max_ctx, int ps) {
     len = len < 0 ? 0 : (len > max_ctx ? max_ctx : len);

@@ -141,6 +141,57 @@ def test_empty_and_mixed_lengths():
         check_seq(bt, out, lse, b)
 
 
+def test_attention_equals_split_then_reduce_and_workspace_reuse():
+    """kvq_decode_attention must equal kvq_decode_split + kvq_decode_reduce bit for
+    bit, repeated calls on one workspace must give the same bits, and a smaller
+    batch on that workspace must match the two calls on that batch."""
+    w = small("tiny", batch=6)
+    lens = np.array([0, 511, 17, 300, 0, 129])
+    say("one launch vs two launches build")
+    bt = H.build(w, lens=lens)
+    B, Hq, d = bt.q.shape[0], bt.q.shape[1], bt.w.head_dim
+    scale = 1.0 / np.sqrt(d)
+    for part in (0, 1, 3, 16):
+        say("one launch vs two launches part", part)
+        nbytes = kvq.decode_workspace_bytes(bt.cache, B, Hq, bt.max_ctx, part)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        outs = []
+        for rep in range(3):
+            out = torch.full((B, Hq, d), float("nan"), device="cuda")
+            lse = torch.full((B, Hq), float("nan"), device="cuda")
+            kvq.decode_attention(bt.cache, bt.q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws, out,
+                                 lse, part)
+            outs.append((out.cpu(), lse.cpu()))
+        out2 = torch.full((B, Hq, d), float("nan"), device="cuda")
+        lse2 = torch.full((B, Hq), float("nan"), device="cuda")
+        kvq.decode_split(bt.cache, bt.q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws2, out2, lse2, part)
+        kvq.decode_reduce(bt.cache, B, Hq, bt.max_ctx, ws2, out2, lse2, part)
+        torch.cuda.synchronize()
+        for o, l in outs:
+            assert torch.equal(o, out2.cpu()) and torch.equal(l, lse2.cpu())
+        for b in range(B):
+            if lens[b] > 0:
+                check_seq(bt, out2, lse2, b)
+        # a smaller batch (the last three sequences) on the same workspace, against
+        # the two launches on that batch
+        sub = slice(3, 6)
+        args = (bt.q[sub].contiguous(), bt.block_table[sub].contiguous(), bt.context_lens[sub].contiguous(),
+                bt.max_ctx, scale)
+        res = []
+        for one in (True, False):
+            o = torch.full((3, Hq, d), float("nan"), device="cuda")
+            l = torch.full((3, Hq), float("nan"), device="cuda")
+            if one:
+                kvq.decode_attention(bt.cache, *args, ws, o, l, part)
+            else:
+                kvq.decode_split(bt.cache, *args, ws2, o, l, part)
+                kvq.decode_reduce(bt.cache, 3, Hq, bt.max_ctx, ws2, o, l, part)
+            res.append((o.cpu(), l.cpu()))
+        torch.cuda.synchronize()
+        assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
 def test_unwritten_slots_keep_sentinel():
     w = small("tiny", batch=2)
     lens = np.array([20, 40])
