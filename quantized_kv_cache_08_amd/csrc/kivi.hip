@@ -208,16 +208,9 @@ struct KiviState {
     float m_used, lsum, pz;
 };
 
-// Online-softmax update with the scores of one 32-token chunk (exp2 domain);
-// returns p per (half, r) in pp.  All four lane groups hold the same head.
-__device__ __forceinline__ void kivi_softmax(KiviState& st, float (&sc)[2][4], float (&pp)[2][4],
-                                             const int g) {
-    float mx = sc[0][0];
-#pragma unroll
-    for (int hp = 0; hp < 2; ++hp)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[hp][r]);
-    mx = max_over_groups(mx);
+// Rescale of the running state when a chunk's maximum mx (equal on all lanes
+// of a head) exceeds m_used by more than the headroom.
+__device__ __forceinline__ void kivi_rescale(KiviState& st, const float mx, const int g) {
     if (__builtin_expect(__any(mx > st.m_used + kKiviHeadroom), 0)) {
         __asm__ volatile("");   // keep the rare rescale a branch, not straight-line code
         const float m_new = fmaxf(st.m_used, mx);
@@ -233,11 +226,25 @@ __device__ __forceinline__ void kivi_softmax(KiviState& st, float (&sc)[2][4], f
             for (int t = 0; t < 8; ++t) st.acc[t][r] *= ar;
         }
     }
+}
+
+// Online-softmax update with the scores of one 32-token chunk (exp2 domain);
+// returns p per (half, r) in pp.  All four lane groups hold the same head.
+// keep = false: the lane's column duplicates another lane's head; it follows
+// the maximum but contributes p = 0.
+__device__ __forceinline__ void kivi_softmax(KiviState& st, float (&sc)[2][4], float (&pp)[2][4],
+                                             const int g, const bool keep) {
+    float mx = sc[0][0];
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[hp][r]);
+    kivi_rescale(st, max_over_groups(mx), g);
 #pragma unroll
     for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(sc[hp][r] - st.m_used);
+            const float pr = keep ? __builtin_amdgcn_exp2f(sc[hp][r] - st.m_used) : 0.0f;
             st.lsum += pr;
             pp[hp][r] = pr;
         }
@@ -254,6 +261,21 @@ __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t vmask, uint32_t 
     uint32_t o;
     __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(o) : "v"(w), "v"(vmask), "s"(c));
     return o;
+}
+
+// The same update when lanes j and j + 8 of a row share head j % 8, each
+// holding four of its scores (tokens 4g + r of one 16-token half).
+__device__ __forceinline__ void kivi_softmax_half(KiviState& st, const float (&sc)[4], float (&pp)[4],
+                                                  const int g) {
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = max_over_groups(mx);
+    mx = fmaxf(mx, bits_to_f32(row_swap8(f32_to_bits(mx))));
+    kivi_rescale(st, mx, g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        pp[r] = __builtin_amdgcn_exp2f(sc[r] - st.m_used);
+        st.lsum += pp[r];
+    }
 }
 
 // V code pairs -> bf16 operand words.  Word w holds a token pair's codes of
@@ -388,11 +410,14 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
 #pragma unroll
             for (int x = 0; x < 2; ++x)
                 sf[kk][x] = *(const lds_f32x4*)(m + 512 + 4 * (32 * g + 8 * (kb0 + kk) + 4 * x));
+        // V scales / zero-points of tokens 16 hp + 4g + [0, 4); when sharing, a
+        // lane needs only its own half hp = j / 8
         f32x4_t vsf[2], vzf[2];
 #pragma unroll
-        for (int hp = 0; hp < 2; ++hp) {
-            vsf[hp] = *(const lds_f32x4*)(m + 1024 + 4 * (16 * hp + 4 * g));
-            vzf[hp] = *(const lds_f32x4*)(m + 1152 + 4 * (16 * hp + 4 * g));
+        for (int hp = 0; hp < (SHARE ? 1 : 2); ++hp) {
+            const int hq = SHARE ? (j >> 3) : hp;
+            vsf[hp] = *(const lds_f32x4*)(m + 1024 + 4 * (16 * hq + 4 * g));
+            vzf[hp] = *(const lds_f32x4*)(m + 1152 + 4 * (16 * hq + 4 * g));
         }
 
         // bias = sum_c q_c z_c - 128 sum_c q_c s_c for head j, added to the
@@ -436,7 +461,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 }
         }
 
-        float sc[2][4];
+        f32x4_t dq[2];
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
             f32x4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -450,24 +475,53 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 d = mfma_16x16x32_bf16(a, BH[kb], d);
                 d = mfma_16x16x32_bf16(a, BL[kb], d);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[hp][r] = __builtin_fmaf(d[r], p.score_scale, bias_s);
+            dq[hp] = d;
         }
 
-        float pp[2][4];
-        kivi_softmax(st, sc, pp, g);
-
-        // P' = p s_t as bf16 hi + lo, and the zero-point sum
         u32x4_t ahi, alo;
+        if constexpr (SHARE) {
+            // Columns 8-15 are unused: lanes 8-15 of each row take the second
+            // half (tokens 16 + 4g + r) of head j - 8 (DPP row rotation by 8,
+            // written to banks 2-3 only), so each lane exponentiates and splits
+            // four scores, and lane j gets the second half's P' words back.
+            float sc[4];
 #pragma unroll
-        for (int hp = 0; hp < 2; ++hp) {
+            for (int r = 0; r < 4; ++r) {
+                const float dv = bits_to_f32((uint32_t)__builtin_amdgcn_update_dpp(
+                    (int)f32_to_bits(dq[0][r]), (int)f32_to_bits(dq[1][r]), 0x128, 0xF, 0xC, false));
+                sc[r] = __builtin_fmaf(dv, p.score_scale, bias_s);
+            }
+            float pp[4];
+            kivi_softmax_half(st, sc, pp, g);
+            u32x2_t hl[2];
 #pragma unroll
             for (int rp = 0; rp < 2; ++rp) {
-                const float p0 = pp[hp][2 * rp], p1 = pp[hp][2 * rp + 1];
-                st.pz += p0 * vzf[hp][2 * rp] + p1 * vzf[hp][2 * rp + 1];
-                const u32x2_t hl = split_bf16(p0 * vsf[hp][2 * rp], p1 * vsf[hp][2 * rp + 1], neg_lo, neg_hi);
-                ahi[2 * hp + rp] = hl[0];
-                alo[2 * hp + rp] = hl[1];
+                const float p0 = pp[2 * rp], p1 = pp[2 * rp + 1];
+                st.pz += p0 * vzf[0][2 * rp] + p1 * vzf[0][2 * rp + 1];
+                hl[rp] = split_bf16(p0 * vsf[0][2 * rp], p1 * vsf[0][2 * rp + 1], neg_lo, neg_hi);
+            }
+            ahi = u32x4_t{hl[0][0], hl[1][0], row_swap8(hl[0][0]), row_swap8(hl[1][0])};
+            alo = u32x4_t{hl[0][1], hl[1][1], row_swap8(hl[0][1]), row_swap8(hl[1][1])};
+        } else {
+            float sc[2][4];
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[hp][r] = __builtin_fmaf(dq[hp][r], p.score_scale, bias_s);
+            float pp[2][4];
+            kivi_softmax(st, sc, pp, g, true);
+
+            // P' = p s_t as bf16 hi + lo, and the zero-point sum
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+#pragma unroll
+                for (int rp = 0; rp < 2; ++rp) {
+                    const float p0 = pp[hp][2 * rp], p1 = pp[hp][2 * rp + 1];
+                    st.pz += p0 * vzf[hp][2 * rp] + p1 * vzf[hp][2 * rp + 1];
+                    const u32x2_t hl = split_bf16(p0 * vsf[hp][2 * rp], p1 * vsf[hp][2 * rp + 1], neg_lo, neg_hi);
+                    ahi[2 * hp + rp] = hl[0];
+                    alo[2 * hp + rp] = hl[1];
+                }
             }
         }
         // the code offset 128 multiplies exactly the P' the MFMAs consume: sum them
@@ -552,7 +606,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                     sc[hp][r] = (rbase + 16 * hp + 4 * g + r < len) ? d[r] * p.score_scale : -INFINITY;
             }
             float pp[2][4];
-            kivi_softmax(st, sc, pp, g);
+            kivi_softmax(st, sc, pp, g, !SHARE || j < 8);   // lanes 8-15 duplicate heads 0-7 when sharing
             u32x4_t ahi, alo, ahi8, alo8;
             u32x4_t vr[2][4];
 #pragma unroll
@@ -599,6 +653,10 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     lsum += __shfl_xor(lsum, 32);
     pz += __shfl_xor(pz, 16);
     pz += __shfl_xor(pz, 32);
+    if constexpr (SHARE) {     // lanes j and j + 8 hold halves of head j's sums
+        lsum += bits_to_f32(row_swap8(f32_to_bits(lsum)));
+        pz += bits_to_f32(row_swap8(f32_to_bits(pz)));
+    }
     const size_t row0 = (size_t)b * p.n_q + (size_t)h * G;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
