@@ -389,7 +389,21 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         cb.vm = __builtin_amdgcn_raw_buffer_load_b32(rv, kMetaOff + 4 * lane, 0, 0);
     };
 
-    auto compute_quant = [&](KiviBuf& cb) {
+    // A page is computed in three parts so that the loop can overlap one
+    // page's PV products (back) with the next page's QK work (front):
+    //   front: metadata to LDS, bias, q' = q s, QK products;
+    //   mid:   softmax and P' (state update; holds the rare rescale branch);
+    //   back:  offset sums and PV products of a page whose mid has run.
+    struct Front {
+        f32x4_t dq[2];
+        f32x4_t vsf[2], vzf[2];
+        float bias_s;
+    };
+    struct Pend {
+        u32x2_t vc[2][2];
+        u32x4_t ahi, alo;
+    };
+    auto front = [&](KiviBuf& cb, Front& F) {
         // spread the page's metadata through the wave's LDS slot (the wave's LDS
         // operations execute in order: the reads below see these writes, and the
         // previous page's reads were issued before them)
@@ -412,12 +426,11 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 sf[kk][x] = *(const lds_f32x4*)(m + 512 + 4 * (32 * g + 8 * (kb0 + kk) + 4 * x));
         // V scales / zero-points of tokens 16 hp + 4g + [0, 4); when sharing, a
         // lane needs only its own half hp = j / 8
-        f32x4_t vsf[2], vzf[2];
 #pragma unroll
         for (int hp = 0; hp < (SHARE ? 1 : 2); ++hp) {
             const int hq = SHARE ? (j >> 3) : hp;
-            vsf[hp] = *(const lds_f32x4*)(m + 1024 + 4 * (16 * hq + 4 * g));
-            vzf[hp] = *(const lds_f32x4*)(m + 1152 + 4 * (16 * hq + 4 * g));
+            F.vsf[hp] = *(const lds_f32x4*)(m + 1024 + 4 * (16 * hq + 4 * g));
+            F.vzf[hp] = *(const lds_f32x4*)(m + 1152 + 4 * (16 * hq + 4 * g));
         }
 
         // bias = sum_c q_c z_c - 128 sum_c q_c s_c for head j, added to the
@@ -426,7 +439,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         f32x4_t d2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) d2 = mfma_16x16x32_bf16(kz[kb], qb[kb], d2);
-        const float bias_s = (d2[0] - 128.0f * d2[1]) * p.score_scale;
+        F.bias_s = (d2[0] - 128.0f * d2[1]) * p.score_scale;
 
         // q' = q s, exact in fp32 (at most 16 significant bits): its bf16
         // rounding and the remainder are both exact bf16 values; slots ordered
@@ -461,7 +474,6 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 }
         }
 
-        f32x4_t dq[2];
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
             f32x4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -475,9 +487,15 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 d = mfma_16x16x32_bf16(a, BH[kb], d);
                 d = mfma_16x16x32_bf16(a, BL[kb], d);
             }
-            dq[hp] = d;
+            F.dq[hp] = d;
         }
+    };
 
+    auto mid = [&](const Front& F, const KiviBuf& cb, Pend& pd) {
+        const f32x4_t* dq = F.dq;
+        const f32x4_t* vsf = F.vsf;
+        const f32x4_t* vzf = F.vzf;
+        const float bias_s = F.bias_s;
         u32x4_t ahi, alo;
         if constexpr (SHARE) {
             // Columns 8-15 are unused: lanes 8-15 of each row take the second
@@ -524,6 +542,16 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 }
             }
         }
+        pd.ahi = ahi;
+        pd.alo = alo;
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+            for (int rp = 0; rp < 2; ++rp) pd.vc[hp][rp] = cb.vc[hp][rp];
+    };
+
+    auto back = [&](const Pend& pd) {
+        const u32x4_t ahi = pd.ahi, alo = pd.alo;
         // the code offset 128 multiplies exactly the P' the MFMAs consume: sum them
         // with the same MFMAs against ones
         st.pc = mfma_16x16x32_bf16(ahi, kOnes, st.pc);
@@ -537,7 +565,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
             for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
                 for (int rp = 0; rp < 2; ++rp) {
-                    const uint32_t w = cb.vc[hp][rp][t >> 2];
+                    const uint32_t w = pd.vc[hp][rp][t >> 2];
                     uint32_t o;
                     switch (t & 3) {
                         case 0: o = v_pair<0>(w, vm0, vm1); break;
@@ -553,22 +581,43 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     };
 
     // ---- quantized pages: the loads of the next page are in flight while a
-    // page is computed.  The scheduling barriers keep those loads issued
-    // before the compute, whose first step (the LDS writes) would otherwise be
-    // hoisted above them and wait with nothing in flight.
+    // page is computed, and page c's back part shares a basic block with page
+    // c + 1's front part (independent work to interleave).  The scheduling
+    // barriers keep the loads issued before the compute, whose first step (the
+    // LDS writes) would otherwise be hoisted above them and wait with nothing
+    // in flight.
     if (n_q > 0) {
         KiviBuf b0, b1;
+        Pend pd;
         load(b0, 0);
-        for (int c = 0;;) {
-            load(b1, c + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_quant(b0);
-            if (++c >= n_q) break;
+        load(b1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            Front F;
+            front(b0, F);
+            mid(F, b0, pd);
+        }
+        for (int c = 1; c < n_q;) {
             load(b0, c + 1);
             __builtin_amdgcn_sched_barrier(0);
-            compute_quant(b1);
+            {
+                Front F;
+                front(b1, F);
+                back(pd);
+                mid(F, b1, pd);
+            }
             if (++c >= n_q) break;
+            load(b1, c + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                Front F;
+                front(b0, F);
+                back(pd);
+                mid(F, b0, pd);
+            }
+            ++c;
         }
+        back(pd);
     }
 
     // ---- fp16 window chunks: tokens nq + 32 (c - pq) + [0, 32).  The odd
