@@ -57,14 +57,40 @@ __device__ __forceinline__ uint32_t kivi_code(float x, float zf, float sf) {
     return (uint32_t)t;
 }
 
+// Writes the fp16 window row of new token i of sequence b, KV head h (k or v
+// by kv), 8 channels from lane part (16 lanes per row).
+__device__ __forceinline__ void kivi_window_row(const KiviAppendParams& p, int b, int h, int i, int kv, int part) {
+    const int n0 = max(p.context_lens[b], 0);
+    const int m = p.offsets[b + 1] - p.offsets[b];
+    const int pos = n0 + i;
+    if (i >= m || pos < kivi_nq(n0 + m, p.residual)) return;    // quantized straight from the input
+    const size_t src = ((size_t)(p.offsets[b] + i) * p.n_kv + h) * kHeadDim + 8 * part;
+    const size_t dst = (((size_t)b * p.n_kv + h) * p.window + pos % p.window) * kHeadDim + 8 * part;
+    const u32x4_t w = *(const u32x4_t*)((kv ? p.v : p.k) + src);
+    u32x4_t o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_f16_rne(bf16lo(w[e]), bf16hi(w[e]));
+    *(u32x4_t*)((kv ? p.v_window : p.k_window) + dst) = o;
+}
+
 // One workgroup quantizes one 32-token group of one (sequence, KV head): K
-// per channel (one thread per channel), V per token (one wave per 16 tokens,
-// two channels per lane).  Token rows come from the fp16 window (tokens held
-// before this call) or from the new bf16 rows (rounded to fp16).
-__global__ __launch_bounds__(128) void kivi_flush_kernel(KiviAppendParams p) {
+// per channel (waves 0-1, one thread per channel) and, at the same time, V per
+// token (waves 2-3, 16 tokens per wave, two channels per lane).  Token rows
+// come from the fp16 window (tokens held before this call) or from the new
+// bf16 rows (rounded to fp16).
+// ONE_TOKEN (calls that append one token per sequence): workgroup x = 1, which
+// has no group to flush then, also writes the new token's window row.  Its
+// ring row cannot be one the flush reads: those hold positions p with
+// n0 - (residual + 31) <= p < n0, and the ring has window >= residual + 32 rows.
+template <bool ONE_TOKEN>
+__global__ __launch_bounds__(256) void kivi_flush_kernel(KiviAppendParams p) {
 #pragma clang fp contract(off)
     const int b = blockIdx.z;
     const int h = blockIdx.y;
+    if (ONE_TOKEN && blockIdx.x == 1) {
+        if (threadIdx.x < 32) kivi_window_row(p, b, h, 0, (int)(threadIdx.x >> 4), (int)(threadIdx.x & 15));
+        return;
+    }
     const int n0 = max(p.context_lens[b], 0);
     const int m = p.offsets[b + 1] - p.offsets[b];
     if (m <= 0) return;
@@ -79,21 +105,36 @@ __global__ __launch_bounds__(128) void kivi_flush_kernel(KiviAppendParams p) {
     const size_t wrow0 = ((size_t)b * p.n_kv + h) * p.window;
     const int in0 = p.offsets[b];
 
-    auto value = [&](const uint16_t* win, const uint16_t* in, int pos, int c) -> float {
-        if (pos < n0) return f16_value(win[(wrow0 + pos % p.window) * kHeadDim + c]);
-        const float x = bf16lo(in[((size_t)(in0 + pos - n0) * p.n_kv + h) * kHeadDim + c]);
-        return (float)(_Float16)x;
+    // Token t of the group: window row (t0 + t) mod window if it was held before
+    // this call, else new input row.  The source is selected per token (uniform)
+    // and the 16-bit word converted after the load, so that all of a thread's
+    // loads are in flight together.
+    const int base = grp * kKiviGroup;
+    const int r0 = base % p.window;
+    auto src = [&](const uint16_t* win, const uint16_t* in, int t, int c) -> const uint16_t* {
+        const int pos = base + t;
+        int r = r0 + t;
+        if (r >= p.window) r -= p.window;              // t < 32 <= window
+        return pos < n0 ? win + (wrow0 + r) * kHeadDim + c
+                        : in + ((size_t)(in0 + max(pos - n0, 0)) * p.n_kv + h) * kHeadDim + c;
+    };
+    auto value = [&](uint16_t w, int t) -> float {
+        return base + t < n0 ? f16_value(w) : (float)(_Float16)bf16lo(w);
     };
 
-    // ---- K: channel c over the group's 32 tokens
     uint8_t* krec = p.k_pages + ((size_t)page * p.n_kv + h) * (size_t)p.rec_k;
-    {
+    uint8_t* vrec = p.v_pages + ((size_t)page * p.n_kv + h) * (size_t)p.rec_v;
+    if (tid < kHeadDim) {
+        // ---- K: channel c over the group's 32 tokens
         const int c = tid;
+        uint16_t wv[kKiviGroup];
+#pragma unroll
+        for (int t = 0; t < kKiviGroup; ++t) wv[t] = *src(p.k_window, p.k, t, c);
         float x[kKiviGroup];
         float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
         for (int t = 0; t < kKiviGroup; ++t) {
-            x[t] = value(p.k_window, p.k, grp * kKiviGroup + t, c);
+            x[t] = value(wv[t], t);
             lo = fminf(lo, x[t]);
             hi = fmaxf(hi, x[t]);
         }
@@ -104,29 +145,32 @@ __global__ __launch_bounds__(128) void kivi_flush_kernel(KiviAppendParams p) {
 #pragma unroll
         for (int t = 0; t < kKiviGroup; ++t) {
             const uint32_t code = kivi_code(x[t], zf, sf);
-            const uint32_t other = (uint32_t)__shfl_xor((int)code, 1);
+            const uint32_t other = dpp_mov<0xB1>(code);   // quad_perm [1,0,3,2]: lane c ^ 1
             if ((c & 1) == 0) krec[t * (kHeadDim / 2) + (c >> 1)] = (uint8_t)(code | (other << 4));
         }
         *(uint16_t*)(krec + kKiviGroup * kHeadDim / 2 + 2 * c) = (uint16_t)sb;
         *(uint16_t*)(krec + kKiviGroup * kHeadDim / 2 + 2 * kHeadDim + 2 * c) = (uint16_t)zb;
     }
 
-    // ---- V: token t over its 128 channels
-    uint8_t* vrec = p.v_pages + ((size_t)page * p.n_kv + h) * (size_t)p.rec_v;
-    {
-        const int w = tid >> 6;
+    else {
+        // ---- V: token t over its 128 channels (one wave per 16 tokens, two
+        // channels per lane; all 32 loads of a lane first)
+        const int w = (tid - kHeadDim) >> 6;
         const int l = tid & 63;
+        uint32_t wv[kKiviGroup / 2];
+#pragma unroll
         for (int i = 0; i < kKiviGroup / 2; ++i) {
             const int t = w * (kKiviGroup / 2) + i;
-            const int pos = grp * kKiviGroup + t;
-            const float x0 = value(p.v_window, p.v, pos, 2 * l);
-            const float x1 = value(p.v_window, p.v, pos, 2 * l + 1);
-            float lo = fminf(x0, x1), hi = fmaxf(x0, x1);
+            const uint16_t* a = src(p.v_window, p.v, t, 2 * l);
+            wv[i] = (uint32_t)a[0] | ((uint32_t)a[1] << 16);
+        }
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                lo = fminf(lo, __shfl_xor(lo, o));
-                hi = fmaxf(hi, __shfl_xor(hi, o));
-            }
+        for (int i = 0; i < kKiviGroup / 2; ++i) {
+            const int t = w * (kKiviGroup / 2) + i;
+            const float x0 = value((uint16_t)(wv[i] & 0xFFFFu), t);
+            const float x1 = value((uint16_t)(wv[i] >> 16), t);
+            const float lo = wave_extreme<false>(fminf(x0, x1));
+            const float hi = wave_extreme<true>(fmaxf(x0, x1));
             const uint32_t zb = bf16_down_bits(lo);
             const float zf = bf16lo(zb);
             const uint32_t sb = bf16_up_bits((hi - zf) / 15.0f);
@@ -147,31 +191,19 @@ __global__ __launch_bounds__(128) void kivi_flush_kernel(KiviAppendParams p) {
 // 16 threads per (token, KV head) row, 8 channels each.  Runs after the
 // flush kernel, which may still read window rows this kernel overwrites.
 __global__ __launch_bounds__(256) void kivi_window_kernel(KiviAppendParams p) {
-    const int b = blockIdx.z;
-    const int h = blockIdx.y;
     const int i = (int)blockIdx.x * 16 + (int)(threadIdx.x >> 4);
-    const int part = threadIdx.x & 15;
-    const int m = p.offsets[b + 1] - p.offsets[b];
-    if (i >= m) return;
-    const int n0 = max(p.context_lens[b], 0);
-    const int pos = n0 + i;
-    if (pos < kivi_nq(n0 + m, p.residual)) return;      // quantized straight from the input
-    const size_t src = ((size_t)(p.offsets[b] + i) * p.n_kv + h) * kHeadDim + 8 * part;
-    const size_t dst = (((size_t)b * p.n_kv + h) * p.window + pos % p.window) * kHeadDim + 8 * part;
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv) {
-        const u32x4_t w = *(const u32x4_t*)((kv ? p.v : p.k) + src);
-        u32x4_t o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = pack_f16_rne(bf16lo(w[e]), bf16hi(w[e]));
-        *(u32x4_t*)((kv ? p.v_window : p.k_window) + dst) = o;
-    }
+    for (int kv = 0; kv < 2; ++kv) kivi_window_row(p, blockIdx.z, blockIdx.y, i, kv, threadIdx.x & 15);
 }
 
 hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream) {
     if (p.num_seqs <= 0 || p.max_new <= 0) return hipSuccess;
     const int groups = (p.max_new + kKiviGroup - 1) / kKiviGroup + 1;
-    hipLaunchKernelGGL(kivi_flush_kernel, dim3(groups, p.n_kv, p.num_seqs), dim3(128), 0, stream, p);
+    if (p.max_new == 1) {      // one launch: flush and window row (see kivi_flush_kernel)
+        hipLaunchKernelGGL(kivi_flush_kernel<true>, dim3(groups, p.n_kv, p.num_seqs), dim3(256), 0, stream, p);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(kivi_flush_kernel<false>, dim3(groups, p.n_kv, p.num_seqs), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kivi_window_kernel, dim3((p.max_new + 15) / 16, p.n_kv, p.num_seqs), dim3(256), 0,

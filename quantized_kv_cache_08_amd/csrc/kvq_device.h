@@ -138,15 +138,38 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32_f16(u32x4_t a, u32x4_t b, f32x4
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-// Maximum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups of a
-// 16-column MFMA tile) with the gfx950 lane-swap instructions, in registers.
-__device__ __forceinline__ float max_over_groups(float v) {
+// Maximum (minimum) over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane
+// groups of a 16-column MFMA tile) with the gfx950 lane-swap instructions, in
+// registers.
+template <bool MAX>
+__device__ __forceinline__ float extreme_over_groups(float v) {
     const uint32_t u = f32_to_bits(v);
     const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const float m = fmaxf(bits_to_f32(s32[0]), bits_to_f32(s32[1]));
+    const float a0 = bits_to_f32(s32[0]), a1 = bits_to_f32(s32[1]);
+    const float m = MAX ? fmaxf(a0, a1) : fminf(a0, a1);
     const uint32_t w = f32_to_bits(m);
     const auto s16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-    return fmaxf(bits_to_f32(s16[0]), bits_to_f32(s16[1]));
+    const float b0 = bits_to_f32(s16[0]), b1 = bits_to_f32(s16[1]);
+    return MAX ? fmaxf(b0, b1) : fminf(b0, b1);
+}
+__device__ __forceinline__ float max_over_groups(float v) { return extreme_over_groups<true>(v); }
+
+// DPP move within rows of 16 lanes (row_ror:n = 0x120 + n, quad_perm = 0x00-0xFF).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+
+// Maximum (minimum) over the whole wave in registers: rotations by 1, 2, 4, 8
+// within each row of 16 lanes, then across the four rows.
+template <bool MAX>
+__device__ __forceinline__ float wave_extreme(float v) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+    v = op(v, bits_to_f32(dpp_mov<0x121>(f32_to_bits(v))));
+    v = op(v, bits_to_f32(dpp_mov<0x122>(f32_to_bits(v))));
+    v = op(v, bits_to_f32(dpp_mov<0x124>(f32_to_bits(v))));
+    v = op(v, bits_to_f32(dpp_mov<0x128>(f32_to_bits(v))));
+    return extreme_over_groups<MAX>(v);
 }
 
 template <typename T>
