@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--config", default="llama8b", choices=["tiny", "llama8b", "llama70b", "mixed", "kivi"])
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto)")
     ap.add_argument("--partition-pages", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time the whole step as replays of one HIP graph per cache replica (slower than "
+                         "eager launches on ROCm 7)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough CPU work budget for the oracle sample")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -290,16 +293,37 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    # per-kernel times: a pass of eager steps with an event between the launches
+    # (the events cost a few microseconds per step, so the whole-step time is
+    # taken in a second pass without them)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+
+    # whole-step time: the same steps as eager launches on the stream, or with
+    # --graph as replays of one HIP graph per cache replica
+    if not args.graph:
+        run = step
+    else:
+        graphs = []
+        for r in range(reps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        run = lambda i: graphs[i % reps].replay()     # noqa: E731
+    for i in range(args.warmup):
+        run(i)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        run(i)
     t_end.record()
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
@@ -324,7 +348,8 @@ def main():
         "config": {"workload": w.name, "description": w.description, "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": w.num_kv_heads, "head_dim": d, "page_size": w.page_size,
                    "context_tokens": by["tokens"], "max_context": max_ctx, "cache_replicas": reps,
-                   "partition_pages": args.partition_pages or "auto"},
+                   "partition_pages": args.partition_pages or "auto",
+                   "step_launch": "hip_graph" if args.graph else "eager"},
         "tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "decode_attention_kv_gbs": round(kv_gbs, 2),
         "pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),

@@ -34,16 +34,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     const long long th = row >> 1;
     const int tok = (int)(th / p.n_kv);
     const int h = (int)(th - (long long)tok * p.n_kv);
+    // the slot and the row are loaded together (the row's address does not
+    // depend on the slot)
     long long slot = -1;
-    if (active) slot = p.slot_mapping[tok];
-    active = active && slot >= 0 && slot < p.num_slots;
-
     u32x4_t w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
     if (active) {
+        slot = p.slot_mapping[tok];
         const uint16_t* src = (kv ? p.v : p.k) + ((size_t)tok * p.n_kv + h) * kHeadDim + 16 * li;
         w0 = *(const u32x4_t*)src;
         w1 = *(const u32x4_t*)(src + 8);
     }
+    active = active && slot >= 0 && slot < p.num_slots;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -65,9 +66,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
             float amax = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-            amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-            amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+            amax = group8_extreme<true>(amax);
             scale_bits = bf16_up_bits(amax / 448.0f);
             sf = bf16lo(scale_bits);
         }
@@ -86,12 +85,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
             lo = fminf(lo, x[i]);
             hi = fmaxf(hi, x[i]);
         }
-        lo = fminf(lo, __shfl_xor(lo, 1, 8));
-        lo = fminf(lo, __shfl_xor(lo, 2, 8));
-        lo = fminf(lo, __shfl_xor(lo, 4, 8));
-        hi = fmaxf(hi, __shfl_xor(hi, 1, 8));
-        hi = fmaxf(hi, __shfl_xor(hi, 2, 8));
-        hi = fmaxf(hi, __shfl_xor(hi, 4, 8));
+        lo = group8_extreme<false>(lo);
+        hi = group8_extreme<true>(hi);
         zero_bits = bf16_down_bits(lo);
         const float zf = bf16lo(zero_bits);
         const float range = hi - zf;

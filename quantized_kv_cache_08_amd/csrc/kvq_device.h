@@ -160,6 +160,17 @@ __device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
 }
 
+// Maximum (minimum) over each group of 8 lanes in registers: lane ^ 1 and
+// lane ^ 2 by quad permutations, then the mirror within the half row (lane
+// 7 - i), which pairs each quad with the other.
+template <bool MAX>
+__device__ __forceinline__ float group8_extreme(float v) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+    v = op(v, bits_to_f32(dpp_mov<0xB1>(f32_to_bits(v))));    // quad_perm [1,0,3,2]
+    v = op(v, bits_to_f32(dpp_mov<0x4E>(f32_to_bits(v))));    // quad_perm [2,3,0,1]
+    return op(v, bits_to_f32(dpp_mov<0x141>(f32_to_bits(v))));  // row_half_mirror
+}
+
 // Maximum (minimum) over the whole wave in registers: rotations by 1, 2, 4, 8
 // within each row of 16 lanes, then across the four rows.
 template <bool MAX>

@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 if not gpu_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
+import quantized_kv_cache_08_amd as kvq  # noqa: E402
 import synthetic  # noqa: E402
 from tests import kvq_harness as H  # noqa: E402
 
@@ -144,3 +145,38 @@ def test_kivi_full_size():
         ref = H.kivi_oracle_seq(bt, b)
         check_state(bt, b, ref)
         check_out(bt, out, lse, b, ref)
+
+
+def test_kivi_decode_step_as_hip_graph_matches_eager():
+    """One-token KIVI append (re-appending each sequence's last token, which
+    completes a group for the first length) and decode, captured as a HIP graph:
+    every replay, with eager work in between, reproduces the eager outputs."""
+    from tests.test_gpu_parity import _graph_replays_match
+    w = small(batch=2, num_q_heads=16, num_kv_heads=2)
+    lens = np.array([160, 300])
+    say("kivi graph step build")
+    bt = H.build_kivi(w, lens)
+    B, Hq, d = bt.q.shape[0], bt.q.shape[1], bt.w.head_dim
+    rows = [synthetic.gen_kv(w, b, int(lens[b]) - 1, 1, "cuda") for b in range(B)]
+    knew = torch.cat([r[0] for r in rows]).contiguous()
+    vnew = torch.cat([r[1] for r in rows]).contiguous()
+    offs = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    before = torch.from_numpy((lens - 1).astype(np.int32)).cuda()
+    ws = torch.empty(kvq.decode_workspace_bytes(bt.cache, B, Hq, bt.max_ctx, 2), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty_like(ws)
+    out = torch.empty(B, Hq, d, device="cuda")
+    lse = torch.empty(B, Hq, device="cuda")
+    out2 = torch.empty_like(out)
+    scale = 1.0 / np.sqrt(d)
+
+    def step():
+        kvq.kivi_append(bt.cache, knew, vnew, offs, before, bt.block_table, 1)
+        kvq.decode_split(bt.cache, bt.q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws, out, lse, 2)
+        kvq.decode_reduce(bt.cache, B, Hq, bt.max_ctx, ws, out, lse, 2)
+
+    def other():
+        kvq.decode_attention(bt.cache, bt.q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws2, out2, None, 2)
+
+    _graph_replays_match(step, [out, lse], other)
+    for b in range(B):
+        check_out(bt, out, lse, b, H.kivi_oracle_seq(bt, b))

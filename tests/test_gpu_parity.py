@@ -192,6 +192,62 @@ def test_attention_equals_split_then_reduce_and_workspace_reuse():
         assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
 
 
+def _graph_replays_match(step, outs, eager_other):
+    """Run step() eagerly, capture it in a HIP graph, and replay the graph three
+    times with eager work and synchronisations in between: every replay must
+    reproduce the eager outputs bit for bit."""
+    step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        eager_other()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), f"replay {rep}"
+
+
+def test_decode_step_as_hip_graph_matches_eager():
+    """Append one token per sequence (rewriting its own slot), split, reduce: as a
+    HIP graph on torch's capture stream, for FP8 and INT8."""
+    for dt in ("fp8", "int8"):
+        w = small("tiny", batch=3, dtype=dt)
+        lens = np.array([100, 257, 31])
+        say("graph step", dt)
+        bt = H.build(w, lens=lens)
+        B, Hq, d = bt.q.shape[0], bt.q.shape[1], bt.w.head_dim
+        rows = [synthetic.gen_kv(w, b, int(lens[b]) - 1, 1, "cuda") for b in range(B)]
+        knew = torch.cat([r[0] for r in rows]).contiguous()
+        vnew = torch.cat([r[1] for r in rows]).contiguous()
+        slots = torch.cat([H.slots_for(bt.layout, b, int(lens[b]) - 1, 1, w.page_size, "cuda") for b in range(B)])
+        ws = torch.empty(kvq.decode_workspace_bytes(bt.cache, B, Hq, bt.max_ctx, 3), dtype=torch.uint8,
+                         device="cuda")
+        ws2 = torch.empty_like(ws)
+        out = torch.empty(B, Hq, d, device="cuda")
+        lse = torch.empty(B, Hq, device="cuda")
+        out2 = torch.empty_like(out)
+        scale = 1.0 / np.sqrt(d)
+
+        def step():
+            kvq.append(bt.cache, knew, vnew, slots)
+            kvq.decode_split(bt.cache, bt.q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws, out, lse, 3)
+            kvq.decode_reduce(bt.cache, B, Hq, bt.max_ctx, ws, out, lse, 3)
+
+        def other():
+            kvq.decode_attention(bt.cache, bt.q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws2, out2, None, 3)
+
+        _graph_replays_match(step, [out, lse], other)
+        for b in range(B):
+            check_seq(bt, out, lse, b)
+
+
 def test_unwritten_slots_keep_sentinel():
     w = small("tiny", batch=2)
     lens = np.array([20, 40])
