@@ -167,7 +167,11 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     if (e != hipSuccess) return KVQ_ERR_HIP;
     const int cus = device_cus();
     if (cus <= 0 || per_cu <= 0) return KVQ_ERR_HIP;
-    const int grid = per_cu * cus;
+    // FP8: one workgroup (one wave per SIMD) per CU, although two fit: with
+    // two waves per SIMD the memory system holds more requests than it
+    // serves best, and the measured kernel time is about 2% longer
+    const int blocks_per_cu = (!kivi && c->dtype == KVQ_FP8_E4M3) ? std::min(per_cu, kFp8BlocksPerCu) : per_cu;
+    const int grid = blocks_per_cu * cus;
     p.total_waves = grid * (kSplitThreads / 64);
     if (kivi) {
         KiviSplitParams kp{};
