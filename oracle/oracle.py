@@ -247,6 +247,16 @@ def decode_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_H
     q = bf16_value(q_bf16).astype(np.float64)
     d = q.shape[-1]
     scale = (1.0 / np.sqrt(d)) if softmax_scale is None else softmax_scale
+    res = quantized_cache(k_bf16, v_bf16, dtype, mode, static_kv)
+    out, lse = attention(q, res["k_hat"], res["v_hat"], scale)
+    res["out"], res["lse"] = out, lse
+    return res
+
+
+def quantized_cache(k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD, static_kv=None):
+    """Store-time quantization of one sequence's K/V rows [T][n_kv][d] (bf16
+    bits) and their dequantized fp64 values: dict of K/V codes, scales, zeros
+    and k_hat / v_hat."""
     k_bf16 = _c(k_bf16, np.uint16)
     v_bf16 = _c(v_bf16, np.uint16)
     T, n_kv, _ = k_bf16.shape
@@ -259,6 +269,33 @@ def decode_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_H
         c, s, z = quantize_rows(dtype, mode, x, ss)
         res[name + "_codes"], res[name + "_scale"], res[name + "_zero"] = c, s, z
         res[name + "_hat"] = dequantize_rows(dtype, c, s, z)
-    out, lse = attention(q, res["k_hat"], res["v_hat"], scale)
+    return res
+
+
+# ---------------------------------------------------------------- verification step
+def verify_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD,
+                     static_kv=None, softmax_scale: Optional[float] = None):
+    """Reference for one sequence in a speculative-decoding verification pass.
+
+    The target model scores the K+1 newest positions of the sequence in one
+    pass over the quantized cache, dequantizing as it reads ("KV 캐시 양자화
+    (KV cache quantization) ...", molayo1419.me, section on the interaction
+    with speculative decoding).  q_bf16 [n_new][Hq][d] holds the queries of
+    those positions, whose own K/V rows are the last n_new of k_bf16 / v_bf16
+    [T][n_kv][d].  Position i (0 = oldest of the new ones) attends causally:
+    to cache positions t < T - n_new + 1 + i.  A position that sees no token
+    (T < n_new) gets out = 0 and lse = -inf.  Returns the dict of
+    quantized_cache plus fp64 out [n_new][Hq][d] and lse [n_new][Hq].
+    """
+    q = bf16_value(q_bf16).astype(np.float64)
+    n_new, Hq, d = q.shape
+    scale = (1.0 / np.sqrt(d)) if softmax_scale is None else softmax_scale
+    res = quantized_cache(k_bf16, v_bf16, dtype, mode, static_kv)
+    T = res["k_hat"].shape[0]
+    out = np.zeros((n_new, Hq, d), dtype=np.float64)
+    lse = np.full((n_new, Hq), -np.inf, dtype=np.float64)
+    for i in range(n_new):
+        n_vis = max(0, T - n_new + 1 + i)
+        out[i], lse[i] = attention(q[i], res["k_hat"][:n_vis], res["v_hat"][:n_vis], scale)
     res["out"], res["lse"] = out, lse
     return res

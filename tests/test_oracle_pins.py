@@ -414,3 +414,61 @@ def test_decode_reference_context_one_returns_value_row(oracle):
     for dt in (oracle.FP8, oracle.INT8):
         r = oracle.decode_reference(qb, kb, vb, dt)
         assert np.array_equal(r["out"][:4], np.repeat(r["v_hat"][0, :1], 4, 0))
+
+
+# --------------------------------------------------- verification (K+1 queries)
+def test_verify_reference_matches_masked_sdpa(oracle):
+    """Causal attention of the n_new newest positions against torch's
+    scaled_dot_product_attention with an explicit boolean mask, on the same
+    dequantized cache."""
+    rng = np.random.default_rng(23)
+    for dt in (oracle.FP8, oracle.INT8):
+        for (T, n_new, Hq, n_kv) in [(1, 1, 4, 1), (9, 4, 8, 2), (70, 3, 16, 2), (33, 16, 2, 2)]:
+            kb = _bf16(rng.standard_normal((T, n_kv, 128)) * 1.5)
+            vb = _bf16(rng.standard_normal((T, n_kv, 128)))
+            qb = _bf16(rng.standard_normal((n_new, Hq, 128)))
+            r = oracle.verify_reference(qb, kb, vb, dt, softmax_scale=0.0883)
+            G = Hq // n_kv
+            q = torch.from_numpy(oracle.bf16_value(qb).astype(np.float64)).permute(1, 0, 2)      # [Hq][n_new][d]
+            k = torch.from_numpy(np.repeat(r["k_hat"], G, axis=1)).permute(1, 0, 2)              # [Hq][T][d]
+            v = torch.from_numpy(np.repeat(r["v_hat"], G, axis=1)).permute(1, 0, 2)
+            i = torch.arange(n_new)[:, None]
+            t = torch.arange(T)[None, :]
+            mask = t < (T - n_new + 1 + i)                                                         # [n_new][T]
+            # (the oracle takes the softmax scale as an fp32 value, as the kernels do)
+            o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask,
+                                                                 scale=float(np.float32(0.0883)))
+            assert np.allclose(r["out"], o.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12), (dt, T, n_new)
+
+
+def test_verify_reference_special_cases(oracle):
+    rng = np.random.default_rng(24)
+    T, n_new, Hq, n_kv = 30, 4, 8, 2
+    kb = _bf16(rng.standard_normal((T, n_kv, 128))); vb = _bf16(rng.standard_normal((T, n_kv, 128)))
+    qb = _bf16(rng.standard_normal((n_new, Hq, 128)))
+    for dt in (oracle.FP8, oracle.INT8):
+        r = oracle.verify_reference(qb, kb, vb, dt)
+        # the newest position sees the whole cache: plain one-query decode
+        d = oracle.decode_reference(qb[-1], kb, vb, dt)
+        assert np.array_equal(r["out"][-1], d["out"]) and np.array_equal(r["lse"][-1], d["lse"])
+        # one new position is the decode step itself
+        r1 = oracle.verify_reference(qb[:1], kb, vb, dt)
+        d1 = oracle.decode_reference(qb[0], kb, vb, dt)
+        assert np.array_equal(r1["out"][0], d1["out"]) and np.array_equal(r1["lse"][0], d1["lse"])
+        # causality: changing the rows position i must not see leaves row i as it was
+        kb2, vb2 = kb.copy(), vb.copy()
+        kb2[T - 2:] = _bf16(rng.standard_normal((2, n_kv, 128)) * 4)
+        vb2[T - 2:] = _bf16(rng.standard_normal((2, n_kv, 128)) * 4)
+        r2 = oracle.verify_reference(qb, kb2, vb2, dt)
+        assert np.array_equal(r2["out"][:2], r["out"][:2]) and np.array_equal(r2["lse"][:2], r["lse"][:2])
+        assert not np.allclose(r2["out"][2:], r["out"][2:])
+    # identical keys: uniform weights over exactly the visible prefix
+    k1 = np.tile(_bf16(rng.standard_normal((1, 1, 128))), (T, 1, 1))
+    r = oracle.verify_reference(qb[:, :2], k1, vb[:, :1], oracle.FP8)
+    for i in range(n_new):
+        n_vis = T - n_new + 1 + i
+        assert np.allclose(r["out"][i], r["v_hat"][:n_vis, 0].mean(axis=0), atol=1e-12)
+    # fewer cached tokens than new positions: the first rows see nothing
+    r = oracle.verify_reference(qb, kb[:2], vb[:2], oracle.FP8)
+    assert not r["out"][:2].any() and np.all(np.isneginf(r["lse"][:2]))
+    assert np.all(np.isfinite(r["lse"][2:]))
