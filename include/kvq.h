@@ -197,6 +197,35 @@ kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t n
                              void* workspace, size_t workspace_bytes,
                              float* out, float* lse, hipStream_t stream);
 
+/* Speculative-decoding verification over the quantized paged cache: the
+ * target model scores the q_len = K + 1 newest positions of each sequence in
+ * one pass, reading the FP8 / INT8 cache and dequantizing as it reads
+ * ("KV 캐시 양자화(KV cache quantization) ...", molayo1419.me, section on the
+ * interaction with speculative decoding).  The K/V rows of those positions
+ * must already be in the cache (kvq_append), so context_lens[b] counts them.
+ * Position i of sequence b (0 = oldest of the q_len) attends causally:
+ *   out[b][i][h] = sum_t softmax_t(softmax_scale * q[b][i][h] . k^[t]) v^[t]
+ * over t < context_lens[b] - (q_len - 1 - i); a position that sees no token
+ * (context_lens[b] < q_len) gets out = 0 and lse = -inf.  q_len = 1 is
+ * kvq_decode_attention.
+ * q:     device bf16 [num_seqs][q_len][num_q_heads][head_dim]
+ * out:   device fp32 [num_seqs][q_len][num_q_heads][head_dim]
+ * lse:   device fp32 [num_seqs][q_len][num_q_heads] or NULL
+ * Other arguments as kvq_decode_attention; the workspace size comes from
+ * kvq_verify_workspace_bytes.  The q_len x (num_q_heads / num_kv_heads) query
+ * rows of a KV head are one 16-row tile: their product must be <= 16
+ * (KVQ_ERR_UNSUPPORTED otherwise), and KVQ_INT4_KIVI caches are not supported
+ * (KVQ_ERR_UNSUPPORTED).  The KV bytes are read once for all q_len rows. */
+kvq_status kvq_verify_workspace_bytes(const kvq_cache* cache, int32_t num_seqs, int32_t q_len,
+                                      int32_t num_q_heads, int32_t max_context_len,
+                                      int32_t partition_pages, size_t* bytes);
+kvq_status kvq_verify_attention(const kvq_cache* cache, const void* q, int32_t num_seqs, int32_t q_len,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, float softmax_scale,
+                                int32_t partition_pages, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, hipStream_t stream);
+
 /* The FP8 E4M3 encoder of kvq_append applied to n float32 values (nearest-even,
  * saturating at +-448, sign of zero kept, NaN -> 0x7F).  x: device fp32 [n],
  * codes: device u8 [n]. */

@@ -18,6 +18,7 @@ __all__ = [
     "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI",
     "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
     "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
+    "verify_workspace_bytes", "verify_attention",
     "decode_attention", "decode_split", "decode_reduce", "e4m3_encode", "status_string",
     "LIB_PATH",
 ]
@@ -75,6 +76,11 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_reduce.restype = ctypes.c_int
         L.kvq_decode_reduce.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32, _P,
                                         ctypes.c_size_t, _P, _P, _P]
+        L.kvq_verify_workspace_bytes.restype = ctypes.c_int
+        L.kvq_verify_workspace_bytes.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32, _I32,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+        L.kvq_verify_attention.restype = ctypes.c_int
+        L.kvq_verify_attention.argtypes = [ctypes.POINTER(CacheDesc), _P, _I32, _I32] + _DECODE_ARGS[3:]
         L.kvq_e4m3_encode.restype = ctypes.c_int
         L.kvq_e4m3_encode.argtypes = [_P, _P, ctypes.c_int64, _P]
         L.kvq_status_string.restype = ctypes.c_char_p
@@ -200,6 +206,27 @@ def decode_reduce(cache: Cache, num_seqs: int, num_q_heads: int, max_context_len
         ctypes.byref(cache.desc), num_seqs, num_q_heads, int(max_context_len), int(partition_pages),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse),
         _stream(stream)))
+
+
+def verify_workspace_bytes(cache: Cache, num_seqs: int, q_len: int, num_q_heads: int, max_context_len: int,
+                           partition_pages: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check("kvq_verify_workspace_bytes",
+           lib().kvq_verify_workspace_bytes(ctypes.byref(cache.desc), num_seqs, q_len, num_q_heads,
+                                            max_context_len, partition_pages, ctypes.byref(out)))
+    return int(out.value)
+
+
+def verify_attention(cache: Cache, q, block_table, context_lens, max_context_len: int, softmax_scale: float,
+                     workspace, out, lse=None, partition_pages: int = 0, stream=None) -> None:
+    """Causal attention of the q_len newest positions per sequence (kvq_verify_attention);
+    q [B][q_len][Hq][d] bf16, out [B][q_len][Hq][d] fp32."""
+    num_seqs, q_len, num_q_heads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    _check("kvq_verify_attention", lib().kvq_verify_attention(
+        ctypes.byref(cache.desc), _ptr(q), num_seqs, q_len, num_q_heads, _ptr(block_table),
+        int(block_table.shape[1]), _ptr(context_lens), int(max_context_len), float(softmax_scale),
+        int(partition_pages), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+        _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:

@@ -64,16 +64,25 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
     const int j = lane & 15;
     const int g = lane >> 4;
     const int G = p.group;
+    const int QL = p.q_len;
+    const int GQ = G * QL;                 // query rows of this KV head (<= 16)
     const int len = min(max(p.context_lens[b], 0), p.max_ctx);
     const int tok_base = page0 * PS;
     const int tok_end = min(len, page1 * PS);
+    // Query row j is position qi = j / G of the QL newest ones (query head
+    // h G + j % G) and sees the cache causally: tokens t < len - (QL - 1 - qi).
+    // With QL = 1 every row sees the whole context.
+    const int qi = j / G;
+    const int row_end = min(len - (QL - 1 - min(qi, QL - 1)), page1 * PS);
+    const int tail_from = min(len - (QL - 1), page1 * PS);   // first token some row cannot see
 
-    // ---- query operand (B of QK): head j, channels 32g + 8kb + [0, 8)
+    // ---- query operand (B of QK): row j, channels 32g + 8kb + [0, 8)
     u32x4_t qb[4];
     float qsum = 0.0f;
-    if (j < G) {
-        const u32x4_t* qp =
-            (const u32x4_t*)(p.q + ((size_t)b * p.n_q + (size_t)h * G + j) * kHeadDim + 32 * g);
+    if (j < GQ) {
+        const u32x4_t* qp = (const u32x4_t*)(p.q + (((size_t)b * QL + qi) * p.n_q + (size_t)h * G + (j - qi * G)) *
+                                                       kHeadDim +
+                                                   32 * g);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qb[kb] = qp[kb];
     } else {
@@ -98,7 +107,9 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
     f32x4_t acc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_used = -INFINITY;
+    // finite, so that a row that sees no token of a chunk (causal rows) gets
+    // p = exp2(-inf - m_used) = 0 instead of NaN; any finite score exceeds it
+    float m_used = -3.402823466e38f;   // -FLT_MAX
     float lsum = 0.0f;
     float pz = 0.0f;
 
@@ -158,7 +169,7 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
     // from being flattened into code that every chunk would execute.
     auto compute = [&](ChunkBuf& cb, const int c) {
         const int ctok = tok_base + c * 32;
-        const bool tail = ctok + 32 > tok_end;
+        const bool tail = ctok + 32 > tail_from;
         if (__builtin_expect(tail, 0)) {
             __asm__ volatile("");
             // rows past the end of the context may hold anything (including
@@ -217,7 +228,7 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
             for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (ctok + 16 * hp + 4 * g + r >= tok_end) sc[hp][r] = -INFINITY;
+                    if (ctok + 16 * hp + 4 * g + r >= row_end) sc[hp][r] = -INFINITY;
         }
 
         // ---- online softmax (per head j; all four lane groups agree)
@@ -273,7 +284,7 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
             for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (ctok + 16 * hp + 4 * g + r >= tok_end) {
+                    if (ctok + 16 * hp + 4 * g + r >= row_end) {
                         pp[hp][r] = 0.0f;
                         pzr[hp][r] = 0.0f;
                     }
@@ -371,14 +382,21 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
         pz += __shfl_xor(pz, 16);
         pz += __shfl_xor(pz, 32);
     }
-    const size_t row0 = (size_t)b * p.n_q + (size_t)h * G;   // first query head of the group
+    // Rows: output row of query row x is (b QL + x / G) n_q + h G + x % G;
+    // partial results are kept per (b, h, x) at vrow0 + x.  A row that saw no
+    // token (lsum = 0: causal rows of a short context) gives o = 0, lse = -inf.
+    const size_t vrow0 = ((size_t)b * p.n_kv + h) * GQ;
+    auto out_row = [&](int x) {
+        const int xi = x / G;
+        return ((size_t)b * QL + xi) * p.n_q + (size_t)h * G + (x - xi * G);
+    };
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int head = 4 * g + r;
         const float lr = __shfl(lsum, head & 15);
         const float pzr = (DT == kINT8) ? __shfl(pz, head & 15) : 0.0f;
-        if (head < G) {
-            const float inv = 1.0f / lr;
+        if (head < GQ) {
+            const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
             f32x4_t o0, o1;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -386,18 +404,18 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
                 o1[t] = (acc[t + 4][r] + pzr) * inv;
             }
             float* dst = (n_seg == 1)
-                             ? p.out + (row0 + head) * kHeadDim + 8 * j
-                             : p.part_o + ((row0 + head) * p.max_parts + seg) * kHeadDim + 8 * j;
+                             ? p.out + out_row(head) * kHeadDim + 8 * j
+                             : p.part_o + ((vrow0 + head) * p.max_parts + seg) * kHeadDim + 8 * j;
             *(f32x4_t*)dst = o0;
             *(f32x4_t*)(dst + 4) = o1;
         }
     }
-    if (g == 0 && j < G) {
-        const float l2 = m_used + __log2f(lsum);
+    if (g == 0 && j < GQ) {
+        const float l2 = lsum > 0.0f ? m_used + __log2f(lsum) : -INFINITY;
         if (n_seg == 1) {
-            if (p.lse) p.lse[row0 + j] = l2 * kLn2;
+            if (p.lse) p.lse[out_row(j)] = l2 * kLn2;
         } else {
-            p.part_lse[(row0 + j) * p.max_parts + seg] = l2;
+            p.part_lse[(vrow0 + j) * p.max_parts + seg] = l2;
         }
     }
 }
@@ -413,16 +431,24 @@ __global__ __launch_bounds__(256) void split_kernel(SplitParams p) {
 // row (merge_rows).
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & 63;
+    // idx: partial-result row (b, h, x), x < GQ = group q_len (see the split
+    // kernel's epilogue); orow: its output row
     const long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (idx >= (long long)p.num_seqs * p.n_q) return;
-    const int b = (int)(idx / p.n_q);
-    const int hq = (int)(idx - (long long)b * p.n_q);
-    const int h = hq / p.group;
+    const int GQ = p.group * p.q_len;
+    const long long per_seq = (long long)p.n_kv * GQ;
+    if (idx >= (long long)p.num_seqs * per_seq) return;
+    const int b = (int)(idx / per_seq);
+    const int hx = (int)(idx - (long long)b * per_seq);
+    const int h = hx / GQ;
+    const int x = hx - h * GQ;
+    const int xi = x / p.group;
+    const long long orow = ((long long)b * p.q_len + xi) * ((long long)p.n_kv * p.group) + (long long)h * p.group +
+                           (x - xi * p.group);
     const long long chunk = p.ws_header[0];
     const int cb = p.ws_pfx[b + 1] - p.ws_pfx[b];      // item weight: pages + start-up weight
     if (cb == 0) {
-        *(float2*)(p.out + idx * kHeadDim + 2 * lane) = make_float2(0.0f, 0.0f);
-        if (p.lse && lane == 0) p.lse[idx] = -INFINITY;
+        *(float2*)(p.out + orow * kHeadDim + 2 * lane) = make_float2(0.0f, 0.0f);
+        if (p.lse && lane == 0) p.lse[orow] = -INFINITY;
         return;
     }
     const int pb = cb - p.ws_header[1];
@@ -430,7 +456,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const int n_seg = (int)((item_start + pb - 1) / chunk - item_start / chunk + 1);
     if (n_seg == 1) return;   // written by the split kernel
     merge_rows<1>(p.part_lse + idx * p.max_parts, p.part_o + idx * p.max_parts * kHeadDim, p.max_parts, n_seg,
-                  p.out + idx * kHeadDim, p.lse ? p.lse + idx : nullptr, lane);
+                  p.out + orow * kHeadDim, p.lse ? p.lse + orow : nullptr, lane);
 }
 
 template <int DT, bool STATIC, int PS>
@@ -462,7 +488,7 @@ hipError_t launch_split(int dtype, bool static_scale, int page_size, const Split
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream) {
-    const long long rows = (long long)p.num_seqs * p.n_q;
+    const long long rows = (long long)p.num_seqs * p.n_kv * p.group * p.q_len;
     const long long grid = (rows + 3) / 4;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);

@@ -75,7 +75,7 @@ struct Plan {
     size_t off_pfx = 0, off_lse = 0, off_o = 0, total = 0;
 };
 
-Plan make_plan(int page_size, int num_seqs, int num_q_heads, int max_ctx, int partition_pages) {
+Plan make_plan(int page_size, int num_seqs, int num_q_heads, int max_ctx, int partition_pages, int q_len) {
     Plan pl;
     pl.max_pages = (max_ctx + page_size - 1) / page_size;
     const int mp = std::max(1, pl.max_pages);
@@ -92,7 +92,7 @@ Plan make_plan(int page_size, int num_seqs, int num_q_heads, int max_ctx, int pa
             pl.min_chunk = std::max(pl.min_chunk, bound);
         }
     }
-    const size_t rows = (size_t)num_seqs * (size_t)num_q_heads;
+    const size_t rows = (size_t)num_seqs * (size_t)num_q_heads * (size_t)q_len;
     pl.off_pfx = 256;
     pl.off_lse = pl.off_pfx + align256(((size_t)num_seqs + 1) * sizeof(int32_t));
     pl.off_o = pl.off_lse + align256(rows * pl.max_parts * sizeof(float));
@@ -104,21 +104,24 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
                         const int32_t* block_table, int32_t max_pages_per_seq,
                         const int32_t* context_lens, int32_t max_context_len,
                         int32_t partition_pages, void* workspace, size_t workspace_bytes,
-                        float* out, Plan* plan) {
+                        float* out, int32_t q_len, Plan* plan) {
     kvq_status st = check_cache(c, true);
     if (st != KVQ_OK) return st;
     if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_pages_per_seq < 0 ||
-        partition_pages < 0)
+        partition_pages < 0 || q_len < 1)
         return KVQ_ERR_INVALID;
     if (num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID;
     if (!valid_group(num_q_heads / c->num_kv_heads)) return KVQ_ERR_UNSUPPORTED;
+    // the query rows of one KV head (group x positions) form one 16-wide MFMA tile
+    if ((long long)q_len * (num_q_heads / c->num_kv_heads) > 16) return KVQ_ERR_UNSUPPORTED;
+    if (q_len > 1 && c->dtype == KVQ_INT4_KIVI) return KVQ_ERR_UNSUPPORTED;
     if ((long long)max_context_len > (long long)max_pages_per_seq * c->page_size)
         return KVQ_ERR_INVALID;
     if (num_seqs > 16383) return KVQ_ERR_UNSUPPORTED;   // prefix table lives in LDS
     if (c->dtype == KVQ_INT4_KIVI && num_seqs > c->max_seqs) return KVQ_ERR_INVALID;
     if (num_seqs == 0) return KVQ_OK;
     if (!q || !block_table || !context_lens || !out || !workspace) return KVQ_ERR_INVALID;
-    *plan = make_plan(c->page_size, num_seqs, num_q_heads, max_context_len, partition_pages);
+    *plan = make_plan(c->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, q_len);
     if (workspace_bytes < plan->total) return KVQ_ERR_WORKSPACE;
     return KVQ_OK;
 }
@@ -126,7 +129,8 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
 kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_t num_q_heads,
                      const int32_t* block_table, int32_t max_pages_per_seq,
                      const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
-                     const Plan& pl, void* workspace, float* out, float* lse, hipStream_t stream) {
+                     const Plan& pl, void* workspace, float* out, float* lse, int32_t q_len,
+                     hipStream_t stream) {
     const bool is_static = c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD;
     uint8_t* ws = (uint8_t*)workspace;
     SplitParams p{};
@@ -155,6 +159,7 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     p.max_parts = pl.max_parts;
     p.min_chunk = pl.min_chunk;
     p.forced_chunk = pl.forced_chunk;
+    p.q_len = q_len;
     p.static_head_stride = c->scale_mode == KVQ_SCALE_PER_HEAD ? 1 : 0;
     p.static_kv_stride = c->scale_mode == KVQ_SCALE_PER_HEAD ? c->num_kv_heads : 1;
     p.score_scale = softmax_scale * 1.4426950408889634f;
@@ -188,7 +193,7 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
 }
 
 kvq_status run_reduce(const kvq_cache* c, int32_t num_seqs, int32_t num_q_heads, const Plan& pl,
-                      void* workspace, float* out, float* lse, hipStream_t stream) {
+                      void* workspace, float* out, float* lse, int32_t q_len, hipStream_t stream) {
     uint8_t* ws = (uint8_t*)workspace;
     ReduceParams r{};
     r.part_o = (const float*)(ws + pl.off_o);
@@ -202,6 +207,7 @@ kvq_status run_reduce(const kvq_cache* c, int32_t num_seqs, int32_t num_q_heads,
     r.n_kv = c->num_kv_heads;
     r.group = num_q_heads / c->num_kv_heads;
     r.max_parts = pl.max_parts;
+    r.q_len = q_len;
     return launch_reduce(r, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
@@ -308,7 +314,7 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
     if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_pages < 0)
         return KVQ_ERR_INVALID;
     if (cache->page_size <= 0) return KVQ_ERR_INVALID;
-    *bytes = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages)
+    *bytes = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, 1)
                  .total;
     return KVQ_OK;
 }
@@ -322,10 +328,10 @@ kvq_status kvq_decode_split(const kvq_cache* cache, const void* q, int32_t num_s
     Plan pl;
     kvq_status st = check_decode(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq,
                                  context_lens, max_context_len, partition_pages, workspace,
-                                 workspace_bytes, out, &pl);
+                                 workspace_bytes, out, 1, &pl);
     if (st != KVQ_OK || num_seqs == 0) return st;
     return run_split(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
-                     max_context_len, softmax_scale, pl, workspace, out, lse, stream);
+                     max_context_len, softmax_scale, pl, workspace, out, lse, 1, stream);
 }
 
 kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t num_q_heads,
@@ -338,9 +344,9 @@ kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t n
         return KVQ_ERR_INVALID;
     if (num_seqs == 0) return KVQ_OK;
     if (!workspace || !out) return KVQ_ERR_INVALID;
-    Plan pl = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages);
+    Plan pl = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, 1);
     if (workspace_bytes < pl.total) return KVQ_ERR_WORKSPACE;
-    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, stream);
+    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, 1, stream);
 }
 
 kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t num_seqs,
@@ -352,12 +358,43 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
     Plan pl;
     kvq_status st = check_decode(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq,
                                  context_lens, max_context_len, partition_pages, workspace,
-                                 workspace_bytes, out, &pl);
+                                 workspace_bytes, out, 1, &pl);
     if (st != KVQ_OK || num_seqs == 0) return st;
     st = run_split(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
-                   max_context_len, softmax_scale, pl, workspace, out, lse, stream);
+                   max_context_len, softmax_scale, pl, workspace, out, lse, 1, stream);
     if (st != KVQ_OK) return st;
-    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, stream);
+    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, 1, stream);
+}
+
+kvq_status kvq_verify_workspace_bytes(const kvq_cache* cache, int32_t num_seqs, int32_t q_len,
+                                      int32_t num_q_heads, int32_t max_context_len,
+                                      int32_t partition_pages, size_t* bytes) {
+    if (!bytes) return KVQ_ERR_INVALID;
+    *bytes = 0;
+    if (!cache) return KVQ_ERR_INVALID;
+    if (num_seqs < 0 || q_len < 1 || num_q_heads <= 0 || max_context_len < 0 || partition_pages < 0)
+        return KVQ_ERR_INVALID;
+    if (cache->page_size <= 0) return KVQ_ERR_INVALID;
+    *bytes = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, q_len)
+                 .total;
+    return KVQ_OK;
+}
+
+kvq_status kvq_verify_attention(const kvq_cache* cache, const void* q, int32_t num_seqs, int32_t q_len,
+                                int32_t num_q_heads, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, float softmax_scale,
+                                int32_t partition_pages, void* workspace, size_t workspace_bytes,
+                                float* out, float* lse, hipStream_t stream) {
+    Plan pl;
+    kvq_status st = check_decode(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq,
+                                 context_lens, max_context_len, partition_pages, workspace,
+                                 workspace_bytes, out, q_len, &pl);
+    if (st != KVQ_OK || num_seqs == 0) return st;
+    st = run_split(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
+                   max_context_len, softmax_scale, pl, workspace, out, lse, q_len, stream);
+    if (st != KVQ_OK) return st;
+    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, q_len, stream);
 }
 
 kvq_status kvq_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {

@@ -31,20 +31,21 @@ struct AppendParams {
 struct SplitParams {
     const uint8_t* k_pages;
     const uint8_t* v_pages;
-    const uint16_t* q;             // bf16 [B][Hq][128]
+    const uint16_t* q;             // bf16 [B][q_len][Hq][128]
     const int32_t* block_table;    // [B][max_pages_per_seq]
     const int32_t* context_lens;   // [B]
     const uint16_t* static_scales; // see AppendParams
-    float* out;                    // fp32 [B][Hq][128]
-    float* lse;                    // fp32 [B][Hq] or null
-    float* part_o;                 // fp32 [B][Hq][max_parts][128]
-    float* part_lse;               // fp32 [B][Hq][max_parts] (log2 domain)
+    float* out;                    // fp32 [B][q_len][Hq][128]
+    float* lse;                    // fp32 [B][q_len][Hq] or null
+    float* part_o;                 // fp32 [B][n_kv][group q_len][max_parts][128]
+    float* part_lse;               // fp32 [B][n_kv][group q_len][max_parts] (log2 domain)
     int32_t* ws_header;            // [0] = range length, [1] = per-item start-up weight
     int32_t* ws_pfx;               // [B + 1] exclusive prefix of pages per sequence
     long long rec_k, rec_v;
     int num_seqs, n_q, n_kv, group, num_pages;
     int max_pages_per_seq, max_ctx, max_pages;
     int max_parts, min_chunk, forced_chunk, total_waves;
+    int q_len;                     // query positions per sequence (1: decode; >1: causal verification)
     int static_head_stride, static_kv_stride;
     float score_scale;             // softmax_scale * log2(e)
 };
@@ -57,6 +58,7 @@ struct ReduceParams {
     float* out;
     float* lse;
     int num_seqs, n_q, n_kv, group, max_parts;
+    int q_len;
 };
 
 struct KiviAppendParams {

@@ -58,13 +58,17 @@ __device__ __forceinline__ void merge_rows(const float* pl, const float* po, int
             float mx = m[r];
 #pragma unroll
             for (int u = 0; u < 8; ++u) mx = fmaxf(mx, l[r][u]);
-            const float a = __builtin_amdgcn_exp2f(m[r] - mx);    // 0 on the first group (m = -inf)
+            // every partial so far empty (lse = -inf: a causal row that saw no
+            // token): subtract 0 instead of -inf so that the weights come out
+            // 0, not NaN
+            const float ms = mx == -INFINITY ? 0.0f : mx;
+            const float a = __builtin_amdgcn_exp2f(m[r] - ms);    // 0 on the first group (m = -inf)
             s[r] *= a;
             o0[r] *= a;
             o1[r] *= a;
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const float w = __builtin_amdgcn_exp2f(l[r][u] - mx);
+                const float w = __builtin_amdgcn_exp2f(l[r][u] - ms);
                 s[r] += w;
                 o0[r] += w * v[r][u].x;
                 o1[r] += w * v[r][u].y;
@@ -74,7 +78,7 @@ __device__ __forceinline__ void merge_rows(const float* pl, const float* po, int
     }
 #pragma unroll
     for (int r = 0; r < NH; ++r) {
-        const float inv = 1.0f / s[r];
+        const float inv = s[r] > 0.0f ? 1.0f / s[r] : 0.0f;      // a row that saw no token: o = 0
         *(float2*)(out + (size_t)r * kHeadDim + 2 * lane) = make_float2(o0[r] * inv, o1[r] * inv);
         if (lse && lane == 0) lse[r] = (m[r] + __log2f(s[r])) * kLn2;
     }

@@ -160,6 +160,35 @@ def test_workspace_bytes(L):
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8192, 0, None) == INVALID
 
 
+def _verify(L, desc, num_seqs=2, q_len=4, hq=8, maxp=4, max_ctx=64, part=0, ws=FAKE, ws_bytes=1 << 30,
+            out=FAKE, q=FAKE):
+    return L.kvq_verify_attention(ctypes.byref(desc), q, num_seqs, q_len, hq, FAKE, maxp, FAKE, max_ctx, 0.088,
+                                  part, ws, ws_bytes, out, None, None)
+
+
+def test_verify_validation(L):
+    """Only error paths and empty batches: nothing here reaches a launch."""
+    d = _desc()                                                   # 2 KV heads
+    assert _verify(L, d, q_len=0) == INVALID
+    assert _verify(L, d, q_len=-1) == INVALID
+    assert _verify(L, d, q_len=5) == UNSUPPORTED                  # 5 x group 4 = 20 rows > 16
+    assert _verify(L, d, q_len=3, hq=16) == UNSUPPORTED           # 3 x 8 = 24 rows
+    assert _verify(L, d, hq=6) == UNSUPPORTED                     # group of 3
+    assert _verify(L, d, max_ctx=65) == INVALID
+    assert _verify(L, d, ws_bytes=0) == WORKSPACE
+    assert _verify(L, d, out=None) == INVALID
+    assert _verify(L, d, num_seqs=0) == OK
+    assert _verify(L, _kivi_desc(), q_len=2, hq=16, max_ctx=128) == UNSUPPORTED
+    # workspace: partial rows grow with q_len; q_len 1 is the decode workspace
+    out1, out4, dec = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.kvq_verify_workspace_bytes(ctypes.byref(d), 32, 1, 8, 8192, 0, ctypes.byref(out1)) == OK
+    assert L.kvq_verify_workspace_bytes(ctypes.byref(d), 32, 4, 8, 8192, 0, ctypes.byref(out4)) == OK
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 8, 8192, 0, ctypes.byref(dec)) == OK
+    assert out1.value == dec.value
+    assert out4.value >= 4 * 32 * 8 * 32 * 129 * 4
+    assert L.kvq_verify_workspace_bytes(ctypes.byref(d), 32, 0, 8, 8192, 0, ctypes.byref(out4)) == INVALID
+
+
 def test_encode_and_status(L):
     assert L.kvq_e4m3_encode(FAKE, FAKE, -1, None) == INVALID
     assert L.kvq_e4m3_encode(FAKE, FAKE, 0, None) == OK
