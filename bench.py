@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama8b", choices=["tiny", "llama8b", "llama70b", "mixed", "kivi"])
+    ap.add_argument("--config", default="llama8b",
+                    choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "verify"])
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto)")
     ap.add_argument("--partition-pages", type=int, default=0)
     ap.add_argument("--graph", action="store_true",
@@ -71,6 +72,7 @@ def step_bytes(w, lens: np.ndarray):
     n_kv, d, Hq = w.num_kv_heads, w.head_dim, w.num_q_heads
     tokens = int(lens.sum())
     B = len(lens)
+    QL = w.q_len                                       # query positions per sequence
     if w.dtype == "kivi4":
         rk, rv = 2048 + 4 * d, 2048 + 4 * w.page_size      # INT4 page records (codes + bf16 s, z)
         nq = kivi_quantized(w, lens)
@@ -86,9 +88,9 @@ def step_bytes(w, lens: np.ndarray):
         meta = 2 if w.dtype == "fp8" else 4            # bf16 scale (+ bf16 zero-point) per (token, head)
         pages = int(((lens + w.page_size - 1) // w.page_size).sum())
         kv = tokens * n_kv * 2 * (d + meta)
-        split = kv + pages * 4 + B * Hq * d * 2        # K/V codes+scales, block-table entries, q
-        append = B * n_kv * 2 * (d * 2 + d + meta) + B * 4
-    reduce = B * Hq * d * 4                            # out (fp32)
+        split = kv + pages * 4 + B * QL * Hq * d * 2   # K/V codes+scales, block-table entries, q
+        append = QL * (B * n_kv * 2 * (d * 2 + d + meta) + B * 4)
+    reduce = B * QL * Hq * d * 4                       # out (fp32)
     return dict(kv=kv, split=split, reduce=reduce, append=append, total=split + reduce + append,
                 tokens=tokens, pages=pages)
 
@@ -129,12 +131,18 @@ def cpu_baseline(w, budget_s: float):
         # a 16384-token prefix of each sequence keeps one pass to a few seconds
         lens = np.minimum(lens, 16384)
     dt = O.FP8 if w.dtype == "fp8" else O.INT8
-    q_all = synthetic.gen_q(w, "cpu")
+    QL = w.q_len
+    q_all = synthetic.gen_q(w, "cpu", batch=len(lens) * QL)
+    if QL > 1:
+        q_all = q_all.reshape(len(lens), QL, w.num_q_heads, w.head_dim)
     scale = 1.0 / math.sqrt(w.head_dim)
 
     def run_oracle(qb, kb, vb):
         if not kivi:
-            O.decode_reference(qb, kb, vb, dt)
+            if QL > 1:
+                O.verify_reference(qb, kb, vb, dt)
+            else:
+                O.decode_reference(qb, kb, vb, dt)
             return
         k16, v16 = O.bf16_to_f16_bits(kb), O.bf16_to_f16_bits(vb)
         T = kb.shape[0]
@@ -176,7 +184,8 @@ def cpu_baseline(w, budget_s: float):
     return {"value": round(by["kv"] / t_total / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(done)} sequence passes over the first {len(held)} of {len(lens)} sequences "
                       + ("(16384-token prefixes) " if kivi else "") +
-                      f"({int(sl.sum())} tokens): quantize-on-store of their K/V plus fp64 attention, "
+                      f"({int(sl.sum())} tokens): quantize-on-store of their K/V plus fp64 attention"
+                      + (f" of {QL} causal positions each" if QL > 1 else "") + ", "
                       f"{t_total:.1f} s; value = their K/V code+scale bytes / time",
             "tokens_per_s": round(len(done) / t_total, 4)}
 
@@ -222,8 +231,11 @@ def main():
     reps = args.replicas or (2 if by["kv"] < (1 << 30) else 1)
 
     # each cache replica holds the context minus the newest token (pages laid
-    # out for the full length); every step appends that token, then decodes
+    # out for the full length); every step appends that token, then decodes.
+    # A verification workload (q_len > 1) holds all but the q_len newest
+    # positions, appends those and scores them causally.
     kivi = w.dtype == "kivi4"
+    QL = w.q_len
     full_layout = synthetic.page_layout(w, lens)
     bt_dev = torch.from_numpy(full_layout.block_table).cuda()
     caches = []
@@ -249,7 +261,7 @@ def main():
             code = kvq.KVQ_FP8_E4M3 if w.dtype == "fp8" else kvq.KVQ_INT8_ASYM
             cache = kvq.Cache(code, full_layout.num_pages, w.num_kv_heads, w.page_size, d)
             for b, n in enumerate(lens):
-                m = int(n) - 1
+                m = int(n) - QL
                 for p0 in range(0, m, 1 << 16):
                     mm = min(1 << 16, m - p0)
                     k, v = synthetic.gen_kv(w, b, p0, mm, "cuda")
@@ -259,22 +271,42 @@ def main():
     cl_dev = torch.from_numpy(lens.astype(np.int32)).cuda()
     cl_before = torch.from_numpy((lens - 1).astype(np.int32)).cuda()
     new_offs = torch.arange(B + 1, dtype=torch.int32, device="cuda")
-    q = synthetic.gen_q(w, "cuda")
-    knew = torch.empty(B, w.num_kv_heads, d, dtype=torch.bfloat16, device="cuda")
+    if QL == 1:
+        q = synthetic.gen_q(w, "cuda")
+    else:
+        q = synthetic.gen_q(w, "cuda", batch=B * QL).reshape(B, QL, Hq, d)
+    knew = torch.empty(B * QL, w.num_kv_heads, d, dtype=torch.bfloat16, device="cuda")
     vnew = torch.empty_like(knew)
     for b in range(B):
-        kk, vv = synthetic.gen_new_kv(w, b, 1, "cuda")
-        knew[b], vnew[b] = kk[0], vv[0]
-    pos = lens - 1
-    slot = (full_layout.block_table[np.arange(B), pos // w.page_size].astype(np.int64) * w.page_size
+        kk, vv = synthetic.gen_new_kv(w, b, QL, "cuda")
+        knew[b * QL:(b + 1) * QL], vnew[b * QL:(b + 1) * QL] = kk, vv
+    pos = (lens[:, None] - QL + np.arange(QL)[None, :]).reshape(-1)
+    seq = np.repeat(np.arange(B), QL)
+    slot = (full_layout.block_table[seq, pos // w.page_size].astype(np.int64) * w.page_size
             + pos % w.page_size).astype(np.int32)
     slot_dev = torch.from_numpy(slot).cuda()
     max_ctx = int(lens.max())
-    ws_bytes = kvq.decode_workspace_bytes(caches[0], B, Hq, max_ctx, args.partition_pages)
+    if QL == 1:
+        ws_bytes = kvq.decode_workspace_bytes(caches[0], B, Hq, max_ctx, args.partition_pages)
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
+    else:
+        ws_bytes = kvq.verify_workspace_bytes(caches[0], B, QL, Hq, max_ctx, args.partition_pages)
+        out = torch.empty(B, QL, Hq, d, dtype=torch.float32, device="cuda")
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    out = torch.empty(B, Hq, d, dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(d)
     torch.cuda.synchronize()
+
+    def split(c):
+        if QL == 1:
+            kvq.decode_split(c, q, bt_dev, cl_dev, max_ctx, scale, ws, out, None, args.partition_pages)
+        else:
+            kvq.verify_split(c, q, bt_dev, cl_dev, max_ctx, scale, ws, out, None, args.partition_pages)
+
+    def reduce(c):
+        if QL == 1:
+            kvq.decode_reduce(c, B, Hq, max_ctx, ws, out, None, args.partition_pages)
+        else:
+            kvq.verify_reduce(c, B, QL, Hq, max_ctx, ws, out, None, args.partition_pages)
 
     def step(i, ev=None):
         c = caches[i % reps]
@@ -286,10 +318,10 @@ def main():
             kvq.append(c, knew, vnew, slot_dev)
         if ev is not None:
             ev[1].record()
-        kvq.decode_split(c, q, bt_dev, cl_dev, max_ctx, scale, ws, out, None, args.partition_pages)
+        split(c)
         if ev is not None:
             ev[2].record()
-        kvq.decode_reduce(c, B, Hq, max_ctx, ws, out, None, args.partition_pages)
+        reduce(c)
         if ev is not None:
             ev[3].record()
 
@@ -324,10 +356,8 @@ def main():
         else:
             kvq.append(caches[i % reps], knew, vnew, slot_dev)
     mean_app = back_to_back(app)
-    mean_split = back_to_back(lambda i: kvq.decode_split(caches[i % reps], q, bt_dev, cl_dev, max_ctx, scale, ws,
-                                                          out, None, args.partition_pages))
-    mean_red = back_to_back(lambda i: kvq.decode_reduce(caches[i % reps], B, Hq, max_ctx, ws, out, None,
-                                                         args.partition_pages))
+    mean_split = back_to_back(lambda i: split(caches[i % reps]))
+    mean_red = back_to_back(lambda i: reduce(caches[i % reps]))
 
     # whole-step time: the same steps as eager launches on the stream, or with
     # --graph as replays of one HIP graph per cache replica
@@ -371,9 +401,9 @@ def main():
         "config": {"workload": w.name, "description": w.description, "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": w.num_kv_heads, "head_dim": d, "page_size": w.page_size,
                    "context_tokens": by["tokens"], "max_context": max_ctx, "cache_replicas": reps,
-                   "partition_pages": args.partition_pages or "auto",
+                   "partition_pages": args.partition_pages or "auto", "positions_per_seq": QL,
                    "step_launch": "hip_graph" if args.graph else "eager"},
-        "tokens_per_s": round(B / (ms_step * 1e-3), 1),
+        "tokens_per_s": round(B * QL / (ms_step * 1e-3), 1),
         "decode_attention_kv_gbs": round(kv_gbs, 2),
         "pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         # means: back-to-back launches; p50 / p95: single launches between events

@@ -225,6 +225,18 @@ kvq_status kvq_verify_attention(const kvq_cache* cache, const void* q, int32_t n
                                 int32_t max_context_len, float softmax_scale,
                                 int32_t partition_pages, void* workspace, size_t workspace_bytes,
                                 float* out, float* lse, hipStream_t stream);
+/* The two launches of kvq_verify_attention (split over the context, then the
+ * log-sum-exp merge), as kvq_decode_split / kvq_decode_reduce are for
+ * kvq_decode_attention: call them in this order on one stream with identical
+ * arguments. */
+kvq_status kvq_verify_split(const kvq_cache* cache, const void* q, int32_t num_seqs, int32_t q_len,
+                            int32_t num_q_heads, const int32_t* block_table, int32_t max_pages_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
+                            int32_t partition_pages, void* workspace, size_t workspace_bytes, float* out,
+                            float* lse, hipStream_t stream);
+kvq_status kvq_verify_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                             int32_t max_context_len, int32_t partition_pages, void* workspace,
+                             size_t workspace_bytes, float* out, float* lse, hipStream_t stream);
 
 /* The FP8 E4M3 encoder of kvq_append applied to n float32 values (nearest-even,
  * saturating at +-448, sign of zero kept, NaN -> 0x7F).  x: device fp32 [n],

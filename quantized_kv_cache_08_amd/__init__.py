@@ -18,7 +18,7 @@ __all__ = [
     "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI",
     "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
     "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
-    "verify_workspace_bytes", "verify_attention",
+    "verify_workspace_bytes", "verify_attention", "verify_split", "verify_reduce",
     "decode_attention", "decode_split", "decode_reduce", "e4m3_encode", "status_string",
     "LIB_PATH",
 ]
@@ -79,8 +79,12 @@ def lib() -> ctypes.CDLL:
         L.kvq_verify_workspace_bytes.restype = ctypes.c_int
         L.kvq_verify_workspace_bytes.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32, _I32,
                                                  ctypes.POINTER(ctypes.c_size_t)]
-        L.kvq_verify_attention.restype = ctypes.c_int
-        L.kvq_verify_attention.argtypes = [ctypes.POINTER(CacheDesc), _P, _I32, _I32] + _DECODE_ARGS[3:]
+        for fn in ("kvq_verify_attention", "kvq_verify_split"):
+            getattr(L, fn).restype = ctypes.c_int
+            getattr(L, fn).argtypes = [ctypes.POINTER(CacheDesc), _P, _I32, _I32] + _DECODE_ARGS[3:]
+        L.kvq_verify_reduce.restype = ctypes.c_int
+        L.kvq_verify_reduce.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32, _I32, _P,
+                                        ctypes.c_size_t, _P, _P, _P]
         L.kvq_e4m3_encode.restype = ctypes.c_int
         L.kvq_e4m3_encode.argtypes = [_P, _P, ctypes.c_int64, _P]
         L.kvq_status_string.restype = ctypes.c_char_p
@@ -217,16 +221,36 @@ def verify_workspace_bytes(cache: Cache, num_seqs: int, q_len: int, num_q_heads:
     return int(out.value)
 
 
-def verify_attention(cache: Cache, q, block_table, context_lens, max_context_len: int, softmax_scale: float,
-                     workspace, out, lse=None, partition_pages: int = 0, stream=None) -> None:
-    """Causal attention of the q_len newest positions per sequence (kvq_verify_attention);
-    q [B][q_len][Hq][d] bf16, out [B][q_len][Hq][d] fp32."""
+def _verify(fn: str, cache, q, block_table, context_lens, max_context_len, softmax_scale, workspace, out,
+            lse, partition_pages, stream):
     num_seqs, q_len, num_q_heads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
-    _check("kvq_verify_attention", lib().kvq_verify_attention(
+    _check(fn, getattr(lib(), fn)(
         ctypes.byref(cache.desc), _ptr(q), num_seqs, q_len, num_q_heads, _ptr(block_table),
         int(block_table.shape[1]), _ptr(context_lens), int(max_context_len), float(softmax_scale),
         int(partition_pages), _ptr(workspace), int(workspace.numel() * workspace.element_size()),
         _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def verify_attention(cache: Cache, q, block_table, context_lens, max_context_len: int, softmax_scale: float,
+                     workspace, out, lse=None, partition_pages: int = 0, stream=None) -> None:
+    """Causal attention of the q_len newest positions per sequence (kvq_verify_attention);
+    q [B][q_len][Hq][d] bf16, out [B][q_len][Hq][d] fp32."""
+    _verify("kvq_verify_attention", cache, q, block_table, context_lens, max_context_len, softmax_scale,
+            workspace, out, lse, partition_pages, stream)
+
+
+def verify_split(cache: Cache, q, block_table, context_lens, max_context_len: int, softmax_scale: float,
+                 workspace, out, lse=None, partition_pages: int = 0, stream=None) -> None:
+    _verify("kvq_verify_split", cache, q, block_table, context_lens, max_context_len, softmax_scale,
+            workspace, out, lse, partition_pages, stream)
+
+
+def verify_reduce(cache: Cache, num_seqs: int, q_len: int, num_q_heads: int, max_context_len: int, workspace,
+                  out, lse=None, partition_pages: int = 0, stream=None) -> None:
+    _check("kvq_verify_reduce", lib().kvq_verify_reduce(
+        ctypes.byref(cache.desc), num_seqs, q_len, num_q_heads, int(max_context_len), int(partition_pages),
+        _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse),
+        _stream(stream)))
 
 
 def e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:

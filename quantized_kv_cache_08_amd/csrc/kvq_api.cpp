@@ -380,6 +380,36 @@ kvq_status kvq_verify_workspace_bytes(const kvq_cache* cache, int32_t num_seqs, 
     return KVQ_OK;
 }
 
+kvq_status kvq_verify_split(const kvq_cache* cache, const void* q, int32_t num_seqs, int32_t q_len,
+                            int32_t num_q_heads, const int32_t* block_table, int32_t max_pages_per_seq,
+                            const int32_t* context_lens, int32_t max_context_len, float softmax_scale,
+                            int32_t partition_pages, void* workspace, size_t workspace_bytes, float* out,
+                            float* lse, hipStream_t stream) {
+    Plan pl;
+    kvq_status st = check_decode(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq,
+                                 context_lens, max_context_len, partition_pages, workspace,
+                                 workspace_bytes, out, q_len, &pl);
+    if (st != KVQ_OK || num_seqs == 0) return st;
+    return run_split(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
+                     max_context_len, softmax_scale, pl, workspace, out, lse, q_len, stream);
+}
+
+kvq_status kvq_verify_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                             int32_t max_context_len, int32_t partition_pages, void* workspace,
+                             size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
+    if (!cache) return KVQ_ERR_INVALID;
+    if (num_seqs < 0 || q_len < 1 || num_q_heads <= 0 || max_context_len < 0 || partition_pages < 0)
+        return KVQ_ERR_INVALID;
+    if (cache->num_kv_heads <= 0 || cache->page_size <= 0 || num_q_heads % cache->num_kv_heads)
+        return KVQ_ERR_INVALID;
+    if ((long long)q_len * (num_q_heads / cache->num_kv_heads) > 16) return KVQ_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return KVQ_OK;
+    if (!workspace || !out) return KVQ_ERR_INVALID;
+    Plan pl = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, q_len);
+    if (workspace_bytes < pl.total) return KVQ_ERR_WORKSPACE;
+    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, q_len, stream);
+}
+
 kvq_status kvq_verify_attention(const kvq_cache* cache, const void* q, int32_t num_seqs, int32_t q_len,
                                 int32_t num_q_heads, const int32_t* block_table,
                                 int32_t max_pages_per_seq, const int32_t* context_lens,

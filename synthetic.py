@@ -140,6 +140,7 @@ class Workload:
     len_sigma: float = 0.7
     spare_frac: float = 0.05
     resid: int = 128          # KIVI fp16 recent window
+    q_len: int = 1            # query positions per sequence (> 1: speculative-decoding verification)
     group: int = 32           # KIVI group along tokens
     description: str = ""
 
@@ -162,6 +163,10 @@ WORKLOADS = {
     "mixed": Workload("mixed", "fp8", 256, 32, 8, 128, 16, 32768, seed=4, mixed=True,
                       description="Mixed chat batch: 256 sequences, lognormal lengths (median 1500, sigma 0.7, "
                                   "cap 32768), 32 q / 8 kv heads, d128, shuffled shared page pool, FP8 E4M3"),
+    "verify": Workload("verify", "fp8", 32, 32, 8, 128, 16, 8192, seed=2, q_len=4,
+                       description="Verification pass of speculative decoding on the Llama-3-8B-shaped layer: "
+                                   "batch 32, context 8192 (including 4 new positions), 4 positions per sequence "
+                                   "scored causally, 32 q / 8 kv heads, d128, page 16, FP8 E4M3"),
     "kivi": Workload("kivi", "kivi4", 4, 64, 8, 128, 32, 131072, seed=5,
                      description="KIVI-style 4-bit: 64 q / 8 kv heads, d128, batch 4, context 131072; K per-channel "
                                  "INT4 in 32-token groups, V per-token INT4, last 128 tokens fp16"),

@@ -135,3 +135,22 @@ def test_verify_llama8b_shape_sampled():
     out, lse = run_verify(bt, q, 0)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
     check(bt, 4, out, lse, seqs=[0, w.batch - 1])
+
+
+def test_verify_split_then_reduce_equals_attention():
+    w = workload("tiny", num_q_heads=8, num_kv_heads=2, batch=len(LENS), context=int(LENS.max()))
+    say("verify split + reduce vs attention")
+    bt = H.build(w, lens=LENS)
+    B, q_len, Hq, d = len(LENS), 4, 8, 128
+    q = verify_q(w, B, q_len, "cuda")
+    for part in (0, 1):
+        out_a, lse_a = run_verify(bt, q, part)
+        ws = torch.zeros(kvq.verify_workspace_bytes(bt.cache, B, q_len, Hq, bt.max_ctx, part), dtype=torch.uint8,
+                         device="cuda")
+        out = torch.full((B, q_len, Hq, d), float("nan"), device="cuda")
+        lse = torch.full((B, q_len, Hq), float("nan"), device="cuda")
+        kvq.verify_split(bt.cache, q, bt.block_table, bt.context_lens, bt.max_ctx, 1.0 / math.sqrt(d), ws, out, lse,
+                         part)
+        kvq.verify_reduce(bt.cache, B, q_len, Hq, bt.max_ctx, ws, out, lse, part)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), out_a) and np.array_equal(lse.cpu().numpy(), lse_a)
