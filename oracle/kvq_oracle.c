@@ -146,6 +146,51 @@ void kvqo_e4m3_encode_array(const float* y, int64_t n, uint8_t* codes)
 }
 
 /* ======================================================================= *
+ * OCP FP8 E5M2: 5 exponent bits (bias 15), 2 mantissa bits, with IEEE-style *
+ * specials: exponent 31 holds +-inf (mantissa 0) and NaN (mantissa != 0).  *
+ * Largest finite 57344 = 0x7B; subnormals m * 2^-16.  The pages name E5M2  *
+ * as the wider-range, lower-precision FP8 format and list it among the KV  *
+ * cache dtypes ([molayo] formats notes and the serving-flag values;        *
+ * [ryotta] §3.1).                                                          *
+ * ======================================================================= */
+double kvqo_e5m2_value(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 2) & 31, m = c & 3;
+    double v;
+    if (e == 31) v = (m == 0) ? INFINITY : NAN;
+    else if (e == 0) v = ldexp((double)m, -16);               /* m * 2^-16          */
+    else v = ldexp((double)(4 + m), e - 17);                  /* (1+m/4) 2^(e-15)   */
+    return s ? -v : v;
+}
+
+/* Round to the nearest E5M2 value, ties to the even mantissa, saturating at
+ * +-57344 (the same rule as E4M3: no infinities are produced); NaN -> 0x7F;
+ * the sign of zero is kept. */
+uint8_t kvqo_e5m2_encode(float y)
+{
+    if (isnan(y)) return 0x7F;
+    uint8_t sg = signbit(y) ? 0x80 : 0x00;
+    double a = fabs((double)y);
+    if (a >= 57344.0) return sg | 0x7B;
+    if (a < ldexp(1.0, -14)) {                          /* subnormal binade    */
+        double m = nearbyint(a * ldexp(1.0, 16));       /* 0 .. 4; 4 = 2^-14   */
+        return sg | (uint8_t)m;
+    }
+    int ex;
+    frexp(a, &ex);
+    int e = ex - 1;                                     /* -14 .. 15           */
+    double m = nearbyint((ldexp(a, -e) - 1.0) * 4.0);   /* 0 .. 4              */
+    if (m == 4.0) { e += 1; m = 0.0; }
+    return sg | (uint8_t)(((e + 15) << 2) | (int)m);
+}
+
+void kvqo_e5m2_encode_array(const float* y, int64_t n, uint8_t* codes)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) codes[i] = kvqo_e5m2_encode(y[i]);
+}
+
+/* ======================================================================= *
  * Quantizers.  Quantization happens once, when a token's K/V row is stored, *
  * from the full-precision values, with a per-(token, head) scale kept in     *
  * BF16 next to the codes ([molayo] "what it is"; [ryotta] §5.1 and §6.3).    *
@@ -173,6 +218,30 @@ void kvqo_fp8_row_static(const uint16_t* x, int n, uint16_t scale, uint8_t* code
     float sf = kvqo_bf16_value(scale);
     for (int i = 0; i < n; ++i)
         codes[i] = (sf == 0.0f) ? 0x00 : kvqo_e4m3_encode(kvqo_bf16_value(x[i]) / sf);
+}
+
+/* The same two FP8 quantizers with the E5M2 code: the per-(token, head) scale
+ * maps the row's largest magnitude onto 57344. */
+void kvqo_e5m2_row(const uint16_t* x, int n, uint8_t* codes, uint16_t* scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float a = fabsf(kvqo_bf16_value(x[i]));
+        if (a > amax) amax = a;
+    }
+    float s32 = amax / 57344.0f;                         /* one IEEE division   */
+    uint16_t s = kvqo_bf16_up(s32);
+    float sf = kvqo_bf16_value(s);
+    *scale = s;
+    for (int i = 0; i < n; ++i)
+        codes[i] = (sf == 0.0f) ? 0x00 : kvqo_e5m2_encode(kvqo_bf16_value(x[i]) / sf);
+}
+
+void kvqo_e5m2_row_static(const uint16_t* x, int n, uint16_t scale, uint8_t* codes)
+{
+    float sf = kvqo_bf16_value(scale);
+    for (int i = 0; i < n; ++i)
+        codes[i] = (sf == 0.0f) ? 0x00 : kvqo_e5m2_encode(kvqo_bf16_value(x[i]) / sf);
 }
 
 /* Asymmetric unsigned quantizer with `levels` steps ([molayo] formats notes:
@@ -225,6 +294,8 @@ void kvqo_quantize_rows(int dtype, int mode, const uint16_t* x, int64_t rows, in
         uint8_t* cr = codes + r * n;
         if (dtype == 1 && mode == 2) kvqo_fp8_row(xr, n, cr, &scale[r]);
         else if (dtype == 1) { kvqo_fp8_row_static(xr, n, static_scale[r], cr); if (scale) scale[r] = static_scale[r]; }
+        else if (dtype == 4 && mode == 2) kvqo_e5m2_row(xr, n, cr, &scale[r]);
+        else if (dtype == 4) { kvqo_e5m2_row_static(xr, n, static_scale[r], cr); if (scale) scale[r] = static_scale[r]; }
         else kvqo_int8_row(xr, n, cr, &scale[r], &zero[r]);
     }
 }
@@ -239,7 +310,9 @@ void kvqo_dequantize_rows(int dtype, int mode, const uint8_t* codes, int64_t row
         double z = (dtype == 2) ? (double)kvqo_bf16_value(zero[r]) : 0.0;
         for (int i = 0; i < n; ++i) {
             uint8_t c = codes[r * n + i];
-            out[r * n + i] = (dtype == 1) ? s * kvqo_e4m3_value(c) : (double)c * s + z;
+            out[r * n + i] = (dtype == 1) ? s * kvqo_e4m3_value(c)
+                           : (dtype == 4) ? s * kvqo_e5m2_value(c)
+                                          : (double)c * s + z;
         }
     }
 }

@@ -38,6 +38,9 @@ double   kvqo_e4m3_value(uint8_t code);      /* OCP E4M3 (FN): NaN for 0x7F/0xFF
 uint8_t  kvqo_e4m3_encode(float y);          /* nearest-even, saturating at +-448 */
 void     kvqo_e4m3_encode_range(uint32_t first_bits, uint32_t count, uint8_t* codes);
 void     kvqo_e4m3_encode_array(const float* y, int64_t n, uint8_t* codes);
+double   kvqo_e5m2_value(uint8_t code);      /* OCP E5M2: +-inf at 0x7C/0xFC, NaN for 0x7D-0x7F/0xFD-0xFF */
+uint8_t  kvqo_e5m2_encode(float y);          /* nearest-even, saturating at +-57344 */
+void     kvqo_e5m2_encode_array(const float* y, int64_t n, uint8_t* codes);
 
 /* ---- quantizers: one row of n values ------------------------------------ */
 void kvqo_fp8_row(const uint16_t* x_bf16, int n, uint8_t* codes, uint16_t* scale);
@@ -48,7 +51,7 @@ void kvqo_uint_asym(const float* x, int n, int stride, int levels,
                     uint8_t* codes, int code_stride, uint16_t* scale, uint16_t* zero);
 
 /* ---- bulk helpers (OpenMP over rows) ------------------------------------ */
-/* dtype 1 = FP8 E4M3, 2 = INT8 asymmetric.  mode 2 = per-(token,head) scale;
+/* dtype 1 = FP8 E4M3, 2 = INT8 asymmetric, 4 = FP8 E5M2.  mode 2 = per-(token,head) scale;
  * mode 0/1 = static scale given per row in static_scale[row].                */
 void kvqo_quantize_rows(int dtype, int mode, const uint16_t* x_bf16, int64_t rows, int n,
                         const uint16_t* static_scale, uint8_t* codes, uint16_t* scale,

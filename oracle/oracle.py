@@ -23,7 +23,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvq_oracle.so")
 
-FP8, INT8 = 1, 2
+FP8, INT8, E5M2 = 1, 2, 4       # dtype codes (FP8 = E4M3)
 PER_TENSOR, PER_HEAD, PER_TOKEN_HEAD = 0, 1, 2
 
 _lib = None
@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
         L.kvqo_e4m3_encode.argtypes = [ctypes.c_float]
         L.kvqo_e4m3_encode_range.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _P]
         L.kvqo_e4m3_encode_array.argtypes = [_P, ctypes.c_int64, _P]
+        L.kvqo_e5m2_value.restype = ctypes.c_double
+        L.kvqo_e5m2_value.argtypes = [ctypes.c_uint8]
+        L.kvqo_e5m2_encode.restype = ctypes.c_uint8
+        L.kvqo_e5m2_encode.argtypes = [ctypes.c_float]
+        L.kvqo_e5m2_encode_array.argtypes = [_P, ctypes.c_int64, _P]
         L.kvqo_fp8_row.argtypes = [_P, ctypes.c_int, _P, _P]
         L.kvqo_fp8_row_static.argtypes = [_P, ctypes.c_int, ctypes.c_uint16, _P]
         L.kvqo_int8_row.argtypes = [_P, ctypes.c_int, _P, _P, _P]
@@ -98,6 +103,19 @@ def e4m3_encode(y) -> np.ndarray:
     y = _c(y, np.float32)
     out = np.empty(y.shape, dtype=np.uint8)
     lib().kvqo_e4m3_encode_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def e5m2_table() -> np.ndarray:
+    """fp64 value of each of the 256 E5M2 codes (+-inf at 0x7C / 0xFC, NaN for 0x7D-0x7F / 0xFD-0xFF)."""
+    L = lib()
+    return np.array([L.kvqo_e5m2_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e5m2_encode(y) -> np.ndarray:
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib().kvqo_e5m2_encode_array(_ptr(y), y.size, _ptr(out))
     return out
 
 

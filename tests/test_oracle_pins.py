@@ -472,3 +472,85 @@ def test_verify_reference_special_cases(oracle):
     r = oracle.verify_reference(qb, kb[:2], vb[:2], oracle.FP8)
     assert not r["out"][:2].any() and np.all(np.isneginf(r["lse"][:2]))
     assert np.all(np.isfinite(r["lse"][2:]))
+
+
+# ----------------------------------------------------------------- E5M2
+def test_e5m2_decode_matches_torch(oracle):
+    tab = oracle.e5m2_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e5m2).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(tab), nan)
+    assert np.array_equal(tab[~nan], ref[~nan])
+    # landmarks: largest finite 57344 (0x7B), +inf 0x7C, smallest normal 2^-14, smallest subnormal 2^-16
+    assert tab[0x7B] == 57344.0 and np.isposinf(tab[0x7C]) and np.isneginf(tab[0xFC])
+    assert tab[0x04] == 2.0**-14 and tab[0x01] == 2.0**-16 and tab[0x80] == 0.0 and np.signbit(tab[0x80])
+    assert set(np.flatnonzero(nan)) == {0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF}
+
+
+def test_e5m2_encode_matches_torch_below_saturation(oracle):
+    """torch's float8_e5m2 cast rounds to nearest-even; below 57344 it never
+    overflows, so there the two must agree on every input (a float32 sweep of
+    stride 2^9 in the bit pattern over [2^-20, 57344), both signs)."""
+    lo = int(np.array([2.0**-20], np.float32).view(np.uint32)[0])
+    hi = int(np.array([57344.0], np.float32).view(np.uint32)[0])
+    bits = np.arange(lo, hi, 1 << 9, dtype=np.uint32)
+    for sign in (0, 0x80000000):
+        y = (bits | np.uint32(sign)).view(np.float32)
+        got = oracle.e5m2_encode(y)
+        ref = torch.from_numpy(y.copy()).to(torch.float8_e5m2).view(torch.uint8).numpy()
+        assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:5]
+
+
+def test_e5m2_encode_brute_force_ties_and_saturation(oracle):
+    tab = oracle.e5m2_table()
+    finite = np.flatnonzero(np.isfinite(tab) & (np.arange(256) < 0x80))   # non-negative finite codes
+    vals = tab[finite]
+    order = np.argsort(vals, kind="stable")
+    fv, fc = vals[order], finite[order]
+    fv, keep = np.unique(fv, return_index=True)
+    fc = fc[keep]
+    mids = (fv[:-1] + fv[1:]) / 2
+    probes = np.concatenate([fv, mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                             np.nextafter(mids.astype(np.float32), np.float32(0))]).astype(np.float32)
+    probes = probes[probes < 57344.0]
+    got = oracle.e5m2_encode(probes)
+    for y, c in zip(probes.astype(np.float64), got):
+        d = np.abs(fv - y)
+        best = np.flatnonzero(d == d.min())
+        if len(best) == 1:
+            assert c == fc[best[0]], (y, c)
+        else:                                              # a tie: the even mantissa wins
+            cand = fc[best]
+            assert c in cand and (c & 1) == 0, (y, c, cand)
+    # every finite code round-trips; saturation and specials
+    for c in range(256):
+        if np.isfinite(tab[c]):
+            assert oracle.e5m2_encode(np.array([tab[c]], np.float32))[0] == (0x80 if c == 0x80 else c)
+    sat = oracle.e5m2_encode(np.array([57344.0, 61440.0, 1e9, np.inf, -1e30, -np.inf, np.nan], np.float32))
+    assert list(sat[:6]) == [0x7B, 0x7B, 0x7B, 0x7B, 0xFB, 0xFB] and sat[6] == 0x7F
+
+
+def test_e5m2_quantizer_bounds(oracle):
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal((1500, 128)).astype(np.float32)
+    x[:, [3, 50]] *= 20.0
+    xb = _bf16(x)
+    codes, s, z = oracle.quantize_rows(oracle.E5M2, oracle.PER_TOKEN_HEAD, xb)
+    assert z is None
+    xv = oracle.bf16_value(xb).astype(np.float64)
+    sv = oracle.bf16_value(s).astype(np.float64)[:, None]
+    xh = oracle.dequantize_rows(oracle.E5M2, codes, s)
+    assert np.all(np.abs(xv) / sv <= 57344.0)              # per-row scale: nothing saturates
+    # two mantissa bits: relative error <= 2^-3 for normals, absolute <= 2^-17 s in the subnormal range
+    assert np.all(np.abs(xv - xh) <= np.maximum(2.0**-3 * np.abs(xv), 2.0**-17 * sv))
+    amax = np.abs(xv).max(axis=1, keepdims=True)
+    assert np.all(sv >= amax / 57344.0) and np.all(sv <= amax / 57344.0 * (1 + 2.0**-7))
+    # E4M3 keeps one more mantissa bit: smaller error on the same rows
+    c4, s4, _ = oracle.quantize_rows(oracle.FP8, oracle.PER_TOKEN_HEAD, xb)
+    e4 = np.abs(xv - oracle.dequantize_rows(oracle.FP8, c4, s4)).mean()
+    assert e4 < np.abs(xv - xh).mean()
+    # static scale: elements beyond 57344 s saturate to the largest code
+    cs, _, _ = oracle.quantize_rows(oracle.E5M2, oracle.PER_HEAD, _bf16(np.array([[1e4, -3e5, 0.5]], np.float32)),
+                                    static_scale=_bf16(np.array([1.0], np.float32))[0])
+    assert list(cs[0]) == [oracle.e5m2_encode(np.array([1e4], np.float32))[0], 0xFB,
+                           oracle.e5m2_encode(np.array([0.5], np.float32))[0]]
