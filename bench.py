@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama8b",
-                    choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "verify"])
+                    choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "verify", "e5m2", "static"])
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto)")
     ap.add_argument("--partition-pages", type=int, default=0)
     ap.add_argument("--graph", action="store_true",
@@ -85,7 +85,8 @@ def step_bytes(w, lens: np.ndarray):
         flushes = int((kivi_quantized(w, lens) > kivi_quantized(w, lens - 1)).sum())
         append = B * n_kv * d * 2 * 2 * 2 + flushes * n_kv * (32 * d * 2 * 2 + rk + rv) + B * 8
     else:
-        meta = 2 if w.dtype == "fp8" else 4            # bf16 scale (+ bf16 zero-point) per (token, head)
+        # bf16 scale (+ bf16 zero-point) per (token, head); none with static scales
+        meta = 0 if w.scale_mode != 2 else (4 if w.dtype == "int8" else 2)
         pages = int(((lens + w.page_size - 1) // w.page_size).sum())
         kv = tokens * n_kv * 2 * (d + meta)
         split = kv + pages * 4 + B * QL * Hq * d * 2   # K/V codes+scales, block-table entries, q
@@ -130,8 +131,12 @@ def cpu_baseline(w, budget_s: float):
     if kivi:
         # a 16384-token prefix of each sequence keeps one pass to a few seconds
         lens = np.minimum(lens, 16384)
-    dt = O.FP8 if w.dtype == "fp8" else O.INT8
+    dt = {"fp8": O.FP8, "e5m2": O.E5M2, "int8": O.INT8, "kivi4": None}[w.dtype]
     QL = w.q_len
+    static_kv = None
+    if w.scale_mode != 2:
+        ss = synthetic.static_scales(w).view(torch.int16).numpy().view(np.uint16)
+        static_kv = (ss[0], ss[1])
     q_all = synthetic.gen_q(w, "cpu", batch=len(lens) * QL)
     if QL > 1:
         q_all = q_all.reshape(len(lens), QL, w.num_q_heads, w.head_dim)
@@ -140,9 +145,9 @@ def cpu_baseline(w, budget_s: float):
     def run_oracle(qb, kb, vb):
         if not kivi:
             if QL > 1:
-                O.verify_reference(qb, kb, vb, dt)
+                O.verify_reference(qb, kb, vb, dt, w.scale_mode, static_kv)
             else:
-                O.decode_reference(qb, kb, vb, dt)
+                O.decode_reference(qb, kb, vb, dt, w.scale_mode, static_kv)
             return
         k16, v16 = O.bf16_to_f16_bits(kb), O.bf16_to_f16_bits(vb)
         T = kb.shape[0]
@@ -258,8 +263,9 @@ def main():
                                 torch.from_numpy(held.astype(np.int32)).cuda(), bt_dev, int(step_n.max()))
                 held += step_n
         else:
-            code = kvq.KVQ_FP8_E4M3 if w.dtype == "fp8" else kvq.KVQ_INT8_ASYM
-            cache = kvq.Cache(code, full_layout.num_pages, w.num_kv_heads, w.page_size, d)
+            code = {"fp8": kvq.KVQ_FP8_E4M3, "e5m2": kvq.KVQ_FP8_E5M2, "int8": kvq.KVQ_INT8_ASYM}[w.dtype]
+            ss = synthetic.static_scales(w).cuda() if w.scale_mode != 2 else None
+            cache = kvq.Cache(code, full_layout.num_pages, w.num_kv_heads, w.page_size, d, w.scale_mode, ss)
             for b, n in enumerate(lens):
                 m = int(n) - QL
                 for p0 in range(0, m, 1 << 16):
@@ -396,12 +402,13 @@ def main():
         "metric": "paged FP8/INT8 decode-attn KV GB/s (% of HBM peak) + tokens/s at 1 GPU",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "int8": "u8", "kivi4": "u4"}[w.dtype],
+        "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "e5m2": "fp8_e5m2", "int8": "u8", "kivi4": "u4"}[w.dtype],
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": w.num_kv_heads, "head_dim": d, "page_size": w.page_size,
                    "context_tokens": by["tokens"], "max_context": max_ctx, "cache_replicas": reps,
                    "partition_pages": args.partition_pages or "auto", "positions_per_seq": QL,
+                   "scale_mode": {2: "per_token_head", 1: "static_per_head", 0: "static_per_tensor"}[w.scale_mode],
                    "step_launch": "hip_graph" if args.graph else "eager"},
         "tokens_per_s": round(B * QL / (ms_step * 1e-3), 1),
         "decode_attention_kv_gbs": round(kv_gbs, 2),

@@ -19,9 +19,10 @@
  *    in high precision ("KV 캐시 양자화(KV cache quantization): FP8/INT8 K 및 V가
  *    실제로 제공하는 이점과 한계점", molayo1419.me, section "KV 캐시 양자화란
  *    실제로 무엇인가"; "KV Cache 압축", ryotta.opik.net, sections 5.1 and 6.3).
- *  - Formats: FP8 E4M3 and INT8 per-token asymmetric with a (scale,
- *    zero_point) pair; per-tensor and per-head static scales (molayo1419.me,
- *    formats table notes; ryotta.opik.net section 3.1).  KIVI: K quantized per
+ *  - Formats: FP8 E4M3 (and E5M2, the wider-range, lower-precision FP8) and
+ *    INT8 per-token asymmetric with a (scale, zero_point) pair; per-tensor and
+ *    per-head static scales (molayo1419.me, formats table notes and the
+ *    serving-flag values; ryotta.opik.net section 3.1).  KIVI: K quantized per
  *    channel, V per token, the most recent tokens kept in full precision
  *    (ryotta.opik.net section 3.1, KIVI; molayo1419.me formats notes on mixed
  *    4-bit).
@@ -33,12 +34,14 @@
  * Numeric definitions (the pages give no formula; these readings are fixed):
  *  FP8 per-(token,head):  s = bf16_ceil(amax / 448), code = e4m3_rne_sat(x / s)
  *  FP8 static:            code = e4m3_rne_sat(x / s_static)
+ *  E5M2:                  the same two rules with 57344 and e5m2_rne_sat
  *  INT8 per-(token,head): z = bf16_floor(min), s = bf16_ceil((max - z) / 255),
  *                         code = clamp(rne((x - z) / s), 0, 255), x^ = code*s + z
  *  KIVI INT4:             the same asymmetric rule with 15 steps; K over the 32
  *                         tokens of a group per channel, V over the channels of
  *                         a token.  s == 0 (constant row) gives all-zero codes.
- *  Every "/" is one IEEE float32 division; E4M3 is the OCP encoding (max 448).
+ *  Every "/" is one IEEE float32 division; E4M3 is the OCP encoding (max 448),
+ *  E5M2 the OCP encoding (max 57344; saturating, so no infinities are stored).
  *
  * Page records.  A pool holds num_pages x num_kv_heads records; record
  * (page p, head h) starts at byte (p * num_kv_heads + h) * kvq_record_bytes().
@@ -79,7 +82,8 @@ typedef enum kvq_status {
 typedef enum kvq_dtype {
     KVQ_FP8_E4M3 = 1,         /* OCP E4M3, 1 byte per element                            */
     KVQ_INT8_ASYM = 2,        /* u8 code with per-(token,head) scale and zero-point      */
-    KVQ_INT4_KIVI = 3         /* 4-bit codes, K per channel / V per token, fp16 window   */
+    KVQ_INT4_KIVI = 3,        /* 4-bit codes, K per channel / V per token, fp16 window   */
+    KVQ_FP8_E5M2 = 4          /* OCP E5M2, 1 byte per element; records as KVQ_FP8_E4M3  */
 } kvq_dtype;
 
 typedef enum kvq_scale_mode {
@@ -114,7 +118,7 @@ typedef struct kvq_cache {
 size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size,
                         int32_t head_dim, int32_t which);
 
-/* Quantize-on-append (FP8 / INT8; a KVQ_INT4_KIVI cache returns
+/* Quantize-on-append (FP8 E4M3 / E5M2, INT8; a KVQ_INT4_KIVI cache returns
  * KVQ_ERR_UNSUPPORTED, it has kvq_kivi_append).
  * k, v:          device bf16 [num_tokens][num_kv_heads][head_dim], contiguous.
  * slot_mapping:  device int32 [num_tokens]; slot = page*page_size + row; a
@@ -242,6 +246,14 @@ kvq_status kvq_verify_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t q
  * saturating at +-448, sign of zero kept, NaN -> 0x7F).  x: device fp32 [n],
  * codes: device u8 [n]. */
 kvq_status kvq_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
+
+/* The E5M2 encoder of kvq_append (KVQ_FP8_E5M2 caches) applied to n float32
+ * values: nearest-even, saturating at +-57344 (no infinities), sign of zero
+ * kept, NaN -> 0x7F.  OCP E5M2 is the wider-range, lower-precision FP8 format
+ * ("KV 캐시 양자화(KV cache quantization) ...", molayo1419.me, formats notes
+ * and the serving-flag values; "KV Cache 압축", ryotta.opik.net, section 3.1).
+ * x: device fp32 [n], codes: device u8 [n]. */
+kvq_status kvq_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* kvq_status_string(kvq_status status);

@@ -184,6 +184,13 @@ uint8_t kvqo_e5m2_encode(float y)
     return sg | (uint8_t)(((e + 15) << 2) | (int)m);
 }
 
+void kvqo_e5m2_encode_range(uint32_t first_bits, uint32_t count, uint8_t* codes)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < (int64_t)count; ++i)
+        codes[i] = kvqo_e5m2_encode(bits_f32(first_bits + (uint32_t)i));
+}
+
 void kvqo_e5m2_encode_array(const float* y, int64_t n, uint8_t* codes)
 {
     #pragma omp parallel for schedule(static)

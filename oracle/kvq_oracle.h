@@ -40,6 +40,7 @@ void     kvqo_e4m3_encode_range(uint32_t first_bits, uint32_t count, uint8_t* co
 void     kvqo_e4m3_encode_array(const float* y, int64_t n, uint8_t* codes);
 double   kvqo_e5m2_value(uint8_t code);      /* OCP E5M2: +-inf at 0x7C/0xFC, NaN for 0x7D-0x7F/0xFD-0xFF */
 uint8_t  kvqo_e5m2_encode(float y);          /* nearest-even, saturating at +-57344 */
+void     kvqo_e5m2_encode_range(uint32_t first_bits, uint32_t count, uint8_t* codes);
 void     kvqo_e5m2_encode_array(const float* y, int64_t n, uint8_t* codes);
 
 /* ---- quantizers: one row of n values ------------------------------------ */

@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.kvqo_e5m2_encode.restype = ctypes.c_uint8
         L.kvqo_e5m2_encode.argtypes = [ctypes.c_float]
         L.kvqo_e5m2_encode_array.argtypes = [_P, ctypes.c_int64, _P]
+        L.kvqo_e5m2_encode_range.argtypes = [ctypes.c_uint32, ctypes.c_uint32, _P]
         L.kvqo_fp8_row.argtypes = [_P, ctypes.c_int, _P, _P]
         L.kvqo_fp8_row_static.argtypes = [_P, ctypes.c_int, ctypes.c_uint16, _P]
         L.kvqo_int8_row.argtypes = [_P, ctypes.c_int, _P, _P, _P]
@@ -116,6 +117,12 @@ def e5m2_encode(y) -> np.ndarray:
     y = _c(y, np.float32)
     out = np.empty(y.shape, dtype=np.uint8)
     lib().kvqo_e5m2_encode_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def e5m2_encode_range(first_bits: int, count: int) -> np.ndarray:
+    out = np.empty(count, dtype=np.uint8)
+    lib().kvqo_e5m2_encode_range(first_bits, count, _ptr(out))
     return out
 
 

@@ -15,15 +15,15 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI",
+    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2",
     "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
     "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
     "verify_workspace_bytes", "verify_attention", "verify_split", "verify_reduce",
-    "decode_attention", "decode_split", "decode_reduce", "e4m3_encode", "status_string",
+    "decode_attention", "decode_split", "decode_reduce", "e4m3_encode", "e5m2_encode", "status_string",
     "LIB_PATH",
 ]
 
-KVQ_FP8_E4M3, KVQ_INT8_ASYM, KVQ_INT4_KIVI = 1, 2, 3
+KVQ_FP8_E4M3, KVQ_INT8_ASYM, KVQ_INT4_KIVI, KVQ_FP8_E5M2 = 1, 2, 3, 4
 KVQ_SCALE_PER_TENSOR, KVQ_SCALE_PER_HEAD, KVQ_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -85,8 +85,9 @@ def lib() -> ctypes.CDLL:
         L.kvq_verify_reduce.restype = ctypes.c_int
         L.kvq_verify_reduce.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32, _I32, _P,
                                         ctypes.c_size_t, _P, _P, _P]
-        L.kvq_e4m3_encode.restype = ctypes.c_int
-        L.kvq_e4m3_encode.argtypes = [_P, _P, ctypes.c_int64, _P]
+        for fn in ("kvq_e4m3_encode", "kvq_e5m2_encode"):
+            getattr(L, fn).restype = ctypes.c_int
+            getattr(L, fn).argtypes = [_P, _P, ctypes.c_int64, _P]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -256,3 +257,8 @@ def verify_reduce(cache: Cache, num_seqs: int, q_len: int, num_q_heads: int, max
 def e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
     """float32 -> OCP E4M3 codes with the encoder the append kernel uses."""
     _check("kvq_e4m3_encode", lib().kvq_e4m3_encode(_ptr(x), _ptr(codes), int(x.numel()), _stream(stream)))
+
+
+def e5m2_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
+    """float32 -> OCP E5M2 codes with the encoder the append kernel uses for E5M2 caches."""
+    _check("kvq_e5m2_encode", lib().kvq_e5m2_encode(_ptr(x), _ptr(codes), int(x.numel()), _stream(stream)))

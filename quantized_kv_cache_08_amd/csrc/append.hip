@@ -20,8 +20,6 @@
 
 namespace kvq {
 
-constexpr int kFP8 = 1;
-constexpr int kINT8 = 2;
 
 template <int DT, bool STATIC, int PS>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
@@ -56,7 +54,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 
     uint32_t code[4];
     uint32_t scale_bits = 0, zero_bits = 0;
-    if constexpr (DT == kFP8) {
+    if constexpr (is_fp8_format(DT)) {
+        // the per-(token, head) scale maps the row's largest magnitude onto
+        // the format's largest finite value
+        constexpr float kMaxCode = (DT == kE5M2) ? 57344.0f : 448.0f;
         float sf;
         if constexpr (STATIC) {
             const int idx = kv * p.static_kv_stride + h * p.static_head_stride;
@@ -67,16 +68,21 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
             amax = group8_extreme<true>(amax);
-            scale_bits = bf16_up_bits(amax / 448.0f);
+            scale_bits = bf16_up_bits(amax / kMaxCode);
             sf = bf16lo(scale_bits);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (sf != 0.0f)
-                code[i] = e4m3_encode4(x[4 * i] / sf, x[4 * i + 1] / sf, x[4 * i + 2] / sf,
-                                       x[4 * i + 3] / sf);
-            else
+            if (sf != 0.0f) {
+                if constexpr (DT == kE5M2)
+                    code[i] = e5m2_encode4(x[4 * i] / sf, x[4 * i + 1] / sf, x[4 * i + 2] / sf,
+                                           x[4 * i + 3] / sf);
+                else
+                    code[i] = e4m3_encode4(x[4 * i] / sf, x[4 * i + 1] / sf, x[4 * i + 2] / sf,
+                                           x[4 * i + 3] / sf);
+            } else {
                 code[i] = 0u;
+            }
         }
     } else {
         float lo = x[0], hi = x[0];
@@ -141,6 +147,21 @@ __global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* x, uint8_
     }
 }
 
+__global__ __launch_bounds__(256) void e5m2_encode_kernel(const float* x, uint8_t* codes,
+                                                          long long n) {
+    const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i + 3 < n) {
+        const float* p = x + i;
+        uint32_t w = e5m2_encode4(p[0], p[1], p[2], p[3]);
+        codes[i] = (uint8_t)w;
+        codes[i + 1] = (uint8_t)(w >> 8);
+        codes[i + 2] = (uint8_t)(w >> 16);
+        codes[i + 3] = (uint8_t)(w >> 24);
+    } else {
+        for (long long j = i; j < n; ++j) codes[j] = (uint8_t)e5m2_encode4(x[j], 0.f, 0.f, 0.f);
+    }
+}
+
 template <int DT, bool STATIC, int PS>
 static hipError_t launch_append_t(const AppendParams& p, hipStream_t stream) {
     const long long threads = (long long)p.num_tokens * p.n_kv * 2 * 8;
@@ -160,6 +181,13 @@ hipError_t launch_append(int dtype, bool static_scale, int page_size, const Appe
         return page_size == 16 ? launch_append_t<kFP8, false, 16>(p, stream)
                                : launch_append_t<kFP8, false, 32>(p, stream);
     }
+    if (dtype == kE5M2) {
+        if (static_scale)
+            return page_size == 16 ? launch_append_t<kE5M2, true, 16>(p, stream)
+                                   : launch_append_t<kE5M2, true, 32>(p, stream);
+        return page_size == 16 ? launch_append_t<kE5M2, false, 16>(p, stream)
+                               : launch_append_t<kE5M2, false, 32>(p, stream);
+    }
     return page_size == 16 ? launch_append_t<kINT8, false, 16>(p, stream)
                            : launch_append_t<kINT8, false, 32>(p, stream);
 }
@@ -168,6 +196,13 @@ hipError_t launch_e4m3_encode(const float* x, uint8_t* codes, long long n, hipSt
     const long long grid = (n + 1023) / 1024;
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(e4m3_encode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, codes, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_e5m2_encode(const float* x, uint8_t* codes, long long n, hipStream_t stream) {
+    const long long grid = (n + 1023) / 1024;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL(e5m2_encode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, codes, n);
     return hipGetLastError();
 }
 

@@ -43,8 +43,6 @@
 
 namespace kvq {
 
-constexpr int kFP8 = 1;
-constexpr int kINT8 = 2;
 constexpr float kRescaleHeadroom = 8.0f;  // log2 units
 constexpr int kBufferFlags = 0x00020000;  // raw buffer resource, dword 3 (gfx9 family)
 
@@ -192,9 +190,9 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
                 const uint32_t d0 = src[(kb & 1) * 2];
                 const uint32_t d1 = src[(kb & 1) * 2 + 1];
                 u32x4_t a;
-                if constexpr (DT == kFP8) {
-                    a = u32x4_t{e4m3x2_to_bf16x2<false>(d0), e4m3x2_to_bf16x2<true>(d0),
-                                e4m3x2_to_bf16x2<false>(d1), e4m3x2_to_bf16x2<true>(d1)};
+                if constexpr (is_fp8_format(DT)) {
+                    a = u32x4_t{fp8x2_to_bf16x2<DT, false>(d0), fp8x2_to_bf16x2<DT, true>(d0),
+                                fp8x2_to_bf16x2<DT, false>(d1), fp8x2_to_bf16x2<DT, true>(d1)};
                 } else {
                     a = u32x4_t{hi_halves(u8_to_f32<0>(d0), u8_to_f32<1>(d0)),
                                 hi_halves(u8_to_f32<2>(d0), u8_to_f32<3>(d0)),
@@ -316,17 +314,17 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
             const int w = t >> 2;
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
-                if constexpr (DT == kFP8) {
+                if constexpr (is_fp8_format(DT)) {
                     const uint32_t bp = (uint32_t)(t & 2);
                     const uint32_t sel = bp | ((4u + bp) << 8) | ((bp + 1u) << 16) | ((5u + bp) << 24);
                     const uint32_t x01 = perm(cb.v[hp][1][w], cb.v[hp][0][w], sel);
                     const uint32_t x23 = perm(cb.v[hp][3][w], cb.v[hp][2][w], sel);
                     if (t & 1) {
-                        bv[2 * hp] = e4m3x2_to_bf16x2<true>(x01);
-                        bv[2 * hp + 1] = e4m3x2_to_bf16x2<true>(x23);
+                        bv[2 * hp] = fp8x2_to_bf16x2<DT, true>(x01);
+                        bv[2 * hp + 1] = fp8x2_to_bf16x2<DT, true>(x23);
                     } else {
-                        bv[2 * hp] = e4m3x2_to_bf16x2<false>(x01);
-                        bv[2 * hp + 1] = e4m3x2_to_bf16x2<false>(x23);
+                        bv[2 * hp] = fp8x2_to_bf16x2<DT, false>(x01);
+                        bv[2 * hp + 1] = fp8x2_to_bf16x2<DT, false>(x23);
                     }
                 } else {
                     const int by = t & 3;
@@ -347,7 +345,7 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
     // chunk is computed (two buffers, 194 VGPRs: two waves per SIMD); INT8
     // keeps two (three buffers: one wave per SIMD, which measured faster for
     // INT8 than two waves with two buffers)
-    if constexpr (DT == kFP8) {
+    if constexpr (is_fp8_format(DT)) {
         ChunkBuf b0, b1;
         load(b0, 0);
         for (int c = 0;;) {
@@ -468,6 +466,10 @@ static const void* pick_split(int dtype, bool static_scale, int page_size) {
     if (dtype == kFP8) {
         if (static_scale) return page_size == 16 ? split_fn<kFP8, true, 16>() : split_fn<kFP8, true, 32>();
         return page_size == 16 ? split_fn<kFP8, false, 16>() : split_fn<kFP8, false, 32>();
+    }
+    if (dtype == kE5M2) {
+        if (static_scale) return page_size == 16 ? split_fn<kE5M2, true, 16>() : split_fn<kE5M2, true, 32>();
+        return page_size == 16 ? split_fn<kE5M2, false, 16>() : split_fn<kE5M2, false, 32>();
     }
     return page_size == 16 ? split_fn<kINT8, false, 16>() : split_fn<kINT8, false, 32>();
 }

@@ -43,7 +43,8 @@ bool valid_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16
 // decode entry points) or refused as unsupported (the slot-based append).
 kvq_status check_cache(const kvq_cache* c, bool kivi) {
     if (!c) return KVQ_ERR_INVALID;
-    if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_INT8_ASYM && c->dtype != KVQ_INT4_KIVI)
+    if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2 && c->dtype != KVQ_INT8_ASYM &&
+        c->dtype != KVQ_INT4_KIVI)
         return KVQ_ERR_INVALID;
     if (c->scale_mode < KVQ_SCALE_PER_TENSOR || c->scale_mode > KVQ_SCALE_PER_TOKEN_HEAD)
         return KVQ_ERR_INVALID;
@@ -175,7 +176,8 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     // FP8: one workgroup (one wave per SIMD) per CU, although two fit: with
     // two waves per SIMD the memory system holds more requests than it
     // serves best, and the measured kernel time is about 2% longer
-    const int blocks_per_cu = (!kivi && c->dtype == KVQ_FP8_E4M3) ? std::min(per_cu, kFp8BlocksPerCu) : per_cu;
+    const bool fp8 = c->dtype == KVQ_FP8_E4M3 || c->dtype == KVQ_FP8_E5M2;
+    const int blocks_per_cu = fp8 ? std::min(per_cu, kFp8BlocksPerCu) : per_cu;
     const int grid = blocks_per_cu * cus;
     p.total_waves = grid * (kSplitThreads / 64);
     if (kivi) {
@@ -219,7 +221,7 @@ size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size, in
                         int32_t which) {
     if (page_size <= 0 || head_dim <= 0 || (which != 0 && which != 1)) return 0;
     size_t codes, meta;
-    if (dtype == KVQ_FP8_E4M3) {
+    if (dtype == KVQ_FP8_E4M3 || dtype == KVQ_FP8_E5M2) {
         if (scale_mode < KVQ_SCALE_PER_TENSOR || scale_mode > KVQ_SCALE_PER_TOKEN_HEAD) return 0;
         codes = (size_t)page_size * head_dim;
         meta = scale_mode == KVQ_SCALE_PER_TOKEN_HEAD ? 2u * page_size : 0u;
@@ -432,6 +434,13 @@ kvq_status kvq_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_
     if (n == 0) return KVQ_OK;
     if (!x || !codes) return KVQ_ERR_INVALID;
     return launch_e4m3_encode(x, codes, n, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
+    if (n < 0) return KVQ_ERR_INVALID;
+    if (n == 0) return KVQ_OK;
+    if (!x || !codes) return KVQ_ERR_INVALID;
+    return launch_e5m2_encode(x, codes, n, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 const char* kvq_status_string(kvq_status s) {

@@ -98,6 +98,45 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Four fp32 -> four OCP E5M2 codes, as e4m3_encode4: nearest-even through the
+// gfx950 converter (its BF8 format is OCP E5M2) after an explicit clamp to
+// +-57344 (saturation, no infinities); -0 keeps its sign; NaN gives 0x7F.
+__device__ __forceinline__ uint32_t e5m2_encode4(float a, float b, float c, float d) {
+    float ca = fminf(fmaxf(a, -57344.0f), 57344.0f);
+    float cb = fminf(fmaxf(b, -57344.0f), 57344.0f);
+    float cc = fminf(fmaxf(c, -57344.0f), 57344.0f);
+    float cd = fminf(fmaxf(d, -57344.0f), 57344.0f);
+    int w = __builtin_amdgcn_cvt_pk_bf8_f32(ca, cb, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(cc, cd, w, true);
+    uint32_t r = (uint32_t)w;
+    if (a != a) r = (r & 0xFFFFFF00u) | 0x7Fu;
+    if (b != b) r = (r & 0xFFFF00FFu) | 0x7F00u;
+    if (c != c) r = (r & 0xFF00FFFFu) | 0x7F0000u;
+    if (d != d) r = (r & 0x00FFFFFFu) | 0x7F000000u;
+    return r;
+}
+
+// Two E5M2 codes (bytes 0,1 or 2,3 of w) -> packed exact bf16 pair (two
+// mantissa bits and exponents down to 2^-16 fit bf16 exactly).
+template <bool HI>
+__device__ __forceinline__ uint32_t e5m2x2_to_bf16x2(uint32_t w) {
+    bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// The dtype codes of the kernels' templates (as kvq_dtype in kvq.h).
+constexpr int kFP8 = 1;    // OCP E4M3
+constexpr int kINT8 = 2;   // u8 asymmetric
+constexpr int kE5M2 = 4;   // OCP E5M2
+constexpr bool is_fp8_format(int dt) { return dt == kFP8 || dt == kE5M2; }
+
+// Two FP8 codes of format DT -> packed exact bf16 pair.
+template <int DT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    if constexpr (DT == kE5M2) return e5m2x2_to_bf16x2<HI>(w);
+    else return e4m3x2_to_bf16x2<HI>(w);
+}
+
 // Byte select: result byte i = selector byte i of `sel` choosing from
 // {lo bytes 0..3 (values 0..3), hi bytes 0..3 (values 4..7)}.
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {

@@ -36,7 +36,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "Workload", "WORKLOADS", "normal", "gen_q", "gen_kv", "gen_new_kv",
+    "Workload", "WORKLOADS", "normal", "gen_q", "gen_kv", "gen_new_kv", "static_scales",
     "outlier_channels", "seq_lens", "page_layout",
 ]
 
@@ -123,7 +123,7 @@ def _scaled_bf16(x: torch.Tensor, sigma: float, outl: Optional[List[int]], outl_
 @dataclass
 class Workload:
     name: str
-    dtype: str                # "fp8" | "int8" | "kivi4"
+    dtype: str                # "fp8" (E4M3) | "e5m2" | "int8" | "kivi4"
     batch: int
     num_q_heads: int
     num_kv_heads: int
@@ -141,6 +141,7 @@ class Workload:
     spare_frac: float = 0.05
     resid: int = 128          # KIVI fp16 recent window
     q_len: int = 1            # query positions per sequence (> 1: speculative-decoding verification)
+    scale_mode: int = 2       # 2: per-(token, head) scales; 1: static per head; 0: static per tensor
     group: int = 32           # KIVI group along tokens
     description: str = ""
 
@@ -167,10 +168,33 @@ WORKLOADS = {
                        description="Verification pass of speculative decoding on the Llama-3-8B-shaped layer: "
                                    "batch 32, context 8192 (including 4 new positions), 4 positions per sequence "
                                    "scored causally, 32 q / 8 kv heads, d128, page 16, FP8 E4M3"),
+    "e5m2": Workload("e5m2", "e5m2", 32, 32, 8, 128, 16, 8192, seed=2,
+                     description="Llama-3-8B-shaped decode layer in FP8 E5M2: 32 q / 8 kv heads, d128, batch 32, "
+                                 "context 8192, page 16, per-(token,head) BF16 scales, outlier K channels"),
+    "static": Workload("static", "fp8", 32, 32, 8, 128, 16, 8192, seed=2, scale_mode=1,
+                       description="Llama-3-8B-shaped decode layer in FP8 E4M3 with static per-head scales "
+                                   "(from the input distribution, see static_scales): 32 q / 8 kv heads, d128, "
+                                   "batch 32, context 8192, page 16"),
     "kivi": Workload("kivi", "kivi4", 4, 64, 8, 128, 32, 131072, seed=5,
                      description="KIVI-style 4-bit: 64 q / 8 kv heads, d128, batch 4, context 131072; K per-channel "
                                  "INT4 in 32-token groups, V per-token INT4, last 128 tokens fp16"),
 }
+
+
+def static_scales(w: Workload) -> torch.Tensor:
+    """Caller-side static scales for the static modes, bf16 [2][n_kv] (K, V):
+    the largest magnitude the generators put out with any real chance (6
+    sigma; K's outlier channels carry outlier_mult sigma) over the format's
+    largest code (448, E4M3), nudged per KV head so that heads differ.
+    Rarer values saturate, as static scales do."""
+    fmax = 57344.0 if w.dtype == "e5m2" else 448.0
+    kmax = 6.0 * w.sigma_k * (w.outlier_mult if w.n_outliers > 0 else 1.0)
+    vmax = 6.0 * w.sigma_v
+    h = torch.arange(w.num_kv_heads, dtype=torch.float32)
+    s = torch.stack([kmax / fmax * (1.0 + 0.03125 * h), vmax / fmax * (1.0 + 0.03125 * h)])
+    if w.scale_mode == 0:
+        s = s[:, :1]
+    return s.to(torch.bfloat16).contiguous()
 
 
 def seq_lens(w: Workload) -> np.ndarray:

@@ -39,7 +39,11 @@ class Built:
 
 
 def dtype_code(w: synthetic.Workload) -> int:
-    return {"fp8": kvq.KVQ_FP8_E4M3, "int8": kvq.KVQ_INT8_ASYM}[w.dtype]
+    return {"fp8": kvq.KVQ_FP8_E4M3, "int8": kvq.KVQ_INT8_ASYM, "e5m2": kvq.KVQ_FP8_E5M2}[w.dtype]
+
+
+def oracle_dtype(w: synthetic.Workload) -> int:
+    return {"fp8": O.FP8, "int8": O.INT8, "e5m2": O.E5M2}[w.dtype]
 
 
 def slots_for(layout: synthetic.PageLayout, b: int, pos0: int, n: int, ps: int, device) -> torch.Tensor:
@@ -108,8 +112,7 @@ def oracle_seq(bt: Built, b: int, mode: int = kvq.KVQ_SCALE_PER_TOKEN_HEAD, stat
     T = int(bt.lens[b])
     k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
     q = synthetic.gen_q(w, "cpu", batch=len(bt.lens))[b]
-    dt = O.FP8 if w.dtype == "fp8" else O.INT8
-    return O.decode_reference(u16(q), u16(k), u16(v), dt, mode, static_kv, softmax_scale)
+    return O.decode_reference(u16(q), u16(k), u16(v), oracle_dtype(w), mode, static_kv, softmax_scale)
 
 
 def allclose_report(got: np.ndarray, ref: np.ndarray, atol=2e-3, rtol=1e-2):

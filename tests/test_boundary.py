@@ -189,6 +189,27 @@ def test_verify_validation(L):
     assert L.kvq_verify_workspace_bytes(ctypes.byref(d), 32, 0, 8, 8192, 0, ctypes.byref(out4)) == INVALID
 
 
+def test_e5m2_cache_and_encoder_validation(L):
+    """E5M2 caches take the E4M3 record layout and every FP8 scale mode;
+    nothing here reaches a launch."""
+    for mode in (0, 1, 2):
+        for ps in (16, 32):
+            for which in (0, 1):
+                assert kvq.record_bytes(4, mode, ps, 128, which) == kvq.record_bytes(1, mode, ps, 128, which)
+    d = _desc(dtype=4)
+    assert _decode(L, d, hq=6) == UNSUPPORTED
+    assert _decode(L, d, ws_bytes=0) == WORKSPACE
+    assert _decode(L, d, num_seqs=0) == OK
+    assert _decode(L, _desc(dtype=4, scale_mode=1)) == INVALID          # static mode needs its scales
+    assert _verify(L, d, q_len=5) == UNSUPPORTED
+    assert _append(L, _desc(dtype=4), n=-1) == INVALID
+    assert _append(L, _desc(dtype=4), n=0) == OK
+    assert _append(L, _desc(dtype=5)) == INVALID                        # no such dtype
+    assert L.kvq_e5m2_encode(FAKE, FAKE, -1, None) == INVALID
+    assert L.kvq_e5m2_encode(FAKE, FAKE, 0, None) == OK
+    assert L.kvq_e5m2_encode(None, FAKE, 5, None) == INVALID
+
+
 def test_encode_and_status(L):
     assert L.kvq_e4m3_encode(FAKE, FAKE, -1, None) == INVALID
     assert L.kvq_e4m3_encode(FAKE, FAKE, 0, None) == OK

@@ -1,0 +1,160 @@
+"""GPU parity of the FP8 E5M2 cache (KVQ_FP8_E5M2) against the CPU oracle.
+
+The device encoder must equal the oracle's nearest-even saturating E5M2
+encoder on every float32 with |y| < 2^16 (both signs) and on the specials.
+Codes and BF16 scales written by kvq_append must match the oracle's
+quantizers bit for bit; attention outputs must satisfy |gpu - oracle| <=
+2e-3 + 1e-2 |oracle| against fp64 attention on the oracle's own dequantized
+cache (the same bar as E4M3).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from tests.conftest import gpu_available
+
+pytestmark = pytest.mark.gpu
+
+if not gpu_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import quantized_kv_cache_08_amd as kvq  # noqa: E402
+import synthetic  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from tests import kvq_harness as H  # noqa: E402
+
+ATOL, RTOL = 2e-3, 1e-2
+LSE_ATOL = 1e-3
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def workload(base: str, **kw) -> synthetic.Workload:
+    d = dict(synthetic.WORKLOADS[base].__dict__)
+    d.update(kw)
+    return synthetic.Workload(**d)
+
+
+def check_seq(bt: H.Built, out, lse, b: int, mode=kvq.KVQ_SCALE_PER_TOKEN_HEAD, static_kv=None):
+    ref = H.oracle_seq(bt, b, mode, static_kv)
+    for which, name in ((0, "k"), (1, "v")):
+        codes, scales, _ = H.read_seq(bt, b, which, kvq.KVQ_FP8_E5M2, mode)
+        assert np.array_equal(codes, ref[name + "_codes"]), f"{name} codes differ (seq {b})"
+        if scales is not None:
+            assert np.array_equal(scales, ref[name + "_scale"]), f"{name} scales differ (seq {b})"
+    ok, mabs, mrel = H.allclose_report(out[b].cpu().numpy(), ref["out"], ATOL, RTOL)
+    assert ok, f"seq {b}: max abs {mabs:.3e} max rel {mrel:.3e}"
+    if lse is not None:
+        dl = np.abs(lse[b].cpu().numpy().astype(np.float64) - ref["lse"]).max()
+        assert dl <= LSE_ATOL, f"seq {b}: lse diff {dl:.3e}"
+
+
+def test_e5m2_encoder_exhaustive_sweep():
+    """Every float32 bit pattern with |y| < 2^16 (past the 57344 saturation
+    point), both signs, plus specials."""
+    say("e5m2 sweep")
+    top = int(np.array([65536.0], dtype=np.float32).view(np.uint32)[0])
+    step = 1 << 27
+    x = torch.empty(step, dtype=torch.float32, device="cuda")
+    codes = torch.empty(step, dtype=torch.uint8, device="cuda")
+    for sign in (0, 1 << 31):
+        for start in range(0, top, step):
+            n = min(step, top - start)
+            bits = torch.arange(start, start + n, dtype=torch.int64, device="cuda") | sign
+            x[:n] = bits.to(torch.int32).view(torch.float32)
+            kvq.e5m2_encode(x[:n], codes[:n])
+            got = codes[:n].cpu().numpy()
+            ref = O.e5m2_encode_range((start | sign) & 0xFFFFFFFF, n)
+            bad = np.nonzero(got != ref)[0]
+            assert bad.size == 0, (hex((start | sign) + int(bad[0])), got[bad[0]], ref[bad[0]])
+    sp = np.array([np.inf, -np.inf, np.nan, 1e30, -1e30, 3.4e38, 57344.0, 61440.0, -61440.0, 1e-40, -1e-40,
+                   0.0, -0.0, 2.0**-17, 3 * 2.0**-18], dtype=np.float32)
+    t = torch.from_numpy(sp).cuda()
+    c = torch.empty(sp.size, dtype=torch.uint8, device="cuda")
+    kvq.e5m2_encode(t, c)
+    assert np.array_equal(c.cpu().numpy(), O.e5m2_encode(sp))
+
+
+LENS = np.array([1, 5, 17, 96, 250, 700], dtype=np.int64)
+
+
+def test_e5m2_ragged_batch_partitions():
+    w = workload("tiny", dtype="e5m2", batch=len(LENS), context=int(LENS.max()))
+    say("e5m2 ragged")
+    bt = H.build(w, lens=LENS)
+    for part in (0, 1, 3):
+        say("  partition pages", part)
+        out, lse = H.run_decode(bt, part)
+        for b in range(len(LENS)):
+            check_seq(bt, out, lse, b)
+
+
+def test_e5m2_static_scale_modes():
+    w = workload("tiny", dtype="e5m2", batch=2)
+    lens = np.array([96, 250])
+    for mode in (kvq.KVQ_SCALE_PER_TENSOR, kvq.KVQ_SCALE_PER_HEAD):
+        if mode == kvq.KVQ_SCALE_PER_TENSOR:
+            host = np.array([2.0**-12, 2.0**-14], dtype=np.float32)          # K saturates on the outliers
+            static_kv = tuple(H.u16(torch.tensor(v).to(torch.bfloat16)) for v in host)
+        else:
+            host = np.array([[2.0**-11, 2.0**-13], [2.0**-15, 1e-4]], dtype=np.float32)
+            static_kv = tuple(H.u16(torch.from_numpy(r).to(torch.bfloat16)) for r in host)
+        ss = torch.from_numpy(host).to(torch.bfloat16).cuda().contiguous()
+        say("e5m2 static mode", mode)
+        bt = H.build(w, lens=lens, mode=mode, static_scales=ss)
+        out, lse = H.run_decode(bt)
+        for b in range(2):
+            check_seq(bt, out, lse, b, mode=mode, static_kv=static_kv)
+
+
+def test_e5m2_page_size_32_and_groups():
+    for heads, ps in (((8, 2), 32), ((16, 2), 16), ((2, 2), 16)):
+        w = workload("tiny", dtype="e5m2", batch=3, num_q_heads=heads[0], num_kv_heads=heads[1], page_size=ps)
+        say("e5m2 heads", heads, "page", ps)
+        bt = H.build(w, lens=np.array([31, 300, 64]))
+        out, lse = H.run_decode(bt)
+        for b in range(3):
+            check_seq(bt, out, lse, b)
+
+
+def test_e5m2_verification_pass():
+    w = workload("tiny", dtype="e5m2", batch=len(LENS), context=int(LENS.max()))
+    say("e5m2 verify")
+    bt = H.build(w, lens=LENS)
+    B, q_len, Hq, d = len(LENS), 4, w.num_q_heads, w.head_dim
+    q = synthetic.gen_q(w, "cuda", batch=B * q_len).reshape(B, q_len, Hq, d)
+    ws = torch.zeros(kvq.verify_workspace_bytes(bt.cache, B, q_len, Hq, bt.max_ctx), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((B, q_len, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((B, q_len, Hq), float("nan"), device="cuda")
+    kvq.verify_attention(bt.cache, q, bt.block_table, bt.context_lens, bt.max_ctx, d ** -0.5, ws, out, lse)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qc = synthetic.gen_q(w, "cpu", batch=B * q_len).reshape(B, q_len, Hq, d)
+    for b in range(B):
+        T = int(LENS[b])
+        k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
+        ref = O.verify_reference(H.u16(qc[b]), H.u16(k), H.u16(v), O.E5M2)
+        for i in range(q_len):
+            if T - q_len + 1 + i <= 0:
+                assert not out[b, i].any() and np.all(np.isneginf(lse[b, i]))
+                continue
+            ok, mabs, mrel = H.allclose_report(out[b, i], ref["out"][i], ATOL, RTOL)
+            assert ok, f"seq {b} position {i}: max abs {mabs:.3e} max rel {mrel:.3e}"
+
+
+def test_e5m2_llama8b_shape_sampled():
+    """The 8B-shaped batch (B 32, context 8192) in E5M2, in the benchmark's
+    launch configuration; three sequences checked against the oracle."""
+    w = workload("llama8b", dtype="e5m2")
+    say("e5m2 llama8b shape")
+    bt = H.build(w)
+    out, lse = H.run_decode(bt)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    for b in (0, 13, w.batch - 1):
+        check_seq(bt, out, lse, b)

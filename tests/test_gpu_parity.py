@@ -41,7 +41,7 @@ def small(base: str, **kw) -> synthetic.Workload:
 
 
 def check_seq(bt: H.Built, out, lse, b: int, mode=kvq.KVQ_SCALE_PER_TOKEN_HEAD, static_kv=None):
-    dt = kvq.KVQ_FP8_E4M3 if bt.w.dtype == "fp8" else kvq.KVQ_INT8_ASYM
+    dt = H.dtype_code(bt.w)
     ref = H.oracle_seq(bt, b, mode, static_kv)
     for which, name in ((0, "k"), (1, "v")):
         codes, scales, zeros = H.read_seq(bt, b, which, dt, mode)

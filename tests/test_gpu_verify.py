@@ -63,7 +63,7 @@ def check(bt: H.Built, q_len: int, out: np.ndarray, lse: np.ndarray, seqs=None):
     w = bt.w
     B = len(bt.lens)
     q_cpu = verify_q(w, B, q_len, "cpu")
-    dt = O.FP8 if w.dtype == "fp8" else O.INT8
+    dt = H.oracle_dtype(w)
     for b in (range(B) if seqs is None else seqs):
         T = int(bt.lens[b])
         k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
