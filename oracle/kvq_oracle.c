@@ -325,10 +325,11 @@ void kvqo_dequantize_rows(int dtype, int mode, const uint8_t* codes, int64_t row
 }
 
 /* ======================================================================= *
- * KIVI-style 4-bit ([ryotta] §3.1 KIVI; [molayo] formats notes on mixed    *
- * 4-bit): K per channel, V per token, the most recent tokens kept in full  *
- * precision.  Tokens leave the fp16 window in whole groups, oldest first,  *
- * once the window holds more than `resid` tokens.                          *
+ * KIVI-style b-bit ([ryotta] §3.1 KIVI: asymmetric 2-bit; [molayo] formats *
+ * notes on mixed 4-bit): K per channel, V per token, the most recent       *
+ * tokens kept in full precision.  Tokens leave the fp16 window in whole    *
+ * groups, oldest first, once the window holds more than `resid` tokens.    *
+ * b = 4 or 2: 2^b - 1 steps of the asymmetric quantizer above.             *
  * ======================================================================= */
 int64_t kvqo_kivi_quantized_count(int64_t T, int resid, int group)
 {
@@ -337,10 +338,11 @@ int64_t kvqo_kivi_quantized_count(int64_t T, int resid, int group)
     return (over / group) * group;
 }
 
-void kvqo_kivi_k(const uint16_t* x16, int64_t nq, int n, int group,
+void kvqo_kivi_k(const uint16_t* x16, int64_t nq, int n, int group, int bits,
                  uint8_t* codes, uint16_t* s, uint16_t* z)
 {
     int64_t ng = nq / group;
+    int levels = (1 << bits) - 1;
     #pragma omp parallel for schedule(static)
     for (int64_t gi = 0; gi < ng; ++gi) {
         float buf[group * n];
@@ -348,18 +350,19 @@ void kvqo_kivi_k(const uint16_t* x16, int64_t nq, int n, int group,
             for (int c = 0; c < n; ++c)
                 buf[t * n + c] = (float)kvqo_f16_value(x16[(gi * group + t) * n + c]);
         for (int c = 0; c < n; ++c)
-            kvqo_uint_asym(buf + c, group, n, 15, codes + gi * group * n + c, n,
+            kvqo_uint_asym(buf + c, group, n, levels, codes + gi * group * n + c, n,
                            &s[gi * n + c], &z[gi * n + c]);
     }
 }
 
-void kvqo_kivi_v(const uint16_t* x16, int64_t nq, int n, uint8_t* codes, uint16_t* s, uint16_t* z)
+void kvqo_kivi_v(const uint16_t* x16, int64_t nq, int n, int bits, uint8_t* codes, uint16_t* s, uint16_t* z)
 {
+    int levels = (1 << bits) - 1;
     #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < nq; ++t) {
         float buf[n];
         for (int c = 0; c < n; ++c) buf[c] = (float)kvqo_f16_value(x16[t * n + c]);
-        kvqo_uint_asym(buf, n, 1, 15, codes + t * n, 1, &s[t], &z[t]);
+        kvqo_uint_asym(buf, n, 1, levels, codes + t * n, 1, &s[t], &z[t]);
     }
 }
 

@@ -60,14 +60,15 @@ void kvqo_quantize_rows(int dtype, int mode, const uint16_t* x_bf16, int64_t row
 void kvqo_dequantize_rows(int dtype, int mode, const uint8_t* codes, int64_t rows, int n,
                           const uint16_t* scale, const uint16_t* zero, double* out);
 
-/* KIVI-style 4-bit state of one (sequence, KV head) stream of T fp16 rows
- * x16[T][n] (fp16 bits).  Tokens [0, nq) are quantized in groups of `group`
- * tokens: K per channel within the group, V per token; the rest stays fp16.
- * codes: [nq][n] one code per byte;  K: ks/kz [nq/group][n];  V: vs/vz [nq]. */
+/* KIVI-style b-bit state (bits = 4 or 2) of one (sequence, KV head) stream
+ * of T fp16 rows x16[T][n] (fp16 bits).  Tokens [0, nq) are quantized in
+ * groups of `group` tokens: K per channel within the group, V per token; the
+ * rest stays fp16.  codes: [nq][n] one code per byte (0 .. 2^bits - 1);
+ * K: ks/kz [nq/group][n];  V: vs/vz [nq].                                   */
 int64_t kvqo_kivi_quantized_count(int64_t T, int resid, int group);
-void kvqo_kivi_k(const uint16_t* x16, int64_t nq, int n, int group,
+void kvqo_kivi_k(const uint16_t* x16, int64_t nq, int n, int group, int bits,
                  uint8_t* codes, uint16_t* s, uint16_t* z);
-void kvqo_kivi_v(const uint16_t* x16, int64_t nq, int n,
+void kvqo_kivi_v(const uint16_t* x16, int64_t nq, int n, int bits,
                  uint8_t* codes, uint16_t* s, uint16_t* z);
 
 /* ---- attention (fp64) --------------------------------------------------- */

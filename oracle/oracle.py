@@ -69,8 +69,8 @@ def lib() -> ctypes.CDLL:
                                            _P, _P, _P]
         L.kvqo_kivi_quantized_count.restype = ctypes.c_int64
         L.kvqo_kivi_quantized_count.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
-        L.kvqo_kivi_k.argtypes = [_P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P, _P]
-        L.kvqo_kivi_v.argtypes = [_P, ctypes.c_int64, ctypes.c_int, _P, _P, _P]
+        L.kvqo_kivi_k.argtypes = [_P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P, _P]
+        L.kvqo_kivi_v.argtypes = [_P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P, _P]
         L.kvqo_attention.argtypes = [_P, _P, _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_double, _P, _P]
         L.kvqo_lse_merge.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, _P, _P]
@@ -191,8 +191,9 @@ def kivi_quantized_count(T: int, resid: int, group: int) -> int:
     return int(lib().kvqo_kivi_quantized_count(T, resid, group))
 
 
-def kivi_stream(x16_k, x16_v, resid: int, group: int):
-    """KIVI state of one (sequence, KV head): fp16 bits [T][n] for K and V.
+def kivi_stream(x16_k, x16_v, resid: int, group: int, bits: int = 4):
+    """KIVI state of one (sequence, KV head): fp16 bits [T][n] for K and V,
+    quantized to `bits` (4 or 2) bits.
 
     Returns dict with nq, K codes/s/z (per channel per group), V codes/s/z
     (per token), and the fp16 residual rows [nq, T).
@@ -209,8 +210,8 @@ def kivi_stream(x16_k, x16_v, resid: int, group: int):
     vz = np.zeros(nq, dtype=np.uint16)
     L = lib()
     if nq:
-        L.kvqo_kivi_k(_ptr(k), nq, n, group, _ptr(kc), _ptr(ks), _ptr(kz))
-        L.kvqo_kivi_v(_ptr(v), nq, n, _ptr(vc), _ptr(vs), _ptr(vz))
+        L.kvqo_kivi_k(_ptr(k), nq, n, group, bits, _ptr(kc), _ptr(ks), _ptr(kz))
+        L.kvqo_kivi_v(_ptr(v), nq, n, bits, _ptr(vc), _ptr(vs), _ptr(vz))
     return dict(nq=nq, k_codes=kc, k_s=ks, k_z=kz, v_codes=vc, v_s=vs, v_z=vz,
                 k_res=k[nq:].copy(), v_res=v[nq:].copy())
 

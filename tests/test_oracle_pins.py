@@ -286,17 +286,33 @@ def test_int8_constant_row(oracle):
     assert oracle.dequantize_rows(oracle.INT8, codes, s, z)[0, 0] == 0.75
 
 
-def test_int4_asym_bound(oracle):
-    rng = np.random.default_rng(16)
+@pytest.mark.parametrize("levels", [15, 3])
+def test_int4_int2_asym_bound(oracle, levels):
+    """4-bit (15 steps) and the KIVI 2-bit setting ([ryotta] section 3.1: 3 steps)."""
+    rng = np.random.default_rng(16 + levels)
     for _ in range(300):
         x = (rng.standard_normal(32) * rng.choice([1, 20])).astype(np.float16).astype(np.float32)
-        c, s, z = oracle.uint_asym(x, 15)
+        c, s, z = oracle.uint_asym(x, levels)
         sv, zv = float(oracle.bf16_value([s])[0]), float(oracle.bf16_value([z])[0])
-        assert zv <= x.min() and c.max() <= 15
+        assert zv <= x.min() and c.max() <= levels
         assert np.all(np.abs(x - (c * sv + zv)) <= sv * (0.5 + 2.0**-12))
-        grid = np.arange(16) * sv + zv
+        grid = np.arange(levels + 1) * sv + zv
         d = np.abs(x[:, None].astype(np.float64) - grid[None, :])
         assert np.all(d[np.arange(32), c] <= d.min(axis=1) + sv * 2.0**-12)
+        # the minimum maps to code 0 and (the step being at most 2^-7 above
+        # (max - z) / levels) the maximum to the top code
+        assert c[np.argmin(x)] == 0 and c[np.argmax(x)] == levels
+
+
+def test_int2_grid_values_roundtrip(oracle):
+    """Values on the 2-bit grid {z, z+s, z+2s, z+3s} with bf16-exact z and s
+    quantize back to their own codes and dequantize exactly."""
+    for z, s in ((-1.5, 0.25), (0.0, 2.0**-5), (3.0, 1.0), (-40.0, 12.0)):
+        codes = np.array([0, 1, 2, 3, 3, 2, 1, 0] * 4, dtype=np.float64)
+        x = (z + codes * s).astype(np.float32)
+        c, sb, zb = oracle.uint_asym(x, 3)
+        assert float(oracle.bf16_value([zb])[0]) == z and float(oracle.bf16_value([sb])[0]) == s
+        assert np.array_equal(c, codes.astype(np.uint8))
 
 
 def test_kivi_window_rule(oracle):
@@ -311,14 +327,17 @@ def test_kivi_window_rule(oracle):
         assert nq % 32 == 0 and (T < 128 or 128 <= T - nq < 160)
 
 
-def test_kivi_groups_per_channel_and_per_token(oracle):
+@pytest.mark.parametrize("bits", [4, 2])
+def test_kivi_groups_per_channel_and_per_token(oracle, bits):
     """K statistics run along tokens (one (s, z) per channel per group); V along channels."""
     rng = np.random.default_rng(17)
     T, n = 200, 128
+    levels = (1 << bits) - 1
     k = (rng.standard_normal((T, n)) * np.where(np.arange(n) % 31 == 0, 20, 1)).astype(np.float16)
     v = rng.standard_normal((T, n)).astype(np.float16)
-    st = oracle.kivi_stream(k.view(np.uint16), v.view(np.uint16), 128, 32)
+    st = oracle.kivi_stream(k.view(np.uint16), v.view(np.uint16), 128, 32, bits)
     assert st["nq"] == 64 and st["k_s"].shape == (2, n) and st["v_s"].shape == (64,)
+    assert st["k_codes"].max() == levels and st["v_codes"].max() == levels
     kh, vh = oracle.kivi_dequant(st, 32)
     ks = np.repeat(oracle.bf16_value(st["k_s"]), 32, axis=0)
     assert np.all(np.abs(kh[:64] - k[:64].astype(np.float64)) <= ks * (0.5 + 2.0**-12))
@@ -327,6 +346,29 @@ def test_kivi_groups_per_channel_and_per_token(oracle):
     assert np.array_equal(kh[64:], k[64:].astype(np.float64))         # window kept exactly
     # an outlier channel gets its own, larger step; ordinary channels are not widened by it
     assert ks[0, 0] > 5 * np.median(ks[0])
+    # brute force per K channel of the first group: each code is a nearest of the 2^b levels
+    k0 = k[:32].astype(np.float64)
+    kz = oracle.bf16_value(st["k_z"][0]).astype(np.float64)
+    grid = kz[None, :, None] + np.arange(levels + 1)[None, None, :] * ks[0][None, :, None]
+    dist = np.abs(k0[:, :, None] - grid)
+    chosen = np.take_along_axis(dist, st["k_codes"][:32, :, None].astype(np.int64), axis=2)[..., 0]
+    assert np.all(chosen <= dist.min(axis=2) + ks[0][None, :] * 2.0**-12)
+
+
+def test_kivi_2bit_error_exceeds_4bit(oracle):
+    """Fewer levels, larger steps: on the same rows the 2-bit steps are about
+    5x (15/3) the 4-bit ones and the mean error grows accordingly."""
+    rng = np.random.default_rng(18)
+    k = rng.standard_normal((192, 128)).astype(np.float16)
+    v = rng.standard_normal((192, 128)).astype(np.float16)
+    e = {}
+    for bits in (4, 2):
+        st = oracle.kivi_stream(k.view(np.uint16), v.view(np.uint16), 128, 32, bits)
+        kh, vh = oracle.kivi_dequant(st, 32)
+        e[bits] = (np.abs(kh[:64] - k[:64]).mean(), np.abs(vh[:64] - v[:64]).mean(),
+                   np.median(oracle.bf16_value(st["k_s"])), np.median(oracle.bf16_value(st["v_s"])))
+    assert 4.5 <= e[2][2] / e[4][2] <= 5.5 and 4.5 <= e[2][3] / e[4][3] <= 5.5
+    assert e[2][0] > 3 * e[4][0] and e[2][1] > 3 * e[4][1]
 
 
 # ----------------------------------------------------------------- P6 attention
