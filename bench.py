@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama8b",
-                    choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "verify", "e5m2", "static"])
+                    choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "kivi2", "verify", "e5m2", "static"])
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto)")
     ap.add_argument("--partition-pages", type=int, default=0)
     ap.add_argument("--graph", action="store_true",
@@ -73,8 +73,9 @@ def step_bytes(w, lens: np.ndarray):
     tokens = int(lens.sum())
     B = len(lens)
     QL = w.q_len                                       # query positions per sequence
-    if w.dtype == "kivi4":
-        rk, rv = 2048 + 4 * d, 2048 + 4 * w.page_size      # INT4 page records (codes + bf16 s, z)
+    if w.kivi_bits:
+        codes = w.page_size * d * w.kivi_bits // 8         # INT4 / INT2 page records (codes + bf16 s, z)
+        rk, rv = codes + 4 * d, codes + 4 * w.page_size
         nq = kivi_quantized(w, lens)
         pages = int((nq // w.page_size).sum())
         window = (tokens - int(nq.sum())) * n_kv * d * 2 * 2  # fp16 K and V rows
@@ -127,11 +128,11 @@ def cpu_baseline(w, budget_s: float):
     from oracle import oracle as O
 
     lens = synthetic.seq_lens(w)
-    kivi = w.dtype == "kivi4"
+    kivi = w.kivi_bits > 0
     if kivi:
         # a 16384-token prefix of each sequence keeps one pass to a few seconds
         lens = np.minimum(lens, 16384)
-    dt = {"fp8": O.FP8, "e5m2": O.E5M2, "int8": O.INT8, "kivi4": None}[w.dtype]
+    dt = {"fp8": O.FP8, "e5m2": O.E5M2, "int8": O.INT8, "kivi4": None, "kivi2": None}[w.dtype]
     QL = w.q_len
     static_kv = None
     if w.scale_mode != 2:
@@ -154,7 +155,7 @@ def cpu_baseline(w, budget_s: float):
         kd = np.zeros((T, w.num_kv_heads, w.head_dim))
         vd = np.zeros_like(kd)
         for h in range(w.num_kv_heads):
-            st = O.kivi_stream(k16[:, h], v16[:, h], w.resid, w.page_size)
+            st = O.kivi_stream(k16[:, h], v16[:, h], w.resid, w.page_size, w.kivi_bits)
             kd[:, h], vd[:, h] = O.kivi_dequant(st, w.page_size)
         O.attention(O.bf16_value(qb).astype(np.float64), kd, vd, scale)
 
@@ -239,14 +240,14 @@ def main():
     # out for the full length); every step appends that token, then decodes.
     # A verification workload (q_len > 1) holds all but the q_len newest
     # positions, appends those and scores them causally.
-    kivi = w.dtype == "kivi4"
+    kivi = w.kivi_bits > 0
     QL = w.q_len
     full_layout = synthetic.page_layout(w, lens)
     bt_dev = torch.from_numpy(full_layout.block_table).cuda()
     caches = []
     for r in range(reps):
         if kivi:
-            cache = kvq.Cache(kvq.KVQ_INT4_KIVI, full_layout.num_pages, w.num_kv_heads, w.page_size, d,
+            cache = kvq.Cache(kvq.KVQ_INT2_KIVI if w.kivi_bits == 2 else kvq.KVQ_INT4_KIVI, full_layout.num_pages, w.num_kv_heads, w.page_size, d,
                               max_seqs=B, residual=w.resid)
             held = np.zeros(B, dtype=np.int64)
             target = lens - 1
@@ -402,7 +403,7 @@ def main():
         "metric": "paged FP8/INT8 decode-attn KV GB/s (% of HBM peak) + tokens/s at 1 GPU",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "e5m2": "fp8_e5m2", "int8": "u8", "kivi4": "u4"}[w.dtype],
+        "vs_baseline": None, "dtype": {"fp8": "fp8_e4m3", "e5m2": "fp8_e5m2", "int8": "u8", "kivi4": "u4", "kivi2": "u2"}[w.dtype],
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": w.num_kv_heads, "head_dim": d, "page_size": w.page_size,

@@ -1,5 +1,5 @@
 /*
- * kvq.h -- paged FP8 / INT8 (and KIVI-style INT4) KV cache for MI355X (gfx950).
+ * kvq.h -- paged FP8 / INT8 (and KIVI-style INT4 / INT2) KV cache for MI355X (gfx950).
  *
  * C ABI of libkvq.so.  Every pointer argument except `cache` and `bytes` is a
  * DEVICE pointer owned by the caller; the library never allocates, frees or
@@ -24,8 +24,8 @@
  *    per-head static scales (molayo1419.me, formats table notes and the
  *    serving-flag values; ryotta.opik.net section 3.1).  KIVI: K quantized per
  *    channel, V per token, the most recent tokens kept in full precision
- *    (ryotta.opik.net section 3.1, KIVI; molayo1419.me formats notes on mixed
- *    4-bit).
+ *    (ryotta.opik.net section 3.1, KIVI, an asymmetric 2-bit method;
+ *    molayo1419.me formats notes on mixed 4-bit).
  *  - Storage is paged: fixed-size blocks in one pool, mapped per request by a
  *    block table ("FP8 KV Cache부터 INT4 Weight-Only까지", daewooki.github.io,
  *    core concept 2) PagedAttention).
@@ -37,9 +37,10 @@
  *  E5M2:                  the same two rules with 57344 and e5m2_rne_sat
  *  INT8 per-(token,head): z = bf16_floor(min), s = bf16_ceil((max - z) / 255),
  *                         code = clamp(rne((x - z) / s), 0, 255), x^ = code*s + z
- *  KIVI INT4:             the same asymmetric rule with 15 steps; K over the 32
- *                         tokens of a group per channel, V over the channels of
- *                         a token.  s == 0 (constant row) gives all-zero codes.
+ *  KIVI INT4 / INT2:      the same asymmetric rule with 15 / 3 steps; K over
+ *                         the 32 tokens of a group per channel, V over the
+ *                         channels of a token.  s == 0 (constant row) gives
+ *                         all-zero codes.
  *  Every "/" is one IEEE float32 division; E4M3 is the OCP encoding (max 448),
  *  E5M2 the OCP encoding (max 57344; saturating, so no infinities are stored).
  *
@@ -50,7 +51,11 @@
  *   bytes per row, low nibble = even channel; INT4 V: the rows of tokens 2m and
  *   2m + 1 interleaved in 16-bit units, i.e. 32-bit word q of pair row m holds
  *   channels 4q..4q+3 of token 2m in bits 0-15 and of token 2m + 1 in bits
- *   16-31, channel 4q + i in bits 4i..4i+3 of each half), then
+ *   16-31, channel 4q + i in bits 4i..4i+3 of each half;  INT2: half as many
+ *   rows, each the INT4 row layout above in which every 4-bit field holds two
+ *   2-bit codes, bits 0-1 for the first half of the page's tokens and bits 2-3
+ *   for the second: INT2 K row j (64 bytes) holds tokens j and j + 16, INT2 V
+ *   pair row m (128 bytes) holds token pairs m and m + 8), then
  *   per-(token,head) modes: page_size bf16 scales, then (INT8) page_size bf16
  *   zero-points;  KIVI K: head_dim bf16 scales then head_dim bf16 zero-points
  *   (one per channel for the page's 32-token group);  KIVI V: page_size bf16
@@ -83,7 +88,8 @@ typedef enum kvq_dtype {
     KVQ_FP8_E4M3 = 1,         /* OCP E4M3, 1 byte per element                            */
     KVQ_INT8_ASYM = 2,        /* u8 code with per-(token,head) scale and zero-point      */
     KVQ_INT4_KIVI = 3,        /* 4-bit codes, K per channel / V per token, fp16 window   */
-    KVQ_FP8_E5M2 = 4          /* OCP E5M2, 1 byte per element; records as KVQ_FP8_E4M3  */
+    KVQ_FP8_E5M2 = 4,         /* OCP E5M2, 1 byte per element; records as KVQ_FP8_E4M3  */
+    KVQ_INT2_KIVI = 5         /* 2-bit codes, otherwise as KVQ_INT4_KIVI                  */
 } kvq_dtype;
 
 typedef enum kvq_scale_mode {
@@ -95,16 +101,16 @@ typedef enum kvq_scale_mode {
 /* Descriptor of one layer's cache.  Plain data; the library keeps no copy. */
 typedef struct kvq_cache {
     int32_t dtype;            /* kvq_dtype                                               */
-    int32_t scale_mode;       /* kvq_scale_mode; INT8 and INT4 need PER_TOKEN_HEAD       */
+    int32_t scale_mode;       /* kvq_scale_mode; INT8 and KIVI need PER_TOKEN_HEAD       */
     int32_t num_pages;        /* pages in each pool                                      */
-    int32_t page_size;        /* tokens per page: 16 or 32 (INT4: 32 = the group size)   */
+    int32_t page_size;        /* tokens per page: 16 or 32 (KIVI: 32 = the group size)   */
     int32_t num_kv_heads;     /* >= 1                                                    */
     int32_t head_dim;         /* 128                                                     */
     void* k_pages;            /* device: num_pages*num_kv_heads K records                */
     void* v_pages;            /* device: num_pages*num_kv_heads V records                */
     const void* static_scales;/* device bf16; PER_TENSOR: [2] = {K, V};
                                  PER_HEAD: [2][num_kv_heads]; otherwise NULL             */
-    /* INT4 (KIVI) only: fp16 recent-token window, a ring of window_tokens rows
+    /* KIVI (INT4 / INT2) only: fp16 recent-token window, a ring of window_tokens rows
        per (sequence, KV head); token t sits at row t % window_tokens.          */
     void* k_window;           /* device fp16 [max_seqs][num_kv_heads][window_tokens][head_dim] */
     void* v_window;
@@ -118,7 +124,7 @@ typedef struct kvq_cache {
 size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size,
                         int32_t head_dim, int32_t which);
 
-/* Quantize-on-append (FP8 E4M3 / E5M2, INT8; a KVQ_INT4_KIVI cache returns
+/* Quantize-on-append (FP8 E4M3 / E5M2, INT8; a KIVI cache returns
  * KVQ_ERR_UNSUPPORTED, it has kvq_kivi_append).
  * k, v:          device bf16 [num_tokens][num_kv_heads][head_dim], contiguous.
  * slot_mapping:  device int32 [num_tokens]; slot = page*page_size + row; a
@@ -128,12 +134,12 @@ size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size,
 kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,
                       const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream);
 
-/* KIVI-style INT4 append (cache->dtype == KVQ_INT4_KIVI): new tokens of each
+/* KIVI-style append (cache->dtype KVQ_INT4_KIVI or KVQ_INT2_KIVI): new tokens of each
  * sequence enter the fp16 window; whole 32-token groups leave it, oldest
  * first, once it would hold more than cache->residual tokens, and are written
  * quantized (K per channel over the group, V per token) into the page that
  * block_table[b][group index] names.  A sequence of n tokens thus holds its
- * first n_q = 32 * floor(max(0, n - residual) / 32) tokens as INT4 pages and
+ * first n_q = 32 * floor(max(0, n - residual) / 32) tokens as INT4 / INT2 pages and
  * tokens [n_q, n) as fp16 window rows (token t at row t % window_tokens).
  * k, v:           device bf16 [total new tokens][num_kv_heads][head_dim]; the
  *                 rows of sequence b are [token_offsets[b], token_offsets[b+1]).
@@ -146,8 +152,9 @@ kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,
  * Sequence b uses window slot b (num_seqs <= cache->max_seqs).  fp16 window
  * values are the bf16 inputs rounded to nearest-even; the quantizers read
  * those fp16 values.  Requires page_size 32 and window_tokens >= residual + 32.
- * KIVI (ryotta.opik.net "KV Cache 압축" section 3.1; molayo1419.me formats-table
- * notes on mixed-precision 4-bit). */
+ * KIVI (ryotta.opik.net "KV Cache 압축" section 3.1: asymmetric 2-bit, K per
+ * channel, V per token, recent tokens in full precision; molayo1419.me
+ * formats-table notes on mixed-precision 4-bit). */
 kvq_status kvq_kivi_append(const kvq_cache* cache, const void* k, const void* v,
                            const int32_t* token_offsets, const int32_t* context_lens,
                            const int32_t* block_table, int32_t max_pages_per_seq, int32_t num_seqs,
@@ -160,8 +167,9 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
                                       int32_t partition_pages, size_t* bytes);
 
 /* One decode step of attention for one query token per sequence, reading the
- * quantized paged cache (FP8 / INT8, or INT4 pages plus the fp16 window for
- * KVQ_INT4_KIVI, sequence b reading window slot b) with dequantization fused in:
+ * quantized paged cache (FP8 / INT8, or INT4 / INT2 pages plus the fp16 window
+ * for the KIVI dtypes, sequence b reading window slot b) with dequantization
+ * fused in:
  *   out[b][h] = sum_t softmax_t(softmax_scale * q[b][h] . k^[t]) v^[t]
  * over every cached token t < context_lens[b] of KV head h / (num_q_heads /
  * num_kv_heads).  fp32 accumulation, flash-decoding split over the context.
@@ -218,7 +226,7 @@ kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t n
  * Other arguments as kvq_decode_attention; the workspace size comes from
  * kvq_verify_workspace_bytes.  The q_len x (num_q_heads / num_kv_heads) query
  * rows of a KV head are one 16-row tile: their product must be <= 16
- * (KVQ_ERR_UNSUPPORTED otherwise), and KVQ_INT4_KIVI caches are not supported
+ * (KVQ_ERR_UNSUPPORTED otherwise), and KIVI caches are not supported
  * (KVQ_ERR_UNSUPPORTED).  The KV bytes are read once for all q_len rows. */
 kvq_status kvq_verify_workspace_bytes(const kvq_cache* cache, int32_t num_seqs, int32_t q_len,
                                       int32_t num_q_heads, int32_t max_context_len,

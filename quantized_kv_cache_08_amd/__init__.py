@@ -1,4 +1,4 @@
-"""Paged FP8 / INT8 (and KIVI-style INT4) KV cache for MI355X.
+"""Paged FP8 / INT8 (and KIVI-style INT4 / INT2) KV cache for MI355X.
 
 Thin ctypes binding over ``libkvq.so`` (HIP kernels for gfx950, C ABI in
 ``include/kvq.h``).  Argument marshalling only: every step of the path runs in
@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2",
+    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2", "KVQ_INT2_KIVI", "KIVI_DTYPES",
     "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
     "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
     "verify_workspace_bytes", "verify_attention", "verify_split", "verify_reduce",
@@ -23,7 +23,8 @@ __all__ = [
     "LIB_PATH",
 ]
 
-KVQ_FP8_E4M3, KVQ_INT8_ASYM, KVQ_INT4_KIVI, KVQ_FP8_E5M2 = 1, 2, 3, 4
+KVQ_FP8_E4M3, KVQ_INT8_ASYM, KVQ_INT4_KIVI, KVQ_FP8_E5M2, KVQ_INT2_KIVI = 1, 2, 3, 4, 5
+KIVI_DTYPES = (KVQ_INT4_KIVI, KVQ_INT2_KIVI)
 KVQ_SCALE_PER_TENSOR, KVQ_SCALE_PER_HEAD, KVQ_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -137,9 +138,9 @@ class Cache:
         self.v_pages = alloc((n * self.rec_v,), dtype=torch.uint8, device=device)
         self.static_scales = static_scales
         self.max_seqs, self.residual = max_seqs, residual
-        self.window_tokens = residual + page_size if dtype == KVQ_INT4_KIVI else 0
+        self.window_tokens = residual + page_size if dtype in KIVI_DTYPES else 0
         self.k_window = self.v_window = None
-        if dtype == KVQ_INT4_KIVI and max_seqs > 0:
+        if dtype in KIVI_DTYPES and max_seqs > 0:
             shape = (max_seqs, num_kv_heads, self.window_tokens, head_dim)
             self.k_window = torch.zeros(shape, dtype=torch.float16, device=device)
             self.v_window = torch.zeros(shape, dtype=torch.float16, device=device)
@@ -164,7 +165,7 @@ def append(cache: Cache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.T
 
 def kivi_append(cache: Cache, k: torch.Tensor, v: torch.Tensor, token_offsets: torch.Tensor,
                 context_lens: torch.Tensor, block_table: torch.Tensor, max_new_tokens: int, stream=None) -> None:
-    """INT4 (KIVI) append (kvq_kivi_append): new bf16 rows [total][n_kv][d] of each
+    """KIVI INT4 / INT2 append (kvq_kivi_append): new bf16 rows [total][n_kv][d] of each
     sequence (rows token_offsets[b]..token_offsets[b+1]); context_lens = tokens
     held before the call."""
     num_seqs = int(context_lens.numel())

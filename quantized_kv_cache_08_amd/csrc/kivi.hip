@@ -1,10 +1,10 @@
-// kivi.hip -- KIVI-style 4-bit KV cache (gfx950): K quantized per channel
-// over groups of 32 tokens, V per token, the most recent tokens kept in
-// fp16 ("KV Cache 압축", ryotta.opik.net, section 3.1 KIVI; "KV 캐시
-// 양자화(KV cache quantization) ...", molayo1419.me, formats-table notes on
-// mixed-precision 4-bit: K per channel for its channel outliers, V per
-// token), with attention over the quantized pages and the fp16 window fused
-// into one split-K decode kernel.
+// kivi.hip -- KIVI-style 4-bit and 2-bit KV cache (gfx950): K quantized per
+// channel over groups of 32 tokens, V per token, the most recent tokens kept
+// in fp16 ("KV Cache 압축", ryotta.opik.net, section 3.1 KIVI, an asymmetric
+// 2-bit method; "KV 캐시 양자화(KV cache quantization) ...", molayo1419.me,
+// formats-table notes on mixed-precision 4-bit: K per channel for its channel
+// outliers, V per token), with attention over the quantized pages and the
+// fp16 window fused into one split-K decode kernel.
 //
 // Window rule: a sequence of n tokens holds its first
 //   n_q = 32 * floor(max(0, n - residual) / 32)
@@ -12,14 +12,20 @@
 // as fp16 rows in a ring of `window` >= residual + 32 rows (token t at row
 // t % window).  Tokens leave the window whole groups at a time, oldest first.
 //
-// Quantizer (both K and V; 15 steps):  z = bf16 floor of the minimum,
-//   s = bf16 ceil of (max - z) / 15,  code = clamp(rne((x - z) / s), 0, 15),
-//   x^ = code * s + z, every "/" one IEEE float32 division.  The inputs are
-//   the fp16 values (bf16 input rounded to nearest-even fp16).
+// Quantizer (both K and V; L = 2^bits - 1 = 15 or 3 steps):  z = bf16 floor
+//   of the minimum, s = bf16 ceil of (max - z) / L,  code = clamp(rne((x - z)
+//   / s), 0, L), x^ = code * s + z, every "/" one IEEE float32 division.  The
+//   inputs are the fp16 values (bf16 input rounded to nearest-even fp16).
 //
 // V records store each token pair's code rows interleaved in 16-bit units:
 // word q of pair row m holds channels 4q..4q+3 of token 2m (bits 0-15) and of
 // token 2m + 1 (bits 16-31), channel 4q + i in bits 4i..4i+3 of each half.
+//
+// 2-bit records hold the 4-bit layout at half the rows: every 4-bit field
+// carries two codes, bits 0-1 for the first 16 tokens of the page and bits 2-3
+// for the last 16 (K row j: tokens j and j + 16; V pair row m: pairs m and
+// m + 8).  The decode kernel shifts a field's word by 0 or 2 and masks 2 bits
+// where the 4-bit kernel masks 4; the rest of its arithmetic is the same.
 //
 // Decode of one 32-token page, per wave (lane l: j = l % 16, g = l / 16):
 //   score_t = sum_c q_c (n_tc s_c + z_c) = sum_c n_tc (q_c s_c) + sum_c q_c z_c.
@@ -48,12 +54,13 @@ __device__ __forceinline__ int kivi_nq(int n, int resid) {
 }
 
 // ============================================================== append
-// Asymmetric 15-step quantizer of one value given the row's (z, s).
+// Asymmetric quantizer with L steps of one value given the row's (z, s).
+template <int L>
 __device__ __forceinline__ uint32_t kivi_code(float x, float zf, float sf) {
 #pragma clang fp contract(off)
     if (sf == 0.0f) return 0u;
     float t = rintf((x - zf) / sf);
-    t = fminf(fmaxf(t, 0.0f), 15.0f);
+    t = fminf(fmaxf(t, 0.0f), (float)L);
     return (uint32_t)t;
 }
 
@@ -82,9 +89,11 @@ __device__ __forceinline__ void kivi_window_row(const KiviAppendParams& p, int b
 // has no group to flush then, also writes the new token's window row.  Its
 // ring row cannot be one the flush reads: those hold positions p with
 // n0 - (residual + 31) <= p < n0, and the ring has window >= residual + 32 rows.
-template <bool ONE_TOKEN>
+template <int BITS, bool ONE_TOKEN>
 __global__ __launch_bounds__(256) void kivi_flush_kernel(KiviAppendParams p) {
 #pragma clang fp contract(off)
+    constexpr int L = (1 << BITS) - 1;
+    constexpr int kCodeBytes = kKiviGroup * kHeadDim * BITS / 8;    // metadata follows the codes
     const int b = blockIdx.z;
     const int h = blockIdx.y;
     if (ONE_TOKEN && blockIdx.x == 1) {
@@ -140,49 +149,64 @@ __global__ __launch_bounds__(256) void kivi_flush_kernel(KiviAppendParams p) {
         }
         const uint32_t zb = bf16_down_bits(lo);
         const float zf = bf16lo(zb);
-        const uint32_t sb = bf16_up_bits((hi - zf) / 15.0f);
+        const uint32_t sb = bf16_up_bits((hi - zf) / (float)L);
         const float sf = bf16lo(sb);
+        // row r holds token r (4 bits) or tokens r and r + 16 (2 + 2 bits)
+        constexpr int kRows = BITS == 4 ? kKiviGroup : kKiviGroup / 2;
 #pragma unroll
-        for (int t = 0; t < kKiviGroup; ++t) {
-            const uint32_t code = kivi_code(x[t], zf, sf);
+        for (int r = 0; r < kRows; ++r) {
+            uint32_t code = kivi_code<L>(x[r], zf, sf);
+            if constexpr (BITS == 2) code |= kivi_code<L>(x[r + kRows], zf, sf) << 2;
             const uint32_t other = dpp_mov<0xB1>(code);   // quad_perm [1,0,3,2]: lane c ^ 1
-            if ((c & 1) == 0) krec[t * (kHeadDim / 2) + (c >> 1)] = (uint8_t)(code | (other << 4));
+            if ((c & 1) == 0) krec[r * (kHeadDim / 2) + (c >> 1)] = (uint8_t)(code | (other << 4));
         }
-        *(uint16_t*)(krec + kKiviGroup * kHeadDim / 2 + 2 * c) = (uint16_t)sb;
-        *(uint16_t*)(krec + kKiviGroup * kHeadDim / 2 + 2 * kHeadDim + 2 * c) = (uint16_t)zb;
+        *(uint16_t*)(krec + kCodeBytes + 2 * c) = (uint16_t)sb;
+        *(uint16_t*)(krec + kCodeBytes + 2 * kHeadDim + 2 * c) = (uint16_t)zb;
     }
 
     else {
         // ---- V: token t over its 128 channels (one wave per 16 tokens, two
-        // channels per lane; all 32 loads of a lane first)
+        // channels per lane; all 32 loads of a lane first).  4 bits: wave w
+        // takes tokens 16w + i.  2 bits: tokens 8w + i / 2 + 16 (i & 1), so that
+        // the two tokens sharing a code byte (t and t + 16) are in one lane.
         const int w = (tid - kHeadDim) >> 6;
         const int l = tid & 63;
+        auto tok = [&](int i) { return BITS == 4 ? w * (kKiviGroup / 2) + i : 8 * w + (i >> 1) + 16 * (i & 1); };
         uint32_t wv[kKiviGroup / 2];
 #pragma unroll
         for (int i = 0; i < kKiviGroup / 2; ++i) {
-            const int t = w * (kKiviGroup / 2) + i;
-            const uint16_t* a = src(p.v_window, p.v, t, 2 * l);
+            const uint16_t* a = src(p.v_window, p.v, tok(i), 2 * l);
             wv[i] = (uint32_t)a[0] | ((uint32_t)a[1] << 16);
         }
+        uint32_t c0[kKiviGroup / 2], c1[kKiviGroup / 2];
 #pragma unroll
         for (int i = 0; i < kKiviGroup / 2; ++i) {
-            const int t = w * (kKiviGroup / 2) + i;
+            const int t = tok(i);
             const float x0 = value((uint16_t)(wv[i] & 0xFFFFu), t);
             const float x1 = value((uint16_t)(wv[i] >> 16), t);
             const float lo = wave_extreme<false>(fminf(x0, x1));
             const float hi = wave_extreme<true>(fmaxf(x0, x1));
             const uint32_t zb = bf16_down_bits(lo);
             const float zf = bf16lo(zb);
-            const uint32_t sb = bf16_up_bits((hi - zf) / 15.0f);
+            const uint32_t sb = bf16_up_bits((hi - zf) / (float)L);
             const float sf = bf16lo(sb);
-            const uint32_t c0 = kivi_code(x0, zf, sf);
-            const uint32_t c1 = kivi_code(x1, zf, sf);
-            // token pairs interleaved in 16-bit units: pair t / 2, channel quad l / 2
-            vrec[(t >> 1) * kHeadDim + 4 * (l >> 1) + 2 * (t & 1) + (l & 1)] = (uint8_t)(c0 | (c1 << 4));
+            c0[i] = kivi_code<L>(x0, zf, sf);
+            c1[i] = kivi_code<L>(x1, zf, sf);
             if (l == 0) {
-                *(uint16_t*)(vrec + kKiviGroup * kHeadDim / 2 + 2 * t) = (uint16_t)sb;
-                *(uint16_t*)(vrec + kKiviGroup * kHeadDim / 2 + 2 * kKiviGroup + 2 * t) = (uint16_t)zb;
+                *(uint16_t*)(vrec + kCodeBytes + 2 * t) = (uint16_t)sb;
+                *(uint16_t*)(vrec + kCodeBytes + 2 * kKiviGroup + 2 * t) = (uint16_t)zb;
             }
+        }
+        // token pairs interleaved in 16-bit units: pair row t / 2, channel quad l / 2
+#pragma unroll
+        for (int i = 0; i < kKiviGroup / 2; i += (BITS == 4 ? 1 : 2)) {
+            const int t = tok(i);
+            uint32_t b0 = c0[i], b1 = c1[i];
+            if constexpr (BITS == 2) {
+                b0 |= c0[i + 1] << 2;     // token t + 16
+                b1 |= c1[i + 1] << 2;
+            }
+            vrec[(t >> 1) * kHeadDim + 4 * (l >> 1) + 2 * (t & 1) + (l & 1)] = (uint8_t)(b0 | (b1 << 4));
         }
     }
 }
@@ -198,12 +222,16 @@ __global__ __launch_bounds__(256) void kivi_window_kernel(KiviAppendParams p) {
 
 hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream) {
     if (p.num_seqs <= 0 || p.max_new <= 0) return hipSuccess;
+    if (p.bits != 4 && p.bits != 2) return hipErrorInvalidValue;
     const int groups = (p.max_new + kKiviGroup - 1) / kKiviGroup + 1;
+    const dim3 grid(groups, p.n_kv, p.num_seqs);
     if (p.max_new == 1) {      // one launch: flush and window row (see kivi_flush_kernel)
-        hipLaunchKernelGGL(kivi_flush_kernel<true>, dim3(groups, p.n_kv, p.num_seqs), dim3(256), 0, stream, p);
+        if (p.bits == 4) hipLaunchKernelGGL((kivi_flush_kernel<4, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((kivi_flush_kernel<2, true>), grid, dim3(256), 0, stream, p);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(kivi_flush_kernel<false>, dim3(groups, p.n_kv, p.num_seqs), dim3(256), 0, stream, p);
+    if (p.bits == 4) hipLaunchKernelGGL((kivi_flush_kernel<4, false>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((kivi_flush_kernel<2, false>), grid, dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kivi_window_kernel, dim3((p.max_new + 15) / 16, p.n_kv, p.num_seqs), dim3(256), 0,
@@ -327,7 +355,9 @@ __device__ __forceinline__ uint32_t v_pair(uint32_t w, uint32_t m0, uint32_t m1)
 // SHARE (query group <= 8): lanes j and j + 8 hold the same head and each
 // forms q' = q s for half of the channel blocks; lane j receives the other
 // half from lane j + 8.  Columns 8-15 of the score tile are then unused.
-template <bool SHARE>
+// BITS = 2: one load brings a lane's codes of both token halves (hp = 0, 1),
+// in bits 0-1 and 2-3 of each 4-bit field; the buffers' [0] entries hold them.
+template <int BITS, bool SHARE>
 __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const int b, const int h,
                                              const int page0, const int page1, const int seg,
                                              const int n_seg, const int lane, lds_u8* smeta,
@@ -385,7 +415,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     const uint32_t kC = 0x43434343u;           // bf16 high byte of 128 + n
     const u32x4_t kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const uint32_t neg_lo = opaque_sgpr(0x0000BF80u), neg_hi = opaque_sgpr(0xBF800000u);   // bf16 (-1, 0), (0, -1)
-    // V nibble masks, opaque to the compiler so that they stay in two VGPRs
+    // V code masks, opaque to the compiler so that they stay in two VGPRs
     // instead of being rematerialised before every and_or
     uint32_t vm0 = 0x000F000Fu, vm1 = 0x00780078u;
     __asm__("" : "+v"(vm0));
@@ -394,7 +424,8 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     const int off_kc = j * (kHeadDim / 2) + 16 * g;
     const int off_vc = (2 * g) * (2 * kHeadDim / 2) + 8 * j;
     constexpr int kPairBytes = 2 * kHeadDim / 2;                   // one V token pair
-    constexpr int kMetaOff = kKiviGroup * kHeadDim / 2;          // metadata after the codes
+    constexpr int kMetaOff = kKiviGroup * kHeadDim * BITS / 8;   // metadata after the codes
+    constexpr int kHalves = BITS == 4 ? 2 : 1;                    // code loads per page and lane
 
     auto load = [&](KiviBuf& cb, const int c) {
         const bool live = c < n_q;
@@ -408,10 +439,10 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
             (void*)(p.v_pages + rec_idx * (size_t)p.rec_v), (short)0, live ? (int)p.rec_v : 0,
             kKiviBufferFlags);
 #pragma unroll
-        for (int hp = 0; hp < 2; ++hp)
+        for (int hp = 0; hp < kHalves; ++hp)
             cb.kc[hp] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_kc + hp * 16 * (kHeadDim / 2), 0, 0);
 #pragma unroll
-        for (int hp = 0; hp < 2; ++hp)
+        for (int hp = 0; hp < kHalves; ++hp)
 #pragma unroll
             for (int rp = 0; rp < 2; ++rp)
                 cb.vc[hp][rp] = __builtin_amdgcn_raw_buffer_load_b64(
@@ -511,9 +542,16 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
             f32x4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const uint32_t w = cb.kc[hp][kb];
-                const uint32_t x = w & 0x0F0F0F0Fu;
-                const uint32_t y = (w >> 4) & 0x0F0F0F0Fu;
+                uint32_t x, y;
+                if constexpr (BITS == 4) {
+                    const uint32_t w = cb.kc[hp][kb];
+                    x = w & 0x0F0F0F0Fu;
+                    y = (w >> 4) & 0x0F0F0F0Fu;
+                } else {
+                    const uint32_t w = cb.kc[0][kb];
+                    x = (w >> (2 * hp)) & 0x03030303u;
+                    y = (w >> (4 + 2 * hp)) & 0x03030303u;
+                }
                 const u32x4_t a = {perm(kC, x, 0x04010400u), perm(kC, y, 0x04010400u),
                                    perm(kC, x, 0x04030402u), perm(kC, y, 0x04030402u)};
                 d = mfma_16x16x32_bf16(a, BH[kb], d);
@@ -577,7 +615,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         pd.ahi = ahi;
         pd.alo = alo;
 #pragma unroll
-        for (int hp = 0; hp < 2; ++hp)
+        for (int hp = 0; hp < kHalves; ++hp)
 #pragma unroll
             for (int rp = 0; rp < 2; ++rp) pd.vc[hp][rp] = cb.vc[hp][rp];
     };
@@ -597,13 +635,22 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
             for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
                 for (int rp = 0; rp < 2; ++rp) {
-                    const uint32_t w = pd.vc[hp][rp][t >> 2];
                     uint32_t o;
-                    switch (t & 3) {
-                        case 0: o = v_pair<0>(w, vm0, vm1); break;
-                        case 1: o = v_pair<1>(w, vm0, vm1); break;
-                        case 2: o = v_pair<2>(w, vm0, vm1); break;
-                        default: o = v_pair<3>(w, vm0, vm1); break;
+                    if constexpr (BITS == 4) {
+                        const uint32_t w = pd.vc[hp][rp][t >> 2];
+                        switch (t & 3) {
+                            case 0: o = v_pair<0>(w, vm0, vm1); break;
+                            case 1: o = v_pair<1>(w, vm0, vm1); break;
+                            case 2: o = v_pair<2>(w, vm0, vm1); break;
+                            default: o = v_pair<3>(w, vm0, vm1); break;
+                        }
+                    } else {
+                        // the same operand words from the 2-bit fields (bits 2 hp of
+                        // each 4-bit field), in plain code: the inline-assembly form
+                        // gave wrong first-channel products at this width
+                        constexpr uint32_t kSh[4] = {0, 1, 8, 9};
+                        const uint32_t w = pd.vc[0][rp][t >> 2] >> (2 * hp + kSh[t & 3]);
+                        o = (w & ((t & 1) ? 0x00180018u : 0x00030003u)) | 0x43004300u;
                     }
                     bv[2 * hp + rp] = o;
                 }
@@ -771,7 +818,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     }
 }
 
-template <bool SHARE>
+template <int BITS, bool SHARE>
 __global__ __launch_bounds__(256) void kivi_split_kernel(KiviSplitParams kp) {
     __shared__ __attribute__((aligned(16))) uint8_t s_meta[kSplitThreads / 64][kKiviMetaBytes];
     __shared__ __attribute__((aligned(16))) uint32_t s_zero[64];
@@ -780,16 +827,18 @@ __global__ __launch_bounds__(256) void kivi_split_kernel(KiviSplitParams kp) {
     lds_u8* smeta = (lds_u8*)&s_meta[wid][0];
     const lds_u8* szero = (const lds_u8*)&s_zero[0];
     for_each_segment<kKiviGroup>(kp.s, [&](int b, int h, int page0, int page1, int seg, int n_seg, int lane) {
-        kivi_segment<SHARE>(kp, b, h, page0, page1, seg, n_seg, lane, smeta, szero);
+        kivi_segment<BITS, SHARE>(kp, b, h, page0, page1, seg, n_seg, lane, smeta, szero);
     });
 }
 
-static const void* kivi_split_fn(int group) {
-    return group <= 8 ? (const void*)&kivi_split_kernel<true> : (const void*)&kivi_split_kernel<false>;
+static const void* kivi_split_fn(int bits, int group) {
+    if (bits == 2)
+        return group <= 8 ? (const void*)&kivi_split_kernel<2, true> : (const void*)&kivi_split_kernel<2, false>;
+    return group <= 8 ? (const void*)&kivi_split_kernel<4, true> : (const void*)&kivi_split_kernel<4, false>;
 }
 
-hipError_t kivi_split_occupancy(int group, size_t lds_bytes, int* blocks_per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kivi_split_fn(group), kSplitThreads,
+hipError_t kivi_split_occupancy(int bits, int group, size_t lds_bytes, int* blocks_per_cu) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kivi_split_fn(bits, group), kSplitThreads,
                                                         lds_bytes);
 }
 
@@ -797,7 +846,8 @@ hipError_t launch_kivi_split(const KiviSplitParams& p, int grid, size_t lds_byte
     if (grid <= 0) return hipSuccess;
     KiviSplitParams args = p;
     void* kargs[] = {&args};
-    return hipLaunchKernel(kivi_split_fn(p.s.group), dim3(grid), dim3(kSplitThreads), kargs, lds_bytes,
+    if (p.bits != 4 && p.bits != 2) return hipErrorInvalidValue;
+    return hipLaunchKernel(kivi_split_fn(p.bits, p.s.group), dim3(grid), dim3(kSplitThreads), kargs, lds_bytes,
                            stream);
 }
 

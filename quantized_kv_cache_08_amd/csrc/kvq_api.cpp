@@ -39,12 +39,15 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool valid_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
-// Descriptor checks.  kivi: whether the INT4 window layout is accepted (the
+bool is_kivi(int dtype) { return dtype == KVQ_INT4_KIVI || dtype == KVQ_INT2_KIVI; }
+int kivi_bits(int dtype) { return dtype == KVQ_INT2_KIVI ? 2 : 4; }
+
+// Descriptor checks.  kivi: whether the KIVI window layout is accepted (the
 // decode entry points) or refused as unsupported (the slot-based append).
 kvq_status check_cache(const kvq_cache* c, bool kivi) {
     if (!c) return KVQ_ERR_INVALID;
     if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2 && c->dtype != KVQ_INT8_ASYM &&
-        c->dtype != KVQ_INT4_KIVI)
+        !is_kivi(c->dtype))
         return KVQ_ERR_INVALID;
     if (c->scale_mode < KVQ_SCALE_PER_TENSOR || c->scale_mode > KVQ_SCALE_PER_TOKEN_HEAD)
         return KVQ_ERR_INVALID;
@@ -52,7 +55,7 @@ kvq_status check_cache(const kvq_cache* c, bool kivi) {
         return KVQ_ERR_INVALID;
     if (!c->k_pages || !c->v_pages) return KVQ_ERR_INVALID;
     if (c->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
-    if (c->dtype == KVQ_INT4_KIVI) {
+    if (is_kivi(c->dtype)) {
         if (!kivi) return KVQ_ERR_UNSUPPORTED;
         if (c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD || c->page_size != kKiviGroup)
             return KVQ_ERR_UNSUPPORTED;
@@ -115,11 +118,11 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
     if (!valid_group(num_q_heads / c->num_kv_heads)) return KVQ_ERR_UNSUPPORTED;
     // the query rows of one KV head (group x positions) form one 16-wide MFMA tile
     if ((long long)q_len * (num_q_heads / c->num_kv_heads) > 16) return KVQ_ERR_UNSUPPORTED;
-    if (q_len > 1 && c->dtype == KVQ_INT4_KIVI) return KVQ_ERR_UNSUPPORTED;
+    if (q_len > 1 && is_kivi(c->dtype)) return KVQ_ERR_UNSUPPORTED;
     if ((long long)max_context_len > (long long)max_pages_per_seq * c->page_size)
         return KVQ_ERR_INVALID;
     if (num_seqs > 16383) return KVQ_ERR_UNSUPPORTED;   // prefix table lives in LDS
-    if (c->dtype == KVQ_INT4_KIVI && num_seqs > c->max_seqs) return KVQ_ERR_INVALID;
+    if (is_kivi(c->dtype) && num_seqs > c->max_seqs) return KVQ_ERR_INVALID;
     if (num_seqs == 0) return KVQ_OK;
     if (!q || !block_table || !context_lens || !out || !workspace) return KVQ_ERR_INVALID;
     *plan = make_plan(c->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, q_len);
@@ -166,9 +169,9 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     p.score_scale = softmax_scale * 1.4426950408889634f;
 
     const size_t lds = ((size_t)num_seqs + 1) * sizeof(int32_t);
-    const bool kivi = c->dtype == KVQ_INT4_KIVI;
+    const bool kivi = is_kivi(c->dtype);
     int per_cu = 0;
-    hipError_t e = kivi ? kivi_split_occupancy(p.group, lds, &per_cu)
+    hipError_t e = kivi ? kivi_split_occupancy(kivi_bits(c->dtype), p.group, lds, &per_cu)
                         : split_occupancy(c->dtype, is_static, c->page_size, lds, &per_cu);
     if (e != hipSuccess) return KVQ_ERR_HIP;
     const int cus = device_cus();
@@ -187,6 +190,7 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
         kp.v_window = (const uint16_t*)c->v_window;
         kp.window = c->window_tokens;
         kp.residual = c->residual;
+        kp.bits = kivi_bits(c->dtype);
         e = launch_kivi_split(kp, grid, lds, stream);
     } else {
         e = launch_split(c->dtype, is_static, c->page_size, p, grid, lds, stream);
@@ -229,9 +233,9 @@ size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size, in
         if (scale_mode != KVQ_SCALE_PER_TOKEN_HEAD) return 0;
         codes = (size_t)page_size * head_dim;
         meta = 4u * page_size;
-    } else if (dtype == KVQ_INT4_KIVI) {
-        if (scale_mode != KVQ_SCALE_PER_TOKEN_HEAD || (head_dim & 1)) return 0;
-        codes = (size_t)page_size * head_dim / 2;
+    } else if (is_kivi(dtype)) {
+        if (scale_mode != KVQ_SCALE_PER_TOKEN_HEAD || (head_dim & 3)) return 0;
+        codes = (size_t)page_size * head_dim * kivi_bits(dtype) / 8;
         meta = which == 0 ? 4u * (size_t)head_dim : 4u * page_size;
     } else {
         return 0;
@@ -273,7 +277,7 @@ kvq_status kvq_kivi_append(const kvq_cache* cache, const void* k, const void* v,
                            const int32_t* block_table, int32_t max_pages_per_seq, int32_t num_seqs,
                            int32_t max_new_tokens, hipStream_t stream) {
     if (!cache) return KVQ_ERR_INVALID;
-    if (cache->dtype != KVQ_INT4_KIVI) return check_cache(cache, false) == KVQ_OK
+    if (!is_kivi(cache->dtype)) return check_cache(cache, false) == KVQ_OK
                                                   ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
     kvq_status st = check_cache(cache, true);
     if (st != KVQ_OK) return st;
@@ -304,6 +308,7 @@ kvq_status kvq_kivi_append(const kvq_cache* cache, const void* k, const void* v,
     p.residual = cache->residual;
     p.max_new = max_new_tokens;
     p.num_pages = cache->num_pages;
+    p.bits = kivi_bits(cache->dtype);
     return launch_kivi_append(p, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

@@ -14,7 +14,7 @@ constexpr int kMinChunkPages = 4;  // smallest automatic work range per wave
 constexpr int kSegmentCost = 8;    // start-up of a segment, in pages, for ragged batches (measured best on the mixed workload)
 constexpr int kSplitThreads = 256; // 4 waves per workgroup
 constexpr int kFp8BlocksPerCu = 1;  // FP8 split kernel workgroups per CU
-constexpr int kKiviGroup = 32;     // INT4 path: tokens per K group = page size
+constexpr int kKiviGroup = 32;     // KIVI path: tokens per K group = page size
 
 struct AppendParams {
     const uint16_t* k;             // bf16 [T][n_kv][128]
@@ -73,6 +73,7 @@ struct KiviAppendParams {
     uint16_t* v_window;
     long long rec_k, rec_v;
     int num_seqs, n_kv, max_pages_per_seq, window, residual, max_new, num_pages;
+    int bits;                      // code width: 4 or 2
 };
 
 struct KiviSplitParams {
@@ -80,6 +81,7 @@ struct KiviSplitParams {
     const uint16_t* k_window;
     const uint16_t* v_window;
     int window, residual;
+    int bits;                      // code width: 4 or 2
 };
 
 hipError_t launch_append(int dtype, bool static_scale, int page_size, const AppendParams& p,
@@ -95,6 +97,6 @@ hipError_t launch_e5m2_encode(const float* x, uint8_t* codes, long long n, hipSt
 hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream);
 hipError_t launch_kivi_split(const KiviSplitParams& p, int grid, size_t lds_bytes,
                              hipStream_t stream);
-hipError_t kivi_split_occupancy(int group, size_t lds_bytes, int* blocks_per_cu);
+hipError_t kivi_split_occupancy(int bits, int group, size_t lds_bytes, int* blocks_per_cu);
 
 }  // namespace kvq

@@ -123,7 +123,7 @@ def _scaled_bf16(x: torch.Tensor, sigma: float, outl: Optional[List[int]], outl_
 @dataclass
 class Workload:
     name: str
-    dtype: str                # "fp8" (E4M3) | "e5m2" | "int8" | "kivi4"
+    dtype: str                # "fp8" (E4M3) | "e5m2" | "int8" | "kivi4" | "kivi2"
     batch: int
     num_q_heads: int
     num_kv_heads: int
@@ -148,6 +148,11 @@ class Workload:
     @property
     def group_size(self) -> int:
         return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def kivi_bits(self) -> int:
+        """Code width of a KIVI workload (0 for the others)."""
+        return {"kivi4": 4, "kivi2": 2}.get(self.dtype, 0)
 
 
 WORKLOADS = {
@@ -178,6 +183,10 @@ WORKLOADS = {
     "kivi": Workload("kivi", "kivi4", 4, 64, 8, 128, 32, 131072, seed=5,
                      description="KIVI-style 4-bit: 64 q / 8 kv heads, d128, batch 4, context 131072; K per-channel "
                                  "INT4 in 32-token groups, V per-token INT4, last 128 tokens fp16"),
+    "kivi2": Workload("kivi2", "kivi2", 4, 64, 8, 128, 32, 131072, seed=5,
+                      description="KIVI-style 2-bit (KIVI's own setting): the kivi workload's inputs and shapes "
+                                  "(64 q / 8 kv heads, d128, batch 4, context 131072), K per-channel INT2 in "
+                                  "32-token groups, V per-token INT2, last 128 tokens fp16"),
 }
 
 

@@ -154,7 +154,8 @@ def build_kivi(w: synthetic.Workload, lens: Optional[np.ndarray] = None, plan=No
     lens = synthetic.seq_lens(w) if lens is None else np.asarray(lens, dtype=np.int64)
     B = len(lens)
     layout = synthetic.page_layout(w, lens, w.page_size, shuffle)
-    cache = kvq.Cache(kvq.KVQ_INT4_KIVI, max(1, layout.num_pages), w.num_kv_heads, w.page_size, w.head_dim,
+    dtype = kvq.KVQ_INT2_KIVI if w.kivi_bits == 2 else kvq.KVQ_INT4_KIVI
+    cache = kvq.Cache(dtype, max(1, layout.num_pages), w.num_kv_heads, w.page_size, w.head_dim,
                       kvq.KVQ_SCALE_PER_TOKEN_HEAD, device=device, fill=fill, max_seqs=B, residual=w.resid)
     bt = torch.from_numpy(layout.block_table).to(device)
     plan = kivi_plan(lens) if plan is None else plan
@@ -190,7 +191,7 @@ def kivi_oracle_seq(bt: BuiltKivi, b: int, softmax_scale=None):
     k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
     k16 = O.bf16_to_f16_bits(u16(k))          # [T][n_kv][d]
     v16 = O.bf16_to_f16_bits(u16(v))
-    heads = [O.kivi_stream(k16[:, h], v16[:, h], w.resid, w.page_size) for h in range(w.num_kv_heads)]
+    heads = [O.kivi_stream(k16[:, h], v16[:, h], w.resid, w.page_size, w.kivi_bits) for h in range(w.num_kv_heads)]
     kd = np.zeros((T, w.num_kv_heads, w.head_dim))
     vd = np.zeros((T, w.num_kv_heads, w.head_dim))
     for h, st in enumerate(heads):
@@ -217,18 +218,26 @@ def kivi_read_seq(bt: BuiltKivi, b: int):
     rows = np.arange(nq, T) % W
     kwin = bt.cache.k_window[b].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)[:, rows]
     vwin = bt.cache.v_window[b].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)[:, rows]
+    bits = w.kivi_bits
     res = []
     for h in range(w.num_kv_heads):
         def unpack(rec, pairs=False):
-            packed = rec[:, h, :ps * d // 2]
+            """Documented record layout -> [npg * ps][d] codes.  4 bits: row t
+            holds token t, low nibble = even channel (V: token pairs interleaved
+            in 16-bit units).  2 bits: the 4-bit layout of the first ps / 2
+            tokens in bits 0-1 of each nibble and of the last ps / 2 in bits 2-3."""
+            nrow = ps if bits == 4 else ps // 2
+            packed = rec[:, h, :nrow * d // 2]
             if pairs:   # V: the rows of a token pair interleaved in 16-bit units
-                packed = packed.reshape(npg, ps // 2, d // 4, 2, 2).transpose(0, 1, 3, 2, 4)
-            packed = packed.reshape(npg * ps, d // 2)
-            codes = np.empty((npg * ps, d), dtype=np.uint8)
-            codes[:, 0::2] = packed & 0x0F
-            codes[:, 1::2] = packed >> 4
-            return codes
-        off = ps * d // 2
+                packed = packed.reshape(npg, nrow // 2, d // 4, 2, 2).transpose(0, 1, 3, 2, 4)
+            packed = packed.reshape(npg, nrow, d // 2)
+            nib = np.empty((npg, nrow, d), dtype=np.uint8)
+            nib[:, :, 0::2] = packed & 0x0F
+            nib[:, :, 1::2] = packed >> 4
+            if bits == 2:
+                nib = np.concatenate([nib & 0x3, nib >> 2], axis=1)
+            return nib.reshape(npg * ps, d)
+        off = ps * d * bits // 8
         k_s = krec[:, h, off:off + 2 * d].copy().view(np.uint16)
         k_z = krec[:, h, off + 2 * d:off + 4 * d].copy().view(np.uint16)
         v_s = vrec[:, h, off:off + 2 * ps].copy().view(np.uint16).reshape(-1)

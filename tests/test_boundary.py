@@ -46,6 +46,10 @@ def test_record_bytes(L):
     assert kvq.record_bytes(F, TH, 32, 128, 0) == 4096 + 64
     assert kvq.record_bytes(K, TH, 32, 128, 0) == 2048 + 256 + 256 == 2560
     assert kvq.record_bytes(K, TH, 32, 128, 1) == 2048 + 64 + 64 == 2176
+    K2 = kvq.KVQ_INT2_KIVI
+    assert kvq.record_bytes(K2, TH, 32, 128, 0) == 1024 + 256 + 256 == 1536
+    assert kvq.record_bytes(K2, TH, 32, 128, 1) == 1024 + 64 + 64 == 1152
+    assert kvq.record_bytes(K2, PT, 32, 128, 0) == 0
     assert kvq.record_bytes(I, PT, 16, 128, 0) == 0
     assert kvq.record_bytes(9, TH, 16, 128, 0) == 0
     # FP8 per-(token,head) costs 130/256 of bf16 storage, INT8 132/256
@@ -120,16 +124,17 @@ def _kivi_append(L, desc, num_seqs=2, max_new=8, maxp=4, k=FAKE, offs=FAKE, lens
                              num_seqs, max_new, None)
 
 
-def test_kivi_validation(L):
-    d = _kivi_desc()
+@pytest.mark.parametrize("dtype", [3, 5])
+def test_kivi_validation(L, dtype):
+    d = _kivi_desc(dtype=dtype)
     assert _kivi_append(L, None) == INVALID
     assert _kivi_append(L, _desc()) == UNSUPPORTED                        # FP8 cache: use kvq_append
     assert _kivi_append(L, _desc(num_pages=0)) == INVALID
-    assert _kivi_append(L, _kivi_desc(page_size=16)) == UNSUPPORTED       # group = page = 32 tokens
-    assert _kivi_append(L, _kivi_desc(scale_mode=0)) == UNSUPPORTED
-    assert _kivi_append(L, _kivi_desc(k_window=None)) == INVALID
-    assert _kivi_append(L, _kivi_desc(window_tokens=159)) == INVALID      # ring must hold residual + 32
-    assert _kivi_append(L, _kivi_desc(residual=-1)) == INVALID
+    assert _kivi_append(L, _kivi_desc(dtype=dtype, page_size=16)) == UNSUPPORTED       # group = page = 32 tokens
+    assert _kivi_append(L, _kivi_desc(dtype=dtype, scale_mode=0)) == UNSUPPORTED
+    assert _kivi_append(L, _kivi_desc(dtype=dtype, k_window=None)) == INVALID
+    assert _kivi_append(L, _kivi_desc(dtype=dtype, window_tokens=159)) == INVALID      # ring must hold residual + 32
+    assert _kivi_append(L, _kivi_desc(dtype=dtype, residual=-1)) == INVALID
     assert _kivi_append(L, d, num_seqs=5) == INVALID                      # beyond the window slots
     assert _kivi_append(L, d, num_seqs=-1) == INVALID
     assert _kivi_append(L, d, max_new=-1) == INVALID
@@ -141,7 +146,7 @@ def test_kivi_validation(L):
     # decode on a KIVI cache: same checks as FP8 / INT8 plus the window slots
     assert _decode(L, d, num_seqs=5, hq=16, maxp=4, max_ctx=128) == INVALID
     assert _decode(L, d, hq=16, maxp=1, max_ctx=64) == INVALID            # 2 pages of 32 needed
-    assert _decode(L, _kivi_desc(v_window=None), hq=16, maxp=4, max_ctx=128) == INVALID
+    assert _decode(L, _kivi_desc(dtype=dtype, v_window=None), hq=16, maxp=4, max_ctx=128) == INVALID
     assert _decode(L, d, num_seqs=0, hq=16, maxp=4, max_ctx=128) == OK
     assert _decode(L, d, hq=16, maxp=4, max_ctx=128, ws_bytes=0) == WORKSPACE
 
@@ -204,7 +209,8 @@ def test_e5m2_cache_and_encoder_validation(L):
     assert _verify(L, d, q_len=5) == UNSUPPORTED
     assert _append(L, _desc(dtype=4), n=-1) == INVALID
     assert _append(L, _desc(dtype=4), n=0) == OK
-    assert _append(L, _desc(dtype=5)) == INVALID                        # no such dtype
+    assert _append(L, _desc(dtype=6)) == INVALID                        # no such dtype
+    assert _append(L, _desc(dtype=5)) == UNSUPPORTED                    # INT2 KIVI: kvq_kivi_append
     assert L.kvq_e5m2_encode(FAKE, FAKE, -1, None) == INVALID
     assert L.kvq_e5m2_encode(FAKE, FAKE, 0, None) == OK
     assert L.kvq_e5m2_encode(None, FAKE, 5, None) == INVALID

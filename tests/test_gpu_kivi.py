@@ -1,10 +1,11 @@
-"""GPU parity of the KIVI-style INT4 path (kvq_kivi_append + kvq_decode_attention
-on a KVQ_INT4_KIVI cache) against the CPU oracle.
+"""GPU parity of the KIVI-style path (kvq_kivi_append + kvq_decode_attention on
+a KVQ_INT4_KIVI or KVQ_INT2_KIVI cache) against the CPU oracle.
 
-Quantized bytes (4-bit codes, per-channel K and per-token V BF16 scales and
-zero-points) and the fp16 window rows must match bit for bit; attention must
-satisfy |gpu - oracle| <= 2e-3 + 1e-2 |oracle| elementwise against fp64
-attention over the oracle's own dequantized INT4 tokens plus fp16 window.
+Quantized bytes (4-bit or 2-bit codes, per-channel K and per-token V BF16
+scales and zero-points) and the fp16 window rows must match bit for bit;
+attention must satisfy |gpu - oracle| <= 2e-3 + 1e-2 |oracle| elementwise
+against fp64 attention over the oracle's own dequantized tokens plus fp16
+window.  Every case runs at both code widths.
 """
 import sys
 
@@ -32,8 +33,11 @@ def say(*a):
     sys.stdout.flush()
 
 
-def small(**kw) -> synthetic.Workload:
-    w = synthetic.WORKLOADS["kivi"]
+BITS = pytest.mark.parametrize("bits", [4, 2])
+
+
+def small(bits=4, **kw) -> synthetic.Workload:
+    w = synthetic.WORKLOADS["kivi" if bits == 4 else "kivi2"]
     d = dict(w.__dict__)
     d.update(dict(batch=3, num_q_heads=8, num_kv_heads=2, context=1024))
     d.update(kw)
@@ -60,12 +64,13 @@ def check_out(bt, out, lse, b, ref):
     return mabs
 
 
-def test_kivi_append_and_decode_small():
+@BITS
+def test_kivi_append_and_decode_small(bits):
     """Window-only, one group, several groups; groups flushed from the window,
     from new rows and from both (bulk call, one-token steps, remainder)."""
-    w = small()
+    w = small(bits)
     lens = np.array([100, 200, 333])
-    say("kivi small build")
+    say("kivi small build", bits)
     bt = H.build_kivi(w, lens)
     out, lse = H.run_decode_kivi(bt)
     for b in range(len(lens)):
@@ -75,13 +80,14 @@ def test_kivi_append_and_decode_small():
         check_out(bt, out, lse, b, ref)
 
 
-def test_kivi_group_boundaries_one_token_at_a_time():
+@BITS
+def test_kivi_group_boundaries_one_token_at_a_time(bits):
     """Appending one token per call across the 160/192-token boundaries flushes a
     group from the window exactly when the window would exceed 128 + 31 tokens."""
-    w = small(batch=2)
+    w = small(bits, batch=2)
     lens = np.array([161, 197])
     plan = [np.array([120, 120])] + [np.array([1 if 120 + i < n else 0 for n in lens]) for i in range(80)]
-    say("kivi one-token build")
+    say("kivi one-token build", bits)
     bt = H.build_kivi(w, lens, plan=plan)
     out, lse = H.run_decode_kivi(bt)
     for b in range(2):
@@ -90,21 +96,23 @@ def test_kivi_group_boundaries_one_token_at_a_time():
         check_out(bt, out, lse, b, ref)
 
 
+@BITS
 @pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
-def test_kivi_gqa_group_sizes(G):
-    w = small(batch=2, num_q_heads=2 * G, num_kv_heads=2)
+def test_kivi_gqa_group_sizes(G, bits):
+    w = small(bits, batch=2, num_q_heads=2 * G, num_kv_heads=2)
     lens = np.array([290, 77])
-    say("kivi gqa", G)
+    say("kivi gqa", G, bits)
     bt = H.build_kivi(w, lens)
     out, lse = H.run_decode_kivi(bt)
     for b in range(2):
         check_out(bt, out, lse, b, H.kivi_oracle_seq(bt, b))
 
 
-def test_kivi_partition_sweep_and_shuffled_pages():
-    w = small(batch=4, num_q_heads=16, num_kv_heads=2)
+@BITS
+def test_kivi_partition_sweep_and_shuffled_pages(bits):
+    w = small(bits, batch=4, num_q_heads=16, num_kv_heads=2)
     lens = np.array([1000, 1, 450, 161])
-    say("kivi partitions build")
+    say("kivi partitions build", bits)
     bt = H.build_kivi(w, lens, shuffle=True)
     refs = [H.kivi_oracle_seq(bt, b) for b in range(len(lens))]
     outs = []
@@ -115,16 +123,18 @@ def test_kivi_partition_sweep_and_shuffled_pages():
             check_out(bt, out, lse, b, refs[b])
         outs.append(out.cpu())
     # V codes enter the MFMA as 128 + n and the offset is removed at the end, so
-    # fp32 rounding of the accumulator is amplified by about (128 + 7.5) / 7.5;
-    # different partitionings round differently by up to ~1e-4 (the oracle bar
-    # above is 2e-3 + 1e-2 |ref|)
+    # fp32 rounding of the accumulator is amplified by about (128 + 7.5) / 7.5
+    # (4 bits; (128 + 1.5) / 1.5 at 2 bits, with steps 5x larger); different
+    # partitionings round differently by up to ~1e-4 (the oracle bar above is
+    # 2e-3 + 1e-2 |ref|)
     for o in outs[1:]:
         assert torch.allclose(o, outs[0], atol=5e-4, rtol=1e-4)
 
 
-def test_kivi_context_length_one_is_exact():
+@BITS
+def test_kivi_context_length_one_is_exact(bits):
     """One token, still in the fp16 window: the output is its fp16 value row exactly."""
-    w = small(batch=2)
+    w = small(bits, batch=2)
     bt = H.build_kivi(w, np.array([1, 1]))
     out, lse = H.run_decode_kivi(bt)
     for b in range(2):
@@ -133,10 +143,11 @@ def test_kivi_context_length_one_is_exact():
         assert np.array_equal(out[b].cpu().numpy().astype(np.float64), vrow)
 
 
-def test_kivi_full_size():
-    """B 4, 64 q / 8 KV heads, context 131072 (130944 INT4 tokens + 128 fp16)."""
-    w = synthetic.WORKLOADS["kivi"]
-    say("kivi full build")
+@BITS
+def test_kivi_full_size(bits):
+    """B 4, 64 q / 8 KV heads, context 131072 (130944 quantized tokens + 128 fp16)."""
+    w = synthetic.WORKLOADS["kivi" if bits == 4 else "kivi2"]
+    say("kivi full build", bits)
     bt = H.build_kivi(w, plan=[synthetic.seq_lens(w) - 5, np.ones(w.batch, dtype=np.int64) * 5])
     say("kivi full decode")
     out, lse = H.run_decode_kivi(bt)
@@ -147,14 +158,15 @@ def test_kivi_full_size():
         check_out(bt, out, lse, b, ref)
 
 
-def test_kivi_decode_step_as_hip_graph_matches_eager():
+@BITS
+def test_kivi_decode_step_as_hip_graph_matches_eager(bits):
     """One-token KIVI append (re-appending each sequence's last token, which
     completes a group for the first length) and decode, captured as a HIP graph:
     every replay, with eager work in between, reproduces the eager outputs."""
     from tests.test_gpu_parity import _graph_replays_match
-    w = small(batch=2, num_q_heads=16, num_kv_heads=2)
+    w = small(bits, batch=2, num_q_heads=16, num_kv_heads=2)
     lens = np.array([160, 300])
-    say("kivi graph step build")
+    say("kivi graph step build", bits)
     bt = H.build_kivi(w, lens)
     B, Hq, d = bt.q.shape[0], bt.q.shape[1], bt.w.head_dim
     rows = [synthetic.gen_kv(w, b, int(lens[b]) - 1, 1, "cuda") for b in range(B)]
