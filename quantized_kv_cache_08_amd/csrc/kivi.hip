@@ -315,12 +315,13 @@ __device__ __forceinline__ uint32_t row_swap8(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);   // row_ror:8
 }
 
-// (w & mask) | c in one instruction: the masks stay in VGPRs so that the
-// constant c can come from an SGPR (a VOP3 instruction takes no literal here).
+// (w & mask) | c as one v_and_or_b32: the mask is held in a VGPR and c in an
+// SGPR (a VOP3 instruction takes no literal here), both opaque to the
+// compiler so that it neither rematerialises them nor splits the expression
+// into two literal-operand instructions.  Plain code, not inline assembly: the
+// compiler's hazard checks must see these writes of MFMA operands.
 __device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t vmask, uint32_t c) {
-    uint32_t o;
-    __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(o) : "v"(w), "v"(vmask), "s"(c));
-    return o;
+    return (w & vmask) | c;
 }
 
 // The same update when lanes j and j + 8 of a row share head j % 8, each
@@ -342,14 +343,15 @@ __device__ __forceinline__ void kivi_softmax_half(KiviState& st, const float (&s
 // four channels, the pair's first token in bits [0, 16), the second in
 // [16, 32), channel 4q + i in bits [4i, 4i + 4) of each half.  Channel
 // positions 0 and 2 become bf16 128 + n, positions 1 and 3 bf16 128 + 8n.
-// m0 = 0x000F000F, m1 = 0x00780078 (held in VGPRs).
+// m0 = 0x000F000F, m1 = 0x00780078 (4-bit fields; 0x00030003, 0x00180018 for
+// 2-bit codes in the low bits of the fields), held in VGPRs; c = 0x43004300
+// (bf16 128 twice) in an SGPR.
 template <int POS>
-__device__ __forceinline__ uint32_t v_pair(uint32_t w, uint32_t m0, uint32_t m1) {
-    constexpr uint32_t kC = 0x43004300u;
-    if constexpr (POS == 0) return and_or(w, m0, kC);
-    if constexpr (POS == 1) return and_or(w >> 1, m1, kC);
-    if constexpr (POS == 2) return and_or(w >> 8, m0, kC);
-    return and_or(w >> 9, m1, kC);
+__device__ __forceinline__ uint32_t v_pair(uint32_t w, uint32_t m0, uint32_t m1, uint32_t c) {
+    if constexpr (POS == 0) return and_or(w, m0, c);
+    if constexpr (POS == 1) return and_or(w >> 1, m1, c);
+    if constexpr (POS == 2) return and_or(w >> 8, m0, c);
+    return and_or(w >> 9, m1, c);
 }
 
 // SHARE (query group <= 8): lanes j and j + 8 hold the same head and each
@@ -417,9 +419,10 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     const uint32_t neg_lo = opaque_sgpr(0x0000BF80u), neg_hi = opaque_sgpr(0xBF800000u);   // bf16 (-1, 0), (0, -1)
     // V code masks, opaque to the compiler so that they stay in two VGPRs
     // instead of being rematerialised before every and_or
-    uint32_t vm0 = 0x000F000Fu, vm1 = 0x00780078u;
+    uint32_t vm0 = BITS == 4 ? 0x000F000Fu : 0x00030003u, vm1 = BITS == 4 ? 0x00780078u : 0x00180018u;
     __asm__("" : "+v"(vm0));
     __asm__("" : "+v"(vm1));
+    const uint32_t vc128 = opaque_sgpr(0x43004300u);          // bf16 (128, 128)
 
     const int off_kc = j * (kHeadDim / 2) + 16 * g;
     const int off_vc = (2 * g) * (2 * kHeadDim / 2) + 8 * j;
@@ -635,22 +638,14 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
             for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
                 for (int rp = 0; rp < 2; ++rp) {
+                    // 2 bits: the token half hp sits in bits 2 hp of each 4-bit field
+                    const uint32_t w = BITS == 4 ? pd.vc[hp][rp][t >> 2] : pd.vc[0][rp][t >> 2] >> (2 * hp);
                     uint32_t o;
-                    if constexpr (BITS == 4) {
-                        const uint32_t w = pd.vc[hp][rp][t >> 2];
-                        switch (t & 3) {
-                            case 0: o = v_pair<0>(w, vm0, vm1); break;
-                            case 1: o = v_pair<1>(w, vm0, vm1); break;
-                            case 2: o = v_pair<2>(w, vm0, vm1); break;
-                            default: o = v_pair<3>(w, vm0, vm1); break;
-                        }
-                    } else {
-                        // the same operand words from the 2-bit fields (bits 2 hp of
-                        // each 4-bit field), in plain code: the inline-assembly form
-                        // gave wrong first-channel products at this width
-                        constexpr uint32_t kSh[4] = {0, 1, 8, 9};
-                        const uint32_t w = pd.vc[0][rp][t >> 2] >> (2 * hp + kSh[t & 3]);
-                        o = (w & ((t & 1) ? 0x00180018u : 0x00030003u)) | 0x43004300u;
+                    switch (t & 3) {
+                        case 0: o = v_pair<0>(w, vm0, vm1, vc128); break;
+                        case 1: o = v_pair<1>(w, vm0, vm1, vc128); break;
+                        case 2: o = v_pair<2>(w, vm0, vm1, vc128); break;
+                        default: o = v_pair<3>(w, vm0, vm1, vc128); break;
                     }
                     bv[2 * hp + rp] = o;
                 }
