@@ -262,15 +262,28 @@ def kv_bytes(layers, n_kv_heads, head_dim, seq_len, batch, bytes_per_elem) -> fl
 
 
 # ---------------------------------------------------------------- one decode step
+def fp8_query(q_bf16) -> np.ndarray:
+    """FP8-domain attention's query: every query row (one position and head,
+    [..., d] bf16 bits) quantized to E4M3 by the per-(token, head) rule the K
+    rows use (scale = BF16 ceiling of amax / 448, codes of q / scale), returned
+    dequantized in fp64.  Some backends compute attention itself in FP8
+    ("FP8 KV Cache부터 INT4 Weight-Only까지", core concept 3); the query
+    quantizer is the pages' per-token FP8 rule applied to q (a reading: the
+    pages give no query rule)."""
+    c, s, _ = quantize_rows(FP8, PER_TOKEN_HEAD, q_bf16)
+    return dequantize_rows(FP8, c, s)
+
+
 def decode_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD,
-                     static_kv=None, softmax_scale: Optional[float] = None):
+                     static_kv=None, softmax_scale: Optional[float] = None, q8: bool = False):
     """Reference for one sequence.
 
     q_bf16 [Hq][d], k_bf16 / v_bf16 [T][n_kv][d] (bf16 bits).  ``static_kv`` =
     (k_scale, v_scale) bf16 bits broadcastable to [n_kv] for static modes.
+    q8: FP8-domain QK, i.e. attention of fp8_query(q) instead of q.
     Returns dict: K/V codes, scales, zeros, and fp64 out [Hq][d], lse [Hq].
     """
-    q = bf16_value(q_bf16).astype(np.float64)
+    q = fp8_query(q_bf16) if q8 else bf16_value(q_bf16).astype(np.float64)
     d = q.shape[-1]
     scale = (1.0 / np.sqrt(d)) if softmax_scale is None else softmax_scale
     res = quantized_cache(k_bf16, v_bf16, dtype, mode, static_kv)
@@ -300,7 +313,7 @@ def quantized_cache(k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD, stat
 
 # ---------------------------------------------------------------- verification step
 def verify_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD,
-                     static_kv=None, softmax_scale: Optional[float] = None):
+                     static_kv=None, softmax_scale: Optional[float] = None, q8: bool = False):
     """Reference for one sequence in a speculative-decoding verification pass.
 
     The target model scores the K+1 newest positions of the sequence in one
@@ -310,10 +323,11 @@ def verify_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_H
     those positions, whose own K/V rows are the last n_new of k_bf16 / v_bf16
     [T][n_kv][d].  Position i (0 = oldest of the new ones) attends causally:
     to cache positions t < T - n_new + 1 + i.  A position that sees no token
-    (T < n_new) gets out = 0 and lse = -inf.  Returns the dict of
-    quantized_cache plus fp64 out [n_new][Hq][d] and lse [n_new][Hq].
+    (T < n_new) gets out = 0 and lse = -inf.  q8: FP8-domain QK (fp8_query).
+    Returns the dict of quantized_cache plus fp64 out [n_new][Hq][d] and lse
+    [n_new][Hq].
     """
-    q = bf16_value(q_bf16).astype(np.float64)
+    q = fp8_query(q_bf16) if q8 else bf16_value(q_bf16).astype(np.float64)
     n_new, Hq, d = q.shape
     scale = (1.0 / np.sqrt(d)) if softmax_scale is None else softmax_scale
     res = quantized_cache(k_bf16, v_bf16, dtype, mode, static_kv)

@@ -106,13 +106,16 @@ def read_seq(bt: Built, b: int, which: int, dtype: int, mode: int):
 
 
 def oracle_seq(bt: Built, b: int, mode: int = kvq.KVQ_SCALE_PER_TOKEN_HEAD, static_kv=None,
-               softmax_scale=None) -> Dict[str, np.ndarray]:
-    """Oracle result for sequence b from the same seeded inputs (generated on the CPU)."""
+               softmax_scale=None, q8: Optional[bool] = None) -> Dict[str, np.ndarray]:
+    """Oracle result for sequence b from the same seeded inputs (generated on the CPU).
+    q8 (default: the cache's KVQ_ATTN_FP8_QK flag): FP8-domain QK reference."""
     w = bt.w
     T = int(bt.lens[b])
     k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
     q = synthetic.gen_q(w, "cpu", batch=len(bt.lens))[b]
-    return O.decode_reference(u16(q), u16(k), u16(v), oracle_dtype(w), mode, static_kv, softmax_scale)
+    if q8 is None:
+        q8 = bool(bt.cache.attn_flags & kvq.KVQ_ATTN_FP8_QK)
+    return O.decode_reference(u16(q), u16(k), u16(v), oracle_dtype(w), mode, static_kv, softmax_scale, q8)
 
 
 def allclose_report(got: np.ndarray, ref: np.ndarray, atol=2e-3, rtol=1e-2):

@@ -596,3 +596,56 @@ def test_e5m2_quantizer_bounds(oracle):
                                     static_scale=_bf16(np.array([1.0], np.float32))[0])
     assert list(cs[0]) == [oracle.e5m2_encode(np.array([1e4], np.float32))[0], 0xFB,
                            oracle.e5m2_encode(np.array([0.5], np.float32))[0]]
+
+
+# ----------------------------------------------------------------- FP8-domain QK (query in E4M3)
+def _torch_fp8_query(q: torch.Tensor) -> torch.Tensor:
+    """The per-row E4M3 rule through torch's own casts: scale = smallest bf16
+    >= amax / 448 (float32 division), codes = float8_e4m3fn cast of q / scale."""
+    qf = q.float()
+    s32 = qf.abs().amax(dim=-1, keepdim=True) / 448.0
+    sb = s32.to(torch.bfloat16)
+    up = (sb.view(torch.int16) + 1).view(torch.bfloat16)          # next bf16 above (positive values)
+    sb = torch.where(sb.float() < s32, up, sb).float()
+    codes = torch.where(sb > 0, qf / torch.where(sb > 0, sb, torch.ones_like(sb)), torch.zeros_like(qf))
+    return codes.to(torch.float8_e4m3fn).double() * sb.double()
+
+
+def test_fp8_query_matches_torch_casts(oracle):
+    g = torch.Generator().manual_seed(21)
+    q = (torch.randn(64, 128, generator=g) * torch.logspace(-3, 2, 64)[:, None]).to(torch.bfloat16)
+    q[3] = 0.0                                                      # zero row: scale 0, q^ = 0
+    qb = q.view(torch.int16).numpy().view(np.uint16)
+    got = oracle.fp8_query(qb)
+    assert np.array_equal(got, _torch_fp8_query(q).numpy())
+    assert not got[3].any()
+    qf = q.double().numpy()
+    s = np.abs(qf).max(axis=1, keepdims=True) / 448.0
+    # half an E4M3 step: 2^-4 relative for normals, 2^-10 of the scale below 2^-6 s (scale <= 2^-7 above s)
+    assert np.all(np.abs(got - qf) <= np.maximum(2.0**-4 * np.abs(qf), 2.0**-10 * s * (1 + 2.0**-7)) + 1e-30)
+
+
+def test_fp8_domain_reference_exact_for_representable_query(oracle):
+    """A query already on the E4M3 grid of its own scale (one element at code
+    0x7E = 448) quantizes to itself: the FP8-domain reference equals the plain one."""
+    rng = np.random.default_rng(22)
+    Hq, n_kv, T, d = 8, 2, 40, 128
+    table = oracle.e4m3_table()
+    finite = np.array([c for c in range(256) if np.isfinite(table[c])])
+    codes = rng.choice(finite, size=(Hq, d))
+    codes[:, 5] = 0x7E
+    s = 2.0 ** rng.integers(-8, 0, size=(Hq, 1))
+    q = torch.from_numpy(table[codes] * s).to(torch.bfloat16)
+    assert np.array_equal(q.double().numpy(), table[codes] * s)     # exact in bf16
+    qb = q.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.fp8_query(qb), table[codes] * s)
+    k = torch.randn(T, n_kv, d).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    v = torch.randn(T, n_kv, d).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    a = oracle.decode_reference(qb, k, v, oracle.FP8)
+    b = oracle.decode_reference(qb, k, v, oracle.FP8, q8=True)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])
+    # an arbitrary bf16 query is not on the grid: the two references differ
+    q2 = torch.randn(Hq, d).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    c = oracle.decode_reference(q2, k, v, oracle.FP8)
+    e = oracle.decode_reference(q2, k, v, oracle.FP8, q8=True)
+    assert np.abs(c["out"] - e["out"]).max() > 1e-4
