@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama8b",
-                    choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "kivi2", "verify", "e5m2", "static"])
+                    choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "kivi2", "verify", "e5m2", "static", "fp8qk"])
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto)")
     ap.add_argument("--partition-pages", type=int, default=0)
     ap.add_argument("--graph", action="store_true",
@@ -146,9 +146,9 @@ def cpu_baseline(w, budget_s: float):
     def run_oracle(qb, kb, vb):
         if not kivi:
             if QL > 1:
-                O.verify_reference(qb, kb, vb, dt, w.scale_mode, static_kv)
+                O.verify_reference(qb, kb, vb, dt, w.scale_mode, static_kv, q8=w.fp8_qk)
             else:
-                O.decode_reference(qb, kb, vb, dt, w.scale_mode, static_kv)
+                O.decode_reference(qb, kb, vb, dt, w.scale_mode, static_kv, q8=w.fp8_qk)
             return
         k16, v16 = O.bf16_to_f16_bits(kb), O.bf16_to_f16_bits(vb)
         T = kb.shape[0]
@@ -266,7 +266,8 @@ def main():
         else:
             code = {"fp8": kvq.KVQ_FP8_E4M3, "e5m2": kvq.KVQ_FP8_E5M2, "int8": kvq.KVQ_INT8_ASYM}[w.dtype]
             ss = synthetic.static_scales(w).cuda() if w.scale_mode != 2 else None
-            cache = kvq.Cache(code, full_layout.num_pages, w.num_kv_heads, w.page_size, d, w.scale_mode, ss)
+            cache = kvq.Cache(code, full_layout.num_pages, w.num_kv_heads, w.page_size, d, w.scale_mode, ss,
+                              attn_flags=kvq.KVQ_ATTN_FP8_QK if w.fp8_qk else 0)
             for b, n in enumerate(lens):
                 m = int(n) - QL
                 for p0 in range(0, m, 1 << 16):
@@ -410,6 +411,7 @@ def main():
                    "context_tokens": by["tokens"], "max_context": max_ctx, "cache_replicas": reps,
                    "partition_pages": args.partition_pages or "auto", "positions_per_seq": QL,
                    "scale_mode": {2: "per_token_head", 1: "static_per_head", 0: "static_per_tensor"}[w.scale_mode],
+                   "qk": "fp8_domain (query in E4M3)" if w.fp8_qk else "bf16 query",
                    "step_launch": "hip_graph" if args.graph else "eager"},
         "tokens_per_s": round(B * QL / (ms_step * 1e-3), 1),
         "decode_attention_kv_gbs": round(kv_gbs, 2),

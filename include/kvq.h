@@ -92,6 +92,19 @@ typedef enum kvq_dtype {
     KVQ_INT2_KIVI = 5         /* 2-bit codes, otherwise as KVQ_INT4_KIVI                  */
 } kvq_dtype;
 
+/* Attention options of a cache (kvq_cache.attn_flags). */
+typedef enum kvq_attn_flag {
+    /* FP8-domain QK (FP8 E4M3 / E5M2 caches): the query row is quantized to
+     * E4M3 with the K rows' own rule (s_q = bf16_ceil(amax(q) / 448), codes
+     * e4m3_rne_sat(q / s_q)) and QK runs on the FP8 matrix cores:
+     *   score_t = softmax_scale * s_q * s_k[t] * (q codes . k codes),
+     * i.e. the attention of the dequantized query q^ = s_q * e4m3(q codes)
+     * over the cache.  Softmax and PV keep their precision.  Some backends
+     * compute attention in FP8 ("FP8 KV Cache부터 INT4 Weight-Only까지",
+     * daewooki.github.io, core concept 3).  Not for INT8 or KIVI caches. */
+    KVQ_ATTN_FP8_QK = 1
+} kvq_attn_flag;
+
 typedef enum kvq_scale_mode {
     KVQ_SCALE_PER_TENSOR = 0,      /* one static bf16 scale for K and one for V (FP8 only) */
     KVQ_SCALE_PER_HEAD = 1,        /* one static bf16 scale per KV head for K and V (FP8)  */
@@ -117,7 +130,8 @@ typedef struct kvq_cache {
     int32_t max_seqs;         /* rows of the window arrays                               */
     int32_t window_tokens;    /* residual + page_size (160 for residual 128, group 32)   */
     int32_t residual;         /* tokens always kept in fp16 (128)                        */
-    int32_t reserved;
+    int32_t attn_flags;       /* kvq_attn_flag bits read by the decode / verify entry
+                                 points (0: query in bf16); the append calls ignore it */
 } kvq_cache;
 
 /* Bytes of one page record: which = 0 for K, 1 for V.  0 for an invalid combination. */

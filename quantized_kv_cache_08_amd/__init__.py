@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2", "KVQ_INT2_KIVI", "KIVI_DTYPES",
+    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2", "KVQ_INT2_KIVI", "KIVI_DTYPES", "KVQ_ATTN_FP8_QK",
     "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
     "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
     "verify_workspace_bytes", "verify_attention", "verify_split", "verify_reduce",
@@ -25,6 +25,7 @@ __all__ = [
 
 KVQ_FP8_E4M3, KVQ_INT8_ASYM, KVQ_INT4_KIVI, KVQ_FP8_E5M2, KVQ_INT2_KIVI = 1, 2, 3, 4, 5
 KIVI_DTYPES = (KVQ_INT4_KIVI, KVQ_INT2_KIVI)
+KVQ_ATTN_FP8_QK = 1          # kvq_cache.attn_flags: FP8-domain QK (query quantized to E4M3)
 KVQ_SCALE_PER_TENSOR, KVQ_SCALE_PER_HEAD, KVQ_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -39,7 +40,7 @@ class CacheDesc(ctypes.Structure):
         ("num_kv_heads", _I32), ("head_dim", _I32),
         ("k_pages", _P), ("v_pages", _P), ("static_scales", _P),
         ("k_window", _P), ("v_window", _P),
-        ("max_seqs", _I32), ("window_tokens", _I32), ("residual", _I32), ("reserved", _I32),
+        ("max_seqs", _I32), ("window_tokens", _I32), ("residual", _I32), ("attn_flags", _I32),
     ]
 
 
@@ -124,7 +125,7 @@ class Cache:
     def __init__(self, dtype: int, num_pages: int, num_kv_heads: int, page_size: int = 16,
                  head_dim: int = 128, scale_mode: int = KVQ_SCALE_PER_TOKEN_HEAD,
                  static_scales: Optional[torch.Tensor] = None, device="cuda", fill: Optional[int] = None,
-                 max_seqs: int = 0, residual: int = 128):
+                 max_seqs: int = 0, residual: int = 128, attn_flags: int = 0):
         self.dtype, self.scale_mode = dtype, scale_mode
         self.num_pages, self.num_kv_heads = num_pages, num_kv_heads
         self.page_size, self.head_dim = page_size, head_dim
@@ -149,7 +150,16 @@ class Cache:
                               None if static_scales is None else static_scales.data_ptr(),
                               None if self.k_window is None else self.k_window.data_ptr(),
                               None if self.v_window is None else self.v_window.data_ptr(),
-                              max_seqs, self.window_tokens, residual, 0)
+                              max_seqs, self.window_tokens, residual, attn_flags)
+
+    @property
+    def attn_flags(self) -> int:
+        return int(self.desc.attn_flags)
+
+    @attn_flags.setter
+    def attn_flags(self, flags: int) -> None:
+        """kvq_attn_flag bits for the decode / verify calls (KVQ_ATTN_FP8_QK)."""
+        self.desc.attn_flags = int(flags)
 
     def records(self, which: int) -> torch.Tensor:
         """Pool ``which`` (0 = K, 1 = V) viewed as [num_pages][num_kv_heads][record bytes]."""

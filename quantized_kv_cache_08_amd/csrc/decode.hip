@@ -37,6 +37,18 @@
 //      tokens 4g..4g+3 of each half); V is loaded as 8-byte row pieces
 //      (lane (chan-block j, g): channels 8j..8j+7 of tokens 4g..4g+3) and
 //      transposed in registers with byte permutes before conversion.
+//
+// FP8-domain QK (Q8; the cache descriptor's KVQ_ATTN_FP8_QK flag): some
+// serving backends compute attention itself in FP8 ("FP8 KV Cache부터 INT4
+// Weight-Only까지", daewooki.github.io, core concept 3).  Here the query row is
+// quantized at segment start with the K rows' own rule (s_q = bf16 ceil of
+// amax / 448, E4M3 codes of q / s_q, nearest-even) and QK runs on the gfx950
+// FP8 MFMA 16x16x128 straight from the loaded K codes (E4M3, or E5M2 as BF8),
+// one instruction per 16 tokens with no code conversion; the product of two
+// FP8 values is exact in fp32.  The score is s_k s_q (codes . codes).  P and
+// PV are unchanged (P' in bf16 hi + lo): E4M3 probabilities, 3 mantissa bits,
+// would move outputs far past the 2e-3 bar, and their codes would depend on
+// this kernel's running maximum, which no plain definition fixes.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "splitk.h"
@@ -55,7 +67,20 @@ struct ChunkBuf {
     u32x2_t vz[2];
 };
 
-template <int DT, bool STATIC, int PS>
+// FP8 MFMA 16x16x128: A = 32 FP8 bytes of row l % 16 (format A_FMT: 0 E4M3,
+// 1 E5M2), B = 32 E4M3 bytes of column l % 16, the same channels in the same
+// byte order on both sides; unit block scales (E8M0 127 = 2^0).
+template <int A_FMT>
+__device__ __forceinline__ f32x4_t mfma_16x16x128_fp8(const u32x4_t (&a)[2], const uint32_t (&b)[8]) {
+    typedef int i32x8_t __attribute__((ext_vector_type(8)));
+    const i32x8_t av = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3],
+                        (int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
+    const i32x8_t bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], (int)b[4], (int)b[5], (int)b[6], (int)b[7]};
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, A_FMT, 0, 0, 127, 0, 127);
+}
+
+template <int DT, bool STATIC, int PS, bool Q8>
 __device__ __forceinline__ void process_segment(const SplitParams& p, const int b, const int h,
                                                 const int page0, const int page1, const int seg,
                                                 const int n_seg, const int lane) {
@@ -96,9 +121,37 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
         qsum += __shfl_xor(qsum, 32);
     }
 
+    // ---- FP8-domain QK: row j quantized like a K row; byte i of the lane's
+    // 32 codes is channel 32g + i (qb[kb] holds channels 32g + 8kb + [0, 8))
+    uint32_t qc[8];
+    float q_scale = 1.0f;
+    if constexpr (Q8) {
+#pragma clang fp contract(off)
+        float amax = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                amax = fmaxf(amax, fmaxf(fabsf(bf16lo(qb[kb][i])), fabsf(bf16hi(qb[kb][i]))));
+        amax = max_over_groups(amax);
+        q_scale = bf16lo(bf16_up_bits(amax / 448.0f));
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+                const uint32_t w0 = qb[kb][2 * i2], w1 = qb[kb][2 * i2 + 1];
+                qc[2 * kb + i2] = q_scale != 0.0f
+                                      ? e4m3_encode4(bf16lo(w0) / q_scale, bf16hi(w0) / q_scale,
+                                                     bf16lo(w1) / q_scale, bf16hi(w1) / q_scale)
+                                      : 0u;
+            }
+    }
+
+    // the query scale (1 unless Q8) multiplies the softmax scale
+    const float score_scale = p.score_scale * q_scale;
     float k_static = 0.0f, v_static = 0.0f;
     if constexpr (STATIC) {
-        k_static = bf16lo(p.static_scales[h * p.static_head_stride]) * p.score_scale;
+        k_static = bf16lo(p.static_scales[h * p.static_head_stride]) * score_scale;
         v_static = bf16lo(p.static_scales[p.static_kv_stride + h * p.static_head_stride]);
     }
 
@@ -184,6 +237,9 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
 #pragma unroll
         for (int hp = 0; hp < 2; ++hp) {
             f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (Q8) {
+                d = mfma_16x16x128_fp8<DT == kE5M2 ? 1 : 0>(cb.k[hp], qc);
+            } else {
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const u32x4_t src = cb.k[hp][kb >> 1];
@@ -201,6 +257,7 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
                 }
                 d = mfma_16x16x32_bf16(a, qb[kb], d);
             }
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 float s;
@@ -214,7 +271,7 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
                         const float kzr = (r & 1) ? bf16hi(zw) : bf16lo(zw);
                         s = (d[r] * ksr + kzr * qsum) * p.score_scale;
                     } else {
-                        s = d[r] * (ksr * p.score_scale);
+                        s = d[r] * (ksr * score_scale);
                     }
                 }
                 sc[hp][r] = s;
@@ -418,10 +475,10 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
     }
 }
 
-template <int DT, bool STATIC, int PS>
+template <int DT, bool STATIC, int PS, bool Q8>
 __global__ __launch_bounds__(256) void split_kernel(SplitParams p) {
     for_each_segment<PS>(p, [&](int b, int h, int page0, int page1, int seg, int n_seg, int lane) {
-        process_segment<DT, STATIC, PS>(p, b, h, page0, page1, seg, n_seg, lane);
+        process_segment<DT, STATIC, PS, Q8>(p, b, h, page0, page1, seg, n_seg, lane);
     });
 }
 
@@ -458,34 +515,37 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
 }
 
 template <int DT, bool STATIC, int PS>
-static const void* split_fn() {
-    return (const void*)&split_kernel<DT, STATIC, PS>;
+static const void* split_fn(bool q8) {
+    return q8 ? (const void*)&split_kernel<DT, STATIC, PS, true> : (const void*)&split_kernel<DT, STATIC, PS, false>;
 }
 
-static const void* pick_split(int dtype, bool static_scale, int page_size) {
-    if (dtype == kFP8) {
-        if (static_scale) return page_size == 16 ? split_fn<kFP8, true, 16>() : split_fn<kFP8, true, 32>();
-        return page_size == 16 ? split_fn<kFP8, false, 16>() : split_fn<kFP8, false, 32>();
-    }
-    if (dtype == kE5M2) {
-        if (static_scale) return page_size == 16 ? split_fn<kE5M2, true, 16>() : split_fn<kE5M2, true, 32>();
-        return page_size == 16 ? split_fn<kE5M2, false, 16>() : split_fn<kE5M2, false, 32>();
-    }
-    return page_size == 16 ? split_fn<kINT8, false, 16>() : split_fn<kINT8, false, 32>();
+template <int DT>
+static const void* pick_fp8(bool static_scale, int page_size, bool q8) {
+    if (static_scale) return page_size == 16 ? split_fn<DT, true, 16>(q8) : split_fn<DT, true, 32>(q8);
+    return page_size == 16 ? split_fn<DT, false, 16>(q8) : split_fn<DT, false, 32>(q8);
 }
 
-hipError_t split_occupancy(int dtype, bool static_scale, int page_size, size_t lds_bytes,
+// q8 (FP8-domain QK) exists for the FP8 formats only; the host refuses it
+// for INT8 caches.
+static const void* pick_split(int dtype, bool static_scale, int page_size, bool q8) {
+    if (dtype == kFP8) return pick_fp8<kFP8>(static_scale, page_size, q8);
+    if (dtype == kE5M2) return pick_fp8<kE5M2>(static_scale, page_size, q8);
+    return page_size == 16 ? (const void*)&split_kernel<kINT8, false, 16, false>
+                           : (const void*)&split_kernel<kINT8, false, 32, false>;
+}
+
+hipError_t split_occupancy(int dtype, bool static_scale, int page_size, bool q8, size_t lds_bytes,
                            int* blocks_per_cu) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, pick_split(dtype, static_scale, page_size), kSplitThreads, lds_bytes);
+        blocks_per_cu, pick_split(dtype, static_scale, page_size, q8), kSplitThreads, lds_bytes);
 }
 
-hipError_t launch_split(int dtype, bool static_scale, int page_size, const SplitParams& p, int grid,
+hipError_t launch_split(int dtype, bool static_scale, int page_size, bool q8, const SplitParams& p, int grid,
                         size_t lds_bytes, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     SplitParams args = p;
     void* kargs[] = {&args};
-    return hipLaunchKernel(pick_split(dtype, static_scale, page_size), dim3(grid),
+    return hipLaunchKernel(pick_split(dtype, static_scale, page_size, q8), dim3(grid),
                            dim3(kSplitThreads), kargs, lds_bytes, stream);
 }
 

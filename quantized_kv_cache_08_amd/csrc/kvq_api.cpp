@@ -115,6 +115,9 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
         partition_pages < 0 || q_len < 1)
         return KVQ_ERR_INVALID;
     if (num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID;
+    if (c->attn_flags & ~KVQ_ATTN_FP8_QK) return KVQ_ERR_INVALID;
+    if ((c->attn_flags & KVQ_ATTN_FP8_QK) && c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2)
+        return KVQ_ERR_UNSUPPORTED;
     if (!valid_group(num_q_heads / c->num_kv_heads)) return KVQ_ERR_UNSUPPORTED;
     // the query rows of one KV head (group x positions) form one 16-wide MFMA tile
     if ((long long)q_len * (num_q_heads / c->num_kv_heads) > 16) return KVQ_ERR_UNSUPPORTED;
@@ -171,8 +174,9 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     const size_t lds = ((size_t)num_seqs + 1) * sizeof(int32_t);
     const bool kivi = is_kivi(c->dtype);
     int per_cu = 0;
+    const bool q8 = (c->attn_flags & KVQ_ATTN_FP8_QK) != 0;
     hipError_t e = kivi ? kivi_split_occupancy(kivi_bits(c->dtype), p.group, lds, &per_cu)
-                        : split_occupancy(c->dtype, is_static, c->page_size, lds, &per_cu);
+                        : split_occupancy(c->dtype, is_static, c->page_size, q8, lds, &per_cu);
     if (e != hipSuccess) return KVQ_ERR_HIP;
     const int cus = device_cus();
     if (cus <= 0 || per_cu <= 0) return KVQ_ERR_HIP;
@@ -193,7 +197,7 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
         kp.bits = kivi_bits(c->dtype);
         e = launch_kivi_split(kp, grid, lds, stream);
     } else {
-        e = launch_split(c->dtype, is_static, c->page_size, p, grid, lds, stream);
+        e = launch_split(c->dtype, is_static, c->page_size, q8, p, grid, lds, stream);
     }
     return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }

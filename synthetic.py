@@ -143,6 +143,7 @@ class Workload:
     q_len: int = 1            # query positions per sequence (> 1: speculative-decoding verification)
     scale_mode: int = 2       # 2: per-(token, head) scales; 1: static per head; 0: static per tensor
     group: int = 32           # KIVI group along tokens
+    fp8_qk: bool = False      # FP8-domain QK (query quantized to E4M3, QK on the FP8 matrix cores)
     description: str = ""
 
     @property
@@ -180,6 +181,10 @@ WORKLOADS = {
                        description="Llama-3-8B-shaped decode layer in FP8 E4M3 with static per-head scales "
                                    "(from the input distribution, see static_scales): 32 q / 8 kv heads, d128, "
                                    "batch 32, context 8192, page 16"),
+    "fp8qk": Workload("fp8qk", "fp8", 32, 32, 8, 128, 16, 8192, seed=2, fp8_qk=True,
+                      description="Llama-3-8B-shaped decode layer, FP8 E4M3 cache with FP8-domain QK (the query "
+                                  "quantized per (token, head) to E4M3, QK on the FP8 MFMA): 32 q / 8 kv heads, "
+                                  "d128, batch 32, context 8192, page 16"),
     "kivi": Workload("kivi", "kivi4", 4, 64, 8, 128, 32, 131072, seed=5,
                      description="KIVI-style 4-bit: 64 q / 8 kv heads, d128, batch 4, context 131072; K per-channel "
                                  "INT4 in 32-token groups, V per-token INT4, last 128 tokens fp16"),

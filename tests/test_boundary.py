@@ -222,3 +222,25 @@ def test_encode_and_status(L):
     assert L.kvq_e4m3_encode(None, FAKE, 5, None) == INVALID
     assert kvq.status_string(0) == "ok"
     assert "workspace" in kvq.status_string(3)
+
+
+def test_attn_flags_validation(L):
+    """KVQ_ATTN_FP8_QK: FP8 E4M3 / E5M2 caches only; unknown bits are invalid;
+    the append entry points ignore the field.  (num_seqs = 0 / n = 0: the
+    checks run, nothing is launched.)"""
+    for dt in (1, 4):
+        d = _desc(dtype=dt)
+        d.attn_flags = kvq.KVQ_ATTN_FP8_QK
+        assert _decode(L, d, num_seqs=0) == OK
+        assert _verify(L, d, q_len=2, num_seqs=0) == OK
+        assert _append(L, d, n=0) == OK
+        d.attn_flags = 2
+        assert _decode(L, d, num_seqs=0) == INVALID
+        assert _verify(L, d, q_len=2, num_seqs=0) == INVALID
+    d = _desc(dtype=2)
+    d.attn_flags = kvq.KVQ_ATTN_FP8_QK
+    assert _decode(L, d, num_seqs=0) == UNSUPPORTED
+    assert _append(L, d, n=0) == OK
+    d = _kivi_desc()
+    d.attn_flags = kvq.KVQ_ATTN_FP8_QK
+    assert _decode(L, d, num_seqs=0, hq=16, maxp=4, max_ctx=128) == UNSUPPORTED

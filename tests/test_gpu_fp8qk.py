@@ -1,0 +1,183 @@
+"""GPU parity of FP8-domain QK (kvq_cache.attn_flags = KVQ_ATTN_FP8_QK): the
+query row quantized to E4M3 by the K rows' per-(token, head) rule and QK on
+the FP8 matrix cores, over E4M3 and E5M2 caches.
+
+The oracle is the same fp64 attention over the same dequantized cache with
+the query replaced by its E4M3 round trip (oracle.fp8_query); the bar is the
+decode bar, |gpu - oracle| <= 2e-3 + 1e-2 |oracle| elementwise.  Every case
+also checks that the plain bf16-query oracle is off by more than that bar
+somewhere, so the flag demonstrably changes what is computed.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from tests.conftest import gpu_available
+
+pytestmark = pytest.mark.gpu
+
+if not gpu_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import quantized_kv_cache_08_amd as kvq  # noqa: E402
+import synthetic  # noqa: E402
+from oracle import oracle as O  # noqa: E402
+from tests import kvq_harness as H  # noqa: E402
+
+ATOL, RTOL = 2e-3, 1e-2
+LSE_ATOL = 1e-3
+# The FP8 matrix-core dot product of gfx950 does not sum its 128 products in
+# full fp32: on random E4M3 tiles its result deviated from the exact sum by up
+# to 2^-13.8 of sum |products| (sequential fp32: 1.8e-7; narrow-range inputs:
+# exact).  The pages note the same of FP8 accumulation on some GPU generations
+# ("KV cache FP8로 동시 요청 76배 수용하기", sections 4-5).  Each score is one
+# such dot product (nothing accumulates across chunks), so
+# |d score_t| <= 2^-12 * scale * sum_c |q^_c k^_tc|, and lse, a soft maximum of
+# the scores, moves by at most the largest of these.
+MFMA_REL = 2.0**-12
+LENS = np.array([1, 5, 17, 96, 250, 700], dtype=np.int64)
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def workload(base: str, **kw) -> synthetic.Workload:
+    d = dict(synthetic.WORKLOADS[base].__dict__)
+    d.update(kw)
+    return synthetic.Workload(**d)
+
+
+def score_magnitude(bt: H.Built, b: int, k_hat: np.ndarray) -> np.ndarray:
+    """Per query head: softmax_scale * max_t sum_c |q^_c k^_tc| (q^ = E4M3 query)."""
+    w = bt.w
+    q = synthetic.gen_q(w, "cpu", batch=len(bt.lens))[b]
+    qh = np.abs(O.fp8_query(H.u16(q)))                               # [Hq][d]
+    kh = np.abs(k_hat)                                                # [T][n_kv][d]
+    G = w.group_size
+    mag = np.array([(kh[:, h // G, :] @ qh[h]).max() for h in range(w.num_q_heads)])
+    return mag / np.sqrt(w.head_dim)
+
+
+def check(bt: H.Built, out, lse, seqs, mode=kvq.KVQ_SCALE_PER_TOKEN_HEAD, static_kv=None):
+    """Each sequence against the FP8-domain oracle; returns the largest
+    deviation from the plain (bf16-query) oracle over the checked sequences."""
+    off = 0.0
+    for b in seqs:
+        ref = H.oracle_seq(bt, b, mode, static_kv, q8=True)
+        got = out[b].cpu().numpy()
+        ok, mabs, mrel = H.allclose_report(got, ref["out"], ATOL, RTOL)
+        assert ok, f"seq {b}: max abs {mabs:.3e} max rel {mrel:.3e}"
+        if lse is not None:
+            dl = np.abs(lse[b].cpu().numpy().astype(np.float64) - ref["lse"])
+            bar = LSE_ATOL + MFMA_REL * score_magnitude(bt, b, ref["k_hat"])
+            assert np.all(dl <= bar), f"seq {b}: lse diff {dl.max():.3e} (bar {bar[np.argmax(dl - bar)]:.3e})"
+        plain = H.oracle_seq(bt, b, mode, static_kv, q8=False)["out"]
+        off = max(off, float((np.abs(got - plain) - (ATOL + RTOL * np.abs(plain))).max()))
+    return off
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "e5m2"])
+def test_fp8qk_ragged_batch_partitions(dtype):
+    w = workload("tiny", dtype=dtype, batch=len(LENS), context=int(LENS.max()))
+    say("fp8qk ragged", dtype)
+    bt = H.build(w, lens=LENS)
+    bt.cache.attn_flags = kvq.KVQ_ATTN_FP8_QK
+    off = []
+    for part in (0, 1, 3):
+        say("  partition pages", part)
+        out, lse = H.run_decode(bt, part)
+        off.append(check(bt, out, lse, range(len(LENS))))
+    assert max(off) > 0, "FP8-domain output indistinguishable from the bf16-query oracle"
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "e5m2"])
+def test_fp8qk_groups_and_page_sizes(dtype):
+    for heads, ps in (((8, 2), 32), ((16, 2), 16), ((2, 2), 16), ((32, 2), 16)):
+        w = workload("tiny", dtype=dtype, batch=3, num_q_heads=heads[0], num_kv_heads=heads[1], page_size=ps)
+        say("fp8qk", dtype, "heads", heads, "page", ps)
+        bt = H.build(w, lens=np.array([31, 300, 64]))
+        bt.cache.attn_flags = kvq.KVQ_ATTN_FP8_QK
+        out, lse = H.run_decode(bt)
+        check(bt, out, lse, range(3))
+
+
+def test_fp8qk_static_scale_modes():
+    w = workload("tiny", batch=2)
+    lens = np.array([96, 250])
+    for mode in (kvq.KVQ_SCALE_PER_TENSOR, kvq.KVQ_SCALE_PER_HEAD):
+        if mode == kvq.KVQ_SCALE_PER_TENSOR:
+            host = np.array([0.05, 0.01], dtype=np.float32)
+            static_kv = tuple(H.u16(torch.tensor(v).to(torch.bfloat16)) for v in host)
+        else:
+            host = np.array([[0.04, 0.06], [0.009, 0.012]], dtype=np.float32)
+            static_kv = tuple(H.u16(torch.from_numpy(r).to(torch.bfloat16)) for r in host)
+        ss = torch.from_numpy(host).to(torch.bfloat16).cuda().contiguous()
+        say("fp8qk static mode", mode)
+        bt = H.build(w, lens=lens, mode=mode, static_scales=ss)
+        bt.cache.attn_flags = kvq.KVQ_ATTN_FP8_QK
+        out, lse = H.run_decode(bt)
+        check(bt, out, lse, range(2), mode=mode, static_kv=static_kv)
+
+
+def test_fp8qk_context_length_one_is_exact():
+    """One token: p = 1 whatever the scores, so out is its dequantized V row exactly."""
+    w = workload("tiny", batch=2)
+    bt = H.build(w, lens=np.array([1, 1]))
+    bt.cache.attn_flags = kvq.KVQ_ATTN_FP8_QK
+    out, _ = H.run_decode(bt)
+    for b in range(2):
+        ref = H.oracle_seq(bt, b, q8=True)
+        vrow = np.repeat(ref["v_hat"][0], w.group_size, axis=0)
+        assert np.array_equal(out[b].cpu().numpy().astype(np.float64), vrow)
+
+
+def test_fp8qk_verification_pass():
+    w = workload("tiny", batch=len(LENS), context=int(LENS.max()))
+    say("fp8qk verify")
+    bt = H.build(w, lens=LENS)
+    bt.cache.attn_flags = kvq.KVQ_ATTN_FP8_QK
+    B, q_len, Hq, d = len(LENS), 4, w.num_q_heads, w.head_dim
+    q = synthetic.gen_q(w, "cuda", batch=B * q_len).reshape(B, q_len, Hq, d)
+    ws = torch.zeros(kvq.verify_workspace_bytes(bt.cache, B, q_len, Hq, bt.max_ctx), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((B, q_len, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((B, q_len, Hq), float("nan"), device="cuda")
+    kvq.verify_attention(bt.cache, q, bt.block_table, bt.context_lens, bt.max_ctx, d ** -0.5, ws, out, lse)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qc = synthetic.gen_q(w, "cpu", batch=B * q_len).reshape(B, q_len, Hq, d)
+    for b in range(B):
+        T = int(LENS[b])
+        k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
+        ref = O.verify_reference(H.u16(qc[b]), H.u16(k), H.u16(v), O.FP8, q8=True)
+        for i in range(q_len):
+            if T - q_len + 1 + i <= 0:
+                assert not out[b, i].any() and np.all(np.isneginf(lse[b, i]))
+                continue
+            ok, mabs, mrel = H.allclose_report(out[b, i], ref["out"][i], ATOL, RTOL)
+            assert ok, f"seq {b} position {i}: max abs {mabs:.3e} max rel {mrel:.3e}"
+
+
+def test_fp8qk_mixed_small_shuffled_pool():
+    w = workload("mixed", batch=24, context=4096)
+    say("fp8qk mixed small")
+    bt = H.build(w)
+    bt.cache.attn_flags = kvq.KVQ_ATTN_FP8_QK
+    out, lse = H.run_decode(bt)
+    check(bt, out, lse, range(0, 24, 5))
+
+
+def test_fp8qk_llama8b_shape_sampled():
+    """The 8B-shaped batch (B 32, context 8192) with FP8-domain QK, in the
+    benchmark's launch configuration; three sequences checked."""
+    w = synthetic.WORKLOADS["llama8b"]
+    say("fp8qk llama8b shape")
+    bt = H.build(w)
+    bt.cache.attn_flags = kvq.KVQ_ATTN_FP8_QK
+    out, lse = H.run_decode(bt)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    check(bt, out, lse, (0, 13, w.batch - 1))
