@@ -507,7 +507,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
         return;
     }
     const int pb = cb - p.ws_header[1];
-    const long long item_start = (long long)p.ws_pfx[b] * p.n_kv + (long long)h * cb;
+    const long long item_start = p.ws_pfx[b];          // offset inside head h's weight space
     const int n_seg = (int)((item_start + pb - 1) / chunk - item_start / chunk + 1);
     if (n_seg == 1) return;   // written by the split kernel
     merge_rows<1>(p.part_lse + idx * p.max_parts, p.part_o + idx * p.max_parts * kHeadDim, p.max_parts, n_seg,
