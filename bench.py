@@ -53,11 +53,23 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash() -> str:
+# Sources each split kernel is built from: its own file plus the shared
+# headers and the host layer that sizes its launch.
+_SHARED_SRC = ("splitk.h", "kvq_device.h", "kvq_internal.h", "kvq_api.cpp")
+_KERNEL_SRC = {"decode": ("decode.hip",) + _SHARED_SRC, "kivi": ("kivi.hip", "decode.hip") + _SHARED_SRC}
+
+
+def source_hash(config: str = "llama8b") -> str:
+    """Hash of the sources of the workload's split kernel (the KIVI path also
+    launches the reduce kernel of decode.hip), so that recorded counters are
+    used only while that kernel is unchanged."""
+    import synthetic
+    kind = "kivi" if synthetic.WORKLOADS[config].kivi_bits else "decode"
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.dirname(DECODE_SRC))):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(os.path.dirname(DECODE_SRC), f), "rb").read())
+    d = os.path.dirname(DECODE_SRC)
+    for f in sorted(_KERNEL_SRC[kind]):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -207,7 +219,7 @@ def read_traffic(config: str):
         if ":" in line:
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("source_hash") != source_hash():
+    if kv.get("source_hash") != source_hash(config):
         return None
     try:
         return int(float(kv["bytes_per_launch"]))
@@ -427,7 +439,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "split_kernel (paged split-K decode attention)",
                      "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
-        "source_hash": source_hash(),
+        "source_hash": source_hash(args.config),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
