@@ -60,7 +60,9 @@
  *   zero-points;  KIVI K: head_dim bf16 scales then head_dim bf16 zero-points
  *   (one per channel for the page's 32-token group);  KIVI V: page_size bf16
  *   scales then page_size bf16 zero-points;
- *   padded to a multiple of 16 bytes.
+ *   padded to a multiple of 16 bytes, plus 32 bytes when that size is a
+ *   multiple of 1024 (static-scale FP8 records: 2048 -> 2080 at page 16), so
+ *   that a page of records is not a power-of-two stride in the pool.
  * Token t of a sequence lives in page block_table[seq][t / page_size], row
  * t % page_size.  slot = page * page_size + row.
  */

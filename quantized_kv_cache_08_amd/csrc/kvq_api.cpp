@@ -244,7 +244,14 @@ size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size, in
     } else {
         return 0;
     }
-    return (codes + meta + 15) & ~size_t(15);
+    // padded to 16 bytes; a record of a multiple of 1 KiB (static-scale FP8)
+    // gets 32 more, so that a page of records is not a power-of-two stride: the
+    // heads of one page are read together and pages of equal-length sequences
+    // in lockstep, and a 16 KiB page stride put those reads on the same HBM
+    // channels (8B shape: 109 us unpadded, 94 us padded)
+    size_t r = (codes + meta + 15) & ~size_t(15);
+    if (r % 1024 == 0) r += 32;
+    return r;
 }
 
 kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,

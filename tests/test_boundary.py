@@ -42,7 +42,9 @@ def test_record_bytes(L):
     assert kvq.record_bytes(F, TH, 16, 128, 0) == 16 * 128 + 32 == 2080
     assert kvq.record_bytes(F, TH, 16, 128, 1) == 2080
     assert kvq.record_bytes(I, TH, 16, 128, 0) == 16 * 128 + 64 == 2112
-    assert kvq.record_bytes(F, PT, 16, 128, 0) == kvq.record_bytes(F, PH, 16, 128, 1) == 2048
+    # static records: 2048 code bytes, padded by 32 off the power-of-two stride
+    assert kvq.record_bytes(F, PT, 16, 128, 0) == kvq.record_bytes(F, PH, 16, 128, 1) == 2048 + 32
+    assert kvq.record_bytes(F, PT, 32, 128, 0) == 4096 + 32
     assert kvq.record_bytes(F, TH, 32, 128, 0) == 4096 + 64
     assert kvq.record_bytes(K, TH, 32, 128, 0) == 2048 + 256 + 256 == 2560
     assert kvq.record_bytes(K, TH, 32, 128, 1) == 2048 + 64 + 64 == 2176
