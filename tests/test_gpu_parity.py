@@ -371,3 +371,24 @@ def test_full_mixed_fp8():
         order = np.argsort(bt.lens)
         return [int(order[0]), int(order[len(order) // 2]), int(order[-1]), 7]
     _full("mixed", pick)
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+def test_many_short_sequences_odd_kv_heads(dtype):
+    """2000 sequences of 0-47 tokens on 3 KV heads (group 2), shuffled pool: a
+    wave's range holds hundreds of items, and the per-head cut has 1024 / 3 =
+    341 ranges per head (not a multiple of the 32 that lines heads up on one
+    XCD).  Empty sequences give out 0 and lse -inf; a sample of the others is
+    checked against the oracle."""
+    w = small("tiny", dtype=dtype, batch=2000, num_q_heads=6, num_kv_heads=3, context=47)
+    lens = np.random.default_rng(31).integers(0, 48, size=2000)
+    lens[:3] = (0, 47, 1)
+    say("many short sequences", dtype)
+    bt = H.build(w, lens=lens, shuffle=True)
+    out, lse = H.run_decode(bt)
+    assert not torch.isnan(out).any()
+    for b in np.nonzero(lens == 0)[0][:50]:
+        assert torch.all(out[b] == 0) and torch.all(torch.isneginf(lse[b]))
+    for b in list(range(3)) + list(range(17, 2000, 97)):
+        if lens[b]:
+            check_seq(bt, out, lse, int(b))
