@@ -392,3 +392,17 @@ def test_many_short_sequences_odd_kv_heads(dtype):
     for b in list(range(3)) + list(range(17, 2000, 97)):
         if lens[b]:
             check_seq(bt, out, lse, int(b))
+
+
+@pytest.mark.parametrize("dtype,heads", [("fp8", (64, 8)), ("int8", (16, 1))])
+def test_one_long_sequence_131072(dtype, heads):
+    """One 131072-token sequence (8192 pages) next to a 1-token one: the long
+    item is cut over many waves and merged from the maximum of 32 partial
+    results per row; checked against the oracle at full length."""
+    w = small("llama70b", dtype=dtype, batch=2, num_q_heads=heads[0], num_kv_heads=heads[1], context=131072)
+    lens = np.array([131072, 1])
+    say("one long sequence", dtype, heads)
+    bt = H.build(w, lens=lens)
+    out, lse = H.run_decode(bt)
+    for b in range(2):
+        check_seq(bt, out, lse, b)
