@@ -31,6 +31,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# decoder layers of the models whose attention shape (query heads, KV heads)
+# the workloads take: Llama-3-8B (32 / 8, 32 layers), Llama-3-70B (64 / 8, 80)
+MODEL_LAYERS = {(32, 8): 32, (64, 8): 80}
 DECODE_SRC = os.path.join(ROOT, "quantized_kv_cache_08_amd", "csrc", "decode.hip")
 
 
@@ -426,6 +429,12 @@ def main():
                    "qk": "fp8_domain (query in E4M3)" if w.fp8_qk else "bf16 query",
                    "step_launch": "hip_graph" if args.graph else "eager"},
         "tokens_per_s": round(B * QL / (ms_step * 1e-3), 1),
+        # attention-only extrapolation to a whole model of this layer's shape:
+        # every layer runs the same step, nothing else of the model is timed
+        "tokens_per_s_attention_only_model": (
+            None if not MODEL_LAYERS.get((Hq, w.num_kv_heads)) else
+            {"layers": MODEL_LAYERS[(Hq, w.num_kv_heads)],
+             "value": round(B * QL / (ms_step * 1e-3 * MODEL_LAYERS[(Hq, w.num_kv_heads)]), 1)}),
         "decode_attention_kv_gbs": round(kv_gbs, 2),
         "pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         # means: back-to-back launches; p50 / p95: single launches between events
