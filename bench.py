@@ -211,6 +211,15 @@ def cpu_baseline(w, budget_s: float):
             "tokens_per_s": round(len(done) / t_total, 4)}
 
 
+def oracle_threads(n: int) -> int:
+    """Set the oracle's OpenMP thread count; returns the previous one."""
+    import ctypes
+    gomp = ctypes.CDLL("libgomp.so.1")
+    prev = gomp.omp_get_max_threads()
+    gomp.omp_set_num_threads(int(n))
+    return prev
+
+
 def read_traffic(config: str):
     """HBM bytes per split launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel sources."""
@@ -452,6 +461,12 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        # the same oracle on one host thread, a shorter sample
+        threads = oracle_threads(1)
+        one = cpu_baseline(w, max(2.0, args.cpu_seconds / 3))
+        oracle_threads(threads)
+        res["cpu_baseline"]["one_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1,
+                                             "sample": one["sample"]}
     print(json.dumps(res), flush=True)
 
 
