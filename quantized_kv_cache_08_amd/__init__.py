@@ -109,6 +109,33 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape=None, optional: bool = False,
+          min_numel: int = 0) -> None:
+    """The library reads and writes these arrays through raw device pointers with
+    the documented layouts: check type, device, contiguity and size first."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name}: required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name}: needs at least {min_numel} elements, has {t.numel()}")
+
+
+def _need_workspace(ws: torch.Tensor) -> None:
+    if not isinstance(ws, torch.Tensor) or ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("workspace: must be a contiguous device tensor")
+
+
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -169,6 +196,10 @@ class Cache:
 
 def append(cache: Cache, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
     """Quantize bf16 K/V rows [T][n_kv][d] into their slots (kvq_append)."""
+    _need(slot_mapping, "slot_mapping", torch.int32)
+    T = int(slot_mapping.numel())
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16, (T, cache.num_kv_heads, cache.head_dim))
     _check("kvq_append", lib().kvq_append(ctypes.byref(cache.desc), _ptr(k), _ptr(v), _ptr(slot_mapping),
                                           int(slot_mapping.numel()), _stream(stream)))
 
@@ -178,7 +209,16 @@ def kivi_append(cache: Cache, k: torch.Tensor, v: torch.Tensor, token_offsets: t
     """KIVI INT4 / INT2 append (kvq_kivi_append): new bf16 rows [total][n_kv][d] of each
     sequence (rows token_offsets[b]..token_offsets[b+1]); context_lens = tokens
     held before the call."""
+    _need(context_lens, "context_lens", torch.int32)
     num_seqs = int(context_lens.numel())
+    _need(token_offsets, "token_offsets", torch.int32, (num_seqs + 1,))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] < num_seqs:
+        raise ValueError(f"block_table: expected [>= {num_seqs}][max_pages], got {tuple(block_table.shape)}")
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16)
+        if t.dim() != 3 or tuple(t.shape[1:]) != (cache.num_kv_heads, cache.head_dim):
+            raise ValueError(f"{name}: expected [tokens][{cache.num_kv_heads}][{cache.head_dim}], got {tuple(t.shape)}")
     _check("kvq_kivi_append", lib().kvq_kivi_append(
         ctypes.byref(cache.desc), _ptr(k), _ptr(v), _ptr(token_offsets), _ptr(context_lens), _ptr(block_table),
         int(block_table.shape[1]), num_seqs, int(max_new_tokens), _stream(stream)))
@@ -193,9 +233,24 @@ def decode_workspace_bytes(cache: Cache, num_seqs: int, num_q_heads: int, max_co
     return int(out.value)
 
 
+def _check_attention_args(cache, q, block_table, context_lens, workspace, out, lse, rows) -> None:
+    """rows: the leading dimensions of q / out ([B][Hq] or [B][q_len][Hq])."""
+    _need(q, "q", torch.bfloat16, rows + (cache.head_dim,))
+    _need(out, "out", torch.float32, rows + (cache.head_dim,))
+    _need(lse, "lse", torch.float32, rows, optional=True)
+    _need(context_lens, "context_lens", torch.int32, (rows[0],))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] < rows[0]:
+        raise ValueError(f"block_table: expected [>= {rows[0]}][max_pages], got {tuple(block_table.shape)}")
+    _need_workspace(workspace)
+
+
 def _decode(fn: str, cache, q, block_table, context_lens, max_context_len, softmax_scale, workspace, out,
             lse, partition_pages, stream):
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [num_seqs][num_q_heads][head_dim], got {tuple(q.shape)}")
     num_seqs, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    _check_attention_args(cache, q, block_table, context_lens, workspace, out, lse, (num_seqs, num_q_heads))
     _check(fn, getattr(lib(), fn)(
         ctypes.byref(cache.desc), _ptr(q), num_seqs, num_q_heads, _ptr(block_table),
         int(block_table.shape[1]), _ptr(context_lens), int(max_context_len), float(softmax_scale),
@@ -218,6 +273,9 @@ def decode_split(cache: Cache, q, block_table, context_lens, max_context_len: in
 
 def decode_reduce(cache: Cache, num_seqs: int, num_q_heads: int, max_context_len: int, workspace, out,
                   lse=None, partition_pages: int = 0, stream=None) -> None:
+    _need(out, "out", torch.float32, (num_seqs, num_q_heads, cache.head_dim))
+    _need(lse, "lse", torch.float32, (num_seqs, num_q_heads), optional=True)
+    _need_workspace(workspace)
     _check("kvq_decode_reduce", lib().kvq_decode_reduce(
         ctypes.byref(cache.desc), num_seqs, num_q_heads, int(max_context_len), int(partition_pages),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse),
@@ -235,7 +293,10 @@ def verify_workspace_bytes(cache: Cache, num_seqs: int, q_len: int, num_q_heads:
 
 def _verify(fn: str, cache, q, block_table, context_lens, max_context_len, softmax_scale, workspace, out,
             lse, partition_pages, stream):
+    if q.dim() != 4:
+        raise ValueError(f"q: expected [num_seqs][q_len][num_q_heads][head_dim], got {tuple(q.shape)}")
     num_seqs, q_len, num_q_heads = int(q.shape[0]), int(q.shape[1]), int(q.shape[2])
+    _check_attention_args(cache, q, block_table, context_lens, workspace, out, lse, (num_seqs, q_len, num_q_heads))
     _check(fn, getattr(lib(), fn)(
         ctypes.byref(cache.desc), _ptr(q), num_seqs, q_len, num_q_heads, _ptr(block_table),
         int(block_table.shape[1]), _ptr(context_lens), int(max_context_len), float(softmax_scale),
@@ -259,6 +320,9 @@ def verify_split(cache: Cache, q, block_table, context_lens, max_context_len: in
 
 def verify_reduce(cache: Cache, num_seqs: int, q_len: int, num_q_heads: int, max_context_len: int, workspace,
                   out, lse=None, partition_pages: int = 0, stream=None) -> None:
+    _need(out, "out", torch.float32, (num_seqs, q_len, num_q_heads, cache.head_dim))
+    _need(lse, "lse", torch.float32, (num_seqs, q_len, num_q_heads), optional=True)
+    _need_workspace(workspace)
     _check("kvq_verify_reduce", lib().kvq_verify_reduce(
         ctypes.byref(cache.desc), num_seqs, q_len, num_q_heads, int(max_context_len), int(partition_pages),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse),
@@ -267,9 +331,13 @@ def verify_reduce(cache: Cache, num_seqs: int, q_len: int, num_q_heads: int, max
 
 def e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
     """float32 -> OCP E4M3 codes with the encoder the append kernel uses."""
+    _need(x, "x", torch.float32)
+    _need(codes, "codes", torch.uint8, min_numel=x.numel())
     _check("kvq_e4m3_encode", lib().kvq_e4m3_encode(_ptr(x), _ptr(codes), int(x.numel()), _stream(stream)))
 
 
 def e5m2_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
     """float32 -> OCP E5M2 codes with the encoder the append kernel uses for E5M2 caches."""
+    _need(x, "x", torch.float32)
+    _need(codes, "codes", torch.uint8, min_numel=x.numel())
     _check("kvq_e5m2_encode", lib().kvq_e5m2_encode(_ptr(x), _ptr(codes), int(x.numel()), _stream(stream)))

@@ -246,3 +246,27 @@ def test_attn_flags_validation(L):
     d = _kivi_desc()
     d.attn_flags = kvq.KVQ_ATTN_FP8_QK
     assert _decode(L, d, num_seqs=0, hq=16, maxp=4, max_ctx=128) == UNSUPPORTED
+
+
+def test_binding_rejects_malformed_tensors():
+    """The Python binding checks dtype, device, contiguity and shape before
+    handing raw pointers to the library (these raise before any HIP call)."""
+    import torch
+    c = kvq.Cache.__new__(kvq.Cache)
+    c.num_kv_heads, c.head_dim, c.desc = 2, 128, _desc()
+    bf = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
+    i32 = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(TypeError, match="slot_mapping"):
+        kvq.append(c, bf, bf, torch.zeros(4, dtype=torch.int64))
+    with pytest.raises(ValueError, match="device"):
+        kvq.append(c, bf, bf, i32)                                   # host tensors
+    with pytest.raises(TypeError, match="q"):
+        kvq.decode_attention(c, torch.zeros(4, 4, 128), i32.view(4, 1), i32, 16, 0.1,
+                             torch.zeros(8, dtype=torch.uint8), torch.zeros(4, 4, 128))
+    with pytest.raises(ValueError, match="q"):
+        kvq.decode_attention(c, torch.zeros(4, 128, dtype=torch.bfloat16), i32.view(4, 1), i32, 16, 0.1,
+                             torch.zeros(8, dtype=torch.uint8), torch.zeros(4, 4, 128))
+    with pytest.raises(TypeError, match="context_lens"):
+        kvq.kivi_append(c, bf, bf, i32, torch.zeros(3, dtype=torch.int64), i32.view(4, 1), 1)
+    with pytest.raises(TypeError, match="x"):
+        kvq.e4m3_encode(torch.zeros(4, dtype=torch.float64), torch.zeros(4, dtype=torch.uint8))
