@@ -242,8 +242,10 @@ kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t n
  * Other arguments as kvq_decode_attention; the workspace size comes from
  * kvq_verify_workspace_bytes.  The q_len x (num_q_heads / num_kv_heads) query
  * rows of a KV head are one 16-row tile: their product must be <= 16
- * (KVQ_ERR_UNSUPPORTED otherwise), and KIVI caches are not supported
- * (KVQ_ERR_UNSUPPORTED).  The KV bytes are read once for all q_len rows. */
+ * (KVQ_ERR_UNSUPPORTED otherwise).  KIVI caches (INT4 / INT2 pages plus the
+ * fp16 window) need q_len - 1 <= cache->residual, so that every position a
+ * row cannot see is a window token (KVQ_ERR_UNSUPPORTED otherwise).  The KV
+ * bytes are read once for all q_len rows. */
 kvq_status kvq_verify_workspace_bytes(const kvq_cache* cache, int32_t num_seqs, int32_t q_len,
                                       int32_t num_q_heads, int32_t max_context_len,
                                       int32_t partition_pages, size_t* bytes);

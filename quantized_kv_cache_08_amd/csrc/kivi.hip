@@ -368,16 +368,25 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     const int j = lane & 15;
     const int g = lane >> 4;
     const int G = p.group;
-    const int hj = SHARE ? (j & 7) : j;          // head of this lane's query
+    const int QL = p.q_len;
+    const int GQ = G * QL;                       // query rows of this KV head (verification: QL > 1)
+    const int hj = SHARE ? (j & 7) : j;          // query row of this lane
     const int len = min(max(p.context_lens[b], 0), p.max_ctx);
     const int nq = kivi_nq(len, kp.residual);
     const int pq = nq / kKiviGroup;
+    // Row hj is position qi = hj / G of the QL newest (query head h G + hj % G)
+    // and sees tokens t < row_end.  The host requires QL - 1 <= residual, so
+    // every row sees all quantized tokens (nq <= len - residual): only fp16
+    // window chunks are masked.
+    const int qi = hj / G;
+    const int row_end = len - (QL - 1 - min(qi, QL - 1));
 
-    // query (B operand): head hj, channels 32g + 8kb + [0, 8)
+    // query (B operand): row hj, channels 32g + 8kb + [0, 8)
     u32x4_t qb[4];
-    if (hj < G) {
-        const u32x4_t* qp =
-            (const u32x4_t*)(p.q + ((size_t)b * p.n_q + (size_t)h * G + hj) * kHeadDim + 32 * g);
+    if (hj < GQ) {
+        const u32x4_t* qp = (const u32x4_t*)(p.q + (((size_t)b * QL + qi) * p.n_q + (size_t)h * G + (hj - qi * G)) *
+                                                       kHeadDim +
+                                                   32 * g);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qb[kb] = qp[kb];
     } else {
@@ -404,7 +413,9 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
 #pragma unroll
     for (int t = 0; t < 8; ++t) st.acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     st.pc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    st.m_used = -INFINITY;
+    // finite, so that a row that sees no token of a chunk (causal rows) gets
+    // p = exp2(-inf - m_used) = 0 instead of NaN
+    st.m_used = -3.402823466e38f;   // -FLT_MAX
     st.lsum = 0.0f;
     st.pz = 0.0f;
 
@@ -726,7 +737,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 for (int kb = 0; kb < 4; ++kb) d = mfma_16x16x32_f16(kr[kb], qh[kb], d);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    sc[hp][r] = (rbase + 16 * hp + 4 * g + r < len) ? d[r] * p.score_scale : -INFINITY;
+                    sc[hp][r] = (rbase + 16 * hp + 4 * g + r < row_end) ? d[r] * p.score_scale : -INFINITY;
             }
             float pp[2][4];
             kivi_softmax(st, sc, pp, g, !SHARE || j < 8);   // lanes 8-15 duplicate heads 0-7 when sharing
@@ -780,15 +791,22 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         lsum += bits_to_f32(row_swap8(f32_to_bits(lsum)));
         pz += bits_to_f32(row_swap8(f32_to_bits(pz)));
     }
-    const size_t row0 = (size_t)b * p.n_q + (size_t)h * G;
+    // Rows: output row of query row x is (b QL + x / G) n_q + h G + x % G;
+    // partial results are kept per (b, h, x) at vrow0 + x.  A row that saw no
+    // token (lsum = 0: causal rows of a short context) gives o = 0, lse = -inf.
+    const size_t vrow0 = ((size_t)b * p.n_kv + h) * GQ;
+    auto out_row = [&](int x) {
+        const int xi = x / G;
+        return ((size_t)b * QL + xi) * p.n_q + (size_t)h * G + (x - xi * G);
+    };
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int head = 4 * g + r;
         const float lr = __shfl(lsum, head & 15);
         const float pzh = __shfl(pz, head & 15);
         const float off = 128.0f * st.pc[r];
-        if (head < G) {
-            const float inv = 1.0f / lr;
+        if (head < GQ) {
+            const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
             f32x4_t o0, o1;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -797,18 +815,18 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 o1[t] = ((st.acc[t + 4][r] - off) * f + pzh) * inv;
             }
             float* dst = (n_seg == 1)
-                             ? p.out + (row0 + head) * kHeadDim + 8 * j
-                             : p.part_o + ((row0 + head) * p.max_parts + seg) * kHeadDim + 8 * j;
+                             ? p.out + out_row(head) * kHeadDim + 8 * j
+                             : p.part_o + ((vrow0 + head) * p.max_parts + seg) * kHeadDim + 8 * j;
             *(f32x4_t*)dst = o0;
             *(f32x4_t*)(dst + 4) = o1;
         }
     }
-    if (g == 0 && j < G) {
-        const float l2 = st.m_used + __log2f(lsum);
+    if (g == 0 && j < GQ) {
+        const float l2 = lsum > 0.0f ? st.m_used + __log2f(lsum) : -INFINITY;
         if (n_seg == 1) {
-            if (p.lse) p.lse[row0 + j] = l2 * kLn2;
+            if (p.lse) p.lse[out_row(j)] = l2 * kLn2;
         } else {
-            p.part_lse[(row0 + j) * p.max_parts + seg] = l2;
+            p.part_lse[(vrow0 + j) * p.max_parts + seg] = l2;
         }
     }
 }
@@ -826,14 +844,16 @@ __global__ __launch_bounds__(256) void kivi_split_kernel(KiviSplitParams kp) {
     });
 }
 
-static const void* kivi_split_fn(int bits, int group) {
+// rows = query rows per KV head (group x positions): lanes j and j + 8 share a
+// row when there are at most 8
+static const void* kivi_split_fn(int bits, int rows) {
     if (bits == 2)
-        return group <= 8 ? (const void*)&kivi_split_kernel<2, true> : (const void*)&kivi_split_kernel<2, false>;
-    return group <= 8 ? (const void*)&kivi_split_kernel<4, true> : (const void*)&kivi_split_kernel<4, false>;
+        return rows <= 8 ? (const void*)&kivi_split_kernel<2, true> : (const void*)&kivi_split_kernel<2, false>;
+    return rows <= 8 ? (const void*)&kivi_split_kernel<4, true> : (const void*)&kivi_split_kernel<4, false>;
 }
 
-hipError_t kivi_split_occupancy(int bits, int group, size_t lds_bytes, int* blocks_per_cu) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kivi_split_fn(bits, group), kSplitThreads,
+hipError_t kivi_split_occupancy(int bits, int rows, size_t lds_bytes, int* blocks_per_cu) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, kivi_split_fn(bits, rows), kSplitThreads,
                                                         lds_bytes);
 }
 
@@ -842,7 +862,7 @@ hipError_t launch_kivi_split(const KiviSplitParams& p, int grid, size_t lds_byte
     KiviSplitParams args = p;
     void* kargs[] = {&args};
     if (p.bits != 4 && p.bits != 2) return hipErrorInvalidValue;
-    return hipLaunchKernel(kivi_split_fn(p.bits, p.s.group), dim3(grid), dim3(kSplitThreads), kargs, lds_bytes,
+    return hipLaunchKernel(kivi_split_fn(p.bits, p.s.group * p.s.q_len), dim3(grid), dim3(kSplitThreads), kargs, lds_bytes,
                            stream);
 }
 

@@ -121,7 +121,9 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
     if (!valid_group(num_q_heads / c->num_kv_heads)) return KVQ_ERR_UNSUPPORTED;
     // the query rows of one KV head (group x positions) form one 16-wide MFMA tile
     if ((long long)q_len * (num_q_heads / c->num_kv_heads) > 16) return KVQ_ERR_UNSUPPORTED;
-    if (q_len > 1 && is_kivi(c->dtype)) return KVQ_ERR_UNSUPPORTED;
+    // KIVI verification: the positions a row cannot see must lie in the fp16
+    // window, which holds at least `residual` tokens
+    if (q_len > 1 && is_kivi(c->dtype) && q_len - 1 > c->residual) return KVQ_ERR_UNSUPPORTED;
     if ((long long)max_context_len > (long long)max_pages_per_seq * c->page_size)
         return KVQ_ERR_INVALID;
     if (num_seqs > 16383) return KVQ_ERR_UNSUPPORTED;   // prefix table lives in LDS
@@ -175,7 +177,7 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     const bool kivi = is_kivi(c->dtype);
     int per_cu = 0;
     const bool q8 = (c->attn_flags & KVQ_ATTN_FP8_QK) != 0;
-    hipError_t e = kivi ? kivi_split_occupancy(kivi_bits(c->dtype), p.group, lds, &per_cu)
+    hipError_t e = kivi ? kivi_split_occupancy(kivi_bits(c->dtype), p.group * q_len, lds, &per_cu)
                         : split_occupancy(c->dtype, is_static, c->page_size, q8, lds, &per_cu);
     if (e != hipSuccess) return KVQ_ERR_HIP;
     const int cus = device_cus();

@@ -97,6 +97,6 @@ hipError_t launch_e5m2_encode(const float* x, uint8_t* codes, long long n, hipSt
 hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream);
 hipError_t launch_kivi_split(const KiviSplitParams& p, int grid, size_t lds_bytes,
                              hipStream_t stream);
-hipError_t kivi_split_occupancy(int bits, int group, size_t lds_bytes, int* blocks_per_cu);
+hipError_t kivi_split_occupancy(int bits, int rows, size_t lds_bytes, int* blocks_per_cu);
 
 }  // namespace kvq

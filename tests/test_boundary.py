@@ -185,7 +185,10 @@ def test_verify_validation(L):
     assert _verify(L, d, ws_bytes=0) == WORKSPACE
     assert _verify(L, d, out=None) == INVALID
     assert _verify(L, d, num_seqs=0) == OK
-    assert _verify(L, _kivi_desc(), q_len=2, hq=16, max_ctx=128) == UNSUPPORTED
+    # KIVI caches: hidden positions must lie in the fp16 window (q_len - 1 <= residual)
+    assert _verify(L, _kivi_desc(), q_len=2, hq=16, max_ctx=128, num_seqs=0) == OK
+    assert _verify(L, _kivi_desc(residual=0, window_tokens=32), q_len=2, hq=16, max_ctx=128,
+                   num_seqs=0) == UNSUPPORTED
     # workspace: partial rows grow with q_len; q_len 1 is the decode workspace
     out1, out4, dec = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
     assert L.kvq_verify_workspace_bytes(ctypes.byref(d), 32, 1, 8, 8192, 0, ctypes.byref(out1)) == OK

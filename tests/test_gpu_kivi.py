@@ -192,3 +192,54 @@ def test_kivi_decode_step_as_hip_graph_matches_eager(bits):
     _graph_replays_match(step, [out, lse], other)
     for b in range(B):
         check_out(bt, out, lse, b, H.kivi_oracle_seq(bt, b))
+
+
+@BITS
+@pytest.mark.parametrize("G,q_len", [(2, 4), (4, 4), (8, 2)])
+def test_kivi_verification_pass(bits, G, q_len):
+    """The q_len newest positions scored causally over a KIVI cache (rows per
+    KV head G q_len = 8 shares lanes, 16 does not): position i sees the first
+    len - q_len + 1 + i tokens; a position that sees none gives out 0, lse -inf."""
+    from oracle import oracle as O
+    w = small(bits, batch=4, num_q_heads=2 * G, num_kv_heads=2)
+    lens = np.array([2, 100, 161, 300])
+    say("kivi verify", bits, G, q_len)
+    bt = H.build_kivi(w, lens)
+    B, Hq, d = len(lens), w.num_q_heads, w.head_dim
+    q = synthetic.gen_q(w, "cuda", batch=B * q_len).reshape(B, q_len, Hq, d)
+    ws = torch.zeros(kvq.verify_workspace_bytes(bt.cache, B, q_len, Hq, bt.max_ctx), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((B, q_len, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((B, q_len, Hq), float("nan"), device="cuda")
+    kvq.verify_attention(bt.cache, q, bt.block_table, bt.context_lens, bt.max_ctx, d ** -0.5, ws, out, lse)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qc = synthetic.gen_q(w, "cpu", batch=B * q_len).reshape(B, q_len, Hq, d)
+    for b in range(B):
+        ref = H.kivi_oracle_seq(bt, b)
+        T = int(lens[b])
+        for i in range(q_len):
+            n_vis = T - q_len + 1 + i
+            if n_vis <= 0:
+                assert not out[b, i].any() and np.all(np.isneginf(lse[b, i])), (b, i)
+                continue
+            qi = O.bf16_value(H.u16(qc[b, i])).astype(np.float64)
+            o_ref, l_ref = O.attention(qi, ref["k_hat"][:n_vis], ref["v_hat"][:n_vis], d ** -0.5)
+            ok, mabs, mrel = H.allclose_report(out[b, i], o_ref, ATOL, RTOL)
+            assert ok, f"seq {b} position {i}: max abs {mabs:.3e} max rel {mrel:.3e}"
+            assert np.abs(lse[b, i] - l_ref).max() <= LSE_ATOL, (b, i)
+
+
+@BITS
+def test_kivi_verify_one_position_is_decode_bit_for_bit(bits):
+    w = small(bits, batch=3, num_q_heads=8, num_kv_heads=2)
+    bt = H.build_kivi(w, np.array([1, 170, 333]))
+    out_d, lse_d = H.run_decode_kivi(bt)
+    B, Hq, d = 3, 8, w.head_dim
+    ws = torch.zeros(kvq.verify_workspace_bytes(bt.cache, B, 1, Hq, bt.max_ctx), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, 1, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((B, 1, Hq), float("nan"), device="cuda")
+    kvq.verify_attention(bt.cache, bt.q.reshape(B, 1, Hq, d).contiguous(), bt.block_table, bt.context_lens,
+                         bt.max_ctx, d ** -0.5, ws, out, lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, 0], out_d) and torch.equal(lse[:, 0], lse_d)
