@@ -281,6 +281,17 @@ kvq_status kvq_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_
  * x: device fp32 [n], codes: device u8 [n]. */
 kvq_status kvq_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 
+/* Measurement helper, not part of the method: a plain streaming read of
+ * `bytes` bytes at `buf` (16-byte loads, four in flight per thread, a
+ * grid-stride loop over blocks_per_cu x (compute units) workgroups of 256
+ * threads), for timing the HBM read rate a buffer of that size attains on
+ * this device.  buf: device, 16-byte aligned, bytes a multiple of 16.  sink:
+ * one device uint32 the kernel may write (it almost never does).
+ * blocks_per_cu in 1..32.  For benchmarks that compare the decode kernels
+ * with the attainable read rate. */
+kvq_status kvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks_per_cu,
+                          hipStream_t stream);
+
 /* Static text for a status code. */
 const char* kvq_status_string(kvq_status status);
 

@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2", "KVQ_INT2_KIVI", "KIVI_DTYPES", "KVQ_ATTN_FP8_QK",
+    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2", "KVQ_INT2_KIVI", "KIVI_DTYPES", "KVQ_ATTN_FP8_QK", "read_probe",
     "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
     "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
     "verify_workspace_bytes", "verify_attention", "verify_split", "verify_reduce",
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         for fn in ("kvq_e4m3_encode", "kvq_e5m2_encode"):
             getattr(L, fn).restype = ctypes.c_int
             getattr(L, fn).argtypes = [_P, _P, ctypes.c_int64, _P]
+        L.kvq_read_probe.restype = ctypes.c_int
+        L.kvq_read_probe.argtypes = [_P, ctypes.c_int64, _P, _I32, _P]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -341,3 +343,12 @@ def e5m2_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
     _need(x, "x", torch.float32)
     _need(codes, "codes", torch.uint8, min_numel=x.numel())
     _check("kvq_e5m2_encode", lib().kvq_e5m2_encode(_ptr(x), _ptr(codes), int(x.numel()), _stream(stream)))
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, blocks_per_cu: int = 2, stream=None) -> None:
+    """Plain streaming read of a device byte buffer (kvq_read_probe): a
+    measurement of the attainable HBM read rate, not part of the method."""
+    _need(buf, "buf", torch.uint8)
+    _need(sink, "sink", torch.int32, min_numel=1)
+    _check("kvq_read_probe", lib().kvq_read_probe(_ptr(buf), int(buf.numel()), _ptr(sink), int(blocks_per_cu),
+                                                  _stream(stream)))

@@ -461,6 +461,17 @@ kvq_status kvq_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_
     return launch_e5m2_encode(x, codes, n, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
+kvq_status kvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks_per_cu,
+                          hipStream_t stream) {
+    if (bytes < 0 || (bytes & 15) || blocks_per_cu <= 0 || blocks_per_cu > 32) return KVQ_ERR_INVALID;
+    if (bytes == 0) return KVQ_OK;
+    if (!buf || !sink) return KVQ_ERR_INVALID;
+    const int cus = device_cus();
+    if (cus <= 0) return KVQ_ERR_HIP;
+    return launch_read_probe(buf, bytes, sink, cus * blocks_per_cu, stream) == hipSuccess ? KVQ_OK
+                                                                                          : KVQ_ERR_HIP;
+}
+
 const char* kvq_status_string(kvq_status s) {
     switch (s) {
         case KVQ_OK: return "ok";

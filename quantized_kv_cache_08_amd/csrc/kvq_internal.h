@@ -94,6 +94,8 @@ hipError_t split_occupancy(int dtype, bool static_scale, int page_size, bool q8,
 hipError_t launch_e4m3_encode(const float* x, uint8_t* codes, long long n, hipStream_t stream);
 hipError_t launch_e5m2_encode(const float* x, uint8_t* codes, long long n, hipStream_t stream);
 
+hipError_t launch_read_probe(const void* buf, long long bytes, uint32_t* sink, int grid, hipStream_t stream);
+
 hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream);
 hipError_t launch_kivi_split(const KiviSplitParams& p, int grid, size_t lds_bytes,
                              hipStream_t stream);

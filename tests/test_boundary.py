@@ -273,3 +273,15 @@ def test_binding_rejects_malformed_tensors():
         kvq.kivi_append(c, bf, bf, i32, torch.zeros(3, dtype=torch.int64), i32.view(4, 1), 1)
     with pytest.raises(TypeError, match="x"):
         kvq.e4m3_encode(torch.zeros(4, dtype=torch.float64), torch.zeros(4, dtype=torch.uint8))
+
+
+def test_read_probe_validation(L):
+    L.kvq_read_probe.restype = ctypes.c_int
+    L.kvq_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    assert L.kvq_read_probe(FAKE, -16, FAKE, 2, None) == INVALID
+    assert L.kvq_read_probe(FAKE, 17, FAKE, 2, None) == INVALID          # not a multiple of 16
+    assert L.kvq_read_probe(FAKE, 1024, FAKE, 0, None) == INVALID
+    assert L.kvq_read_probe(FAKE, 1024, FAKE, 33, None) == INVALID
+    assert L.kvq_read_probe(None, 1024, FAKE, 2, None) == INVALID
+    assert L.kvq_read_probe(FAKE, 1024, None, 2, None) == INVALID
+    assert L.kvq_read_probe(FAKE, 0, FAKE, 2, None) == OK

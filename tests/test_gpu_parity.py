@@ -406,3 +406,14 @@ def test_one_long_sequence_131072(dtype, heads):
     out, lse = H.run_decode(bt)
     for b in range(2):
         check_seq(bt, out, lse, b)
+
+
+def test_read_probe_runs_on_odd_sizes():
+    """The streaming-read helper stays inside its buffer for sizes that are not
+    a multiple of its unrolled stride."""
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for n in (16, 4096 + 16, (1 << 20) + 48, 37 * (1 << 20)):
+        buf = torch.ones(n, dtype=torch.uint8, device="cuda")
+        for bpc in (1, 8):
+            kvq.read_probe(buf, sink, bpc)
+    torch.cuda.synchronize()
