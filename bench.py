@@ -474,8 +474,10 @@ def main():
             None if not MODEL_LAYERS.get((Hq, w.num_kv_heads)) else
             {"layers": MODEL_LAYERS[(Hq, w.num_kv_heads)],
              "value": round(B * QL / (ms_step * 1e-3 * MODEL_LAYERS[(Hq, w.num_kv_heads)]), 1)}),
-        "decode_attention_kv_gbs": round(kv_gbs, 2),
-        "pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
+        # split + reduce bytes over both kernels' back-to-back means (the reduce
+        # mean is dispatch-bound); the split kernel alone is `roofline`
+        "split_plus_reduce_kv_gbs": round(kv_gbs, 2),
+        "split_plus_reduce_pct_of_hbm_peak": round(100.0 * kv_gbs / HBM_PEAK_GBS, 2),
         # means: back-to-back launches; p50 / p95: single launches between events
         # (these include each launch's dispatch latency)
         "kernel_ms": {"append": round(float(mean_app), 5), "split": round(float(mean_split), 5),
