@@ -200,7 +200,9 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
  * out:           device fp32 [num_seqs][num_q_heads][head_dim]
  * lse:           device fp32 [num_seqs][num_q_heads] natural-log sum-exp of the
  *                scaled scores, or NULL.
- * num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16. */
+ * num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16, and num_seqs at most
+ * 16383 (the kernels keep a per-sequence work table in LDS); beyond either,
+ * KVQ_ERR_UNSUPPORTED. */
 kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t num_seqs,
                                 int32_t num_q_heads, const int32_t* block_table,
                                 int32_t max_pages_per_seq, const int32_t* context_lens,

@@ -104,6 +104,9 @@ def _decode(L, desc, fn="kvq_decode_attention", num_seqs=2, hq=8, maxp=4, max_ct
 
 def test_decode_validation(L):
     d = _desc()
+    # the per-sequence work table lives in LDS: at most 16383 sequences (no launch
+    # happens for the refused call)
+    assert _decode(L, d, num_seqs=16384) == UNSUPPORTED
     for fn in ("kvq_decode_attention", "kvq_decode_split"):
         assert _decode(L, d, fn, hq=6) == UNSUPPORTED            # group of 3
         assert _decode(L, d, fn, hq=7) == INVALID                # not a multiple of n_kv

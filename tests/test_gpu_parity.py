@@ -417,3 +417,17 @@ def test_read_probe_runs_on_odd_sizes():
         for bpc in (1, 8):
             kvq.read_probe(buf, sink, bpc)
     torch.cuda.synchronize()
+
+
+def test_largest_batch_16383_sequences():
+    """The largest batch the work table in LDS holds (16383 sequences, 64 KiB of
+    prefix table), 1-8 tokens each on one KV head: all outputs finite, a sample
+    checked against the oracle."""
+    w = small("tiny", batch=16383, num_q_heads=2, num_kv_heads=1, context=8)
+    lens = np.random.default_rng(41).integers(1, 9, size=16383)
+    say("largest batch")
+    bt = H.build(w, lens=lens, shuffle=True)
+    out, lse = H.run_decode(bt)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    for b in (0, 1, 8191, 16382) + tuple(range(5, 16383, 1601)):
+        check_seq(bt, out, lse, int(b))
