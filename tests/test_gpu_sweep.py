@@ -117,3 +117,56 @@ def test_option_combinations(case):
                 mag = np.array([(kh[:, h // c["G"], :] @ qh[h]).max() for h in range(Hq)]) * scale
                 bar = 1e-3 + 2.0**-12 * mag
             assert np.all(np.abs(lse[b, i] - ref["lse"][i]) <= bar), (b, i)
+
+
+N_KIVI = 16
+
+
+@pytest.mark.parametrize("case", range(N_KIVI))
+def test_kivi_option_combinations(case):
+    """KIVI caches: code width, group, verification positions, partitions,
+    lengths across the window and group boundaries, shuffled pages and append
+    plans (one bulk call, or bulk + one-token steps + rest); state bit-exact and
+    outputs against the oracle."""
+    from tests.test_gpu_kivi import check_state
+    rng = np.random.default_rng(5000 + case)
+    bits = int(rng.choice([4, 2]))
+    n_kv = int(rng.integers(1, 3))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    QL = int(rng.choice([1, 1, 2, 4]))
+    while G * QL > 16:
+        QL //= 2
+    B = int(rng.integers(1, 5))
+    lens = rng.integers(1, 700, size=B)
+    part = int(rng.choice([0, 0, 1, 3]))
+    say("kivi", case, dict(bits=bits, n_kv=n_kv, G=G, QL=QL, lens=lens.tolist(), part=part))
+    d = dict(synthetic.WORKLOADS["kivi" if bits == 4 else "kivi2"].__dict__)
+    d.update(batch=B, num_q_heads=n_kv * G, num_kv_heads=n_kv, context=int(lens.max()), seed=70 + case)
+    w = synthetic.Workload(**d)
+    plan = None if rng.integers(2) else [lens]
+    bt = H.build_kivi(w, lens, plan=plan, shuffle=bool(rng.integers(2)))
+    Hq, dh = w.num_q_heads, w.head_dim
+    scale = dh ** -0.5
+    q = synthetic.gen_q(w, "cuda", batch=B * QL).reshape(B, QL, Hq, dh).contiguous()
+    ws = torch.zeros(kvq.verify_workspace_bytes(bt.cache, B, QL, Hq, bt.max_ctx, part), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.full((B, QL, Hq, dh), float("nan"), device="cuda")
+    lse = torch.full((B, QL, Hq), float("nan"), device="cuda")
+    kvq.verify_attention(bt.cache, q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws, out, lse, part)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qc = synthetic.gen_q(w, "cpu", batch=B * QL).reshape(B, QL, Hq, dh)
+    for b in range(B):
+        ref = H.kivi_oracle_seq(bt, b)
+        check_state(bt, b, ref)
+        T = int(lens[b])
+        for i in range(QL):
+            n_vis = T - QL + 1 + i
+            if n_vis <= 0:
+                assert not out[b, i].any() and np.all(np.isneginf(lse[b, i])), (b, i)
+                continue
+            qi = O.bf16_value(H.u16(qc[b, i])).astype(np.float64)
+            o_ref, l_ref = O.attention(qi, ref["k_hat"][:n_vis], ref["v_hat"][:n_vis], scale)
+            ok, mabs, mrel = H.allclose_report(out[b, i], o_ref, ATOL, RTOL)
+            assert ok, f"seq {b} position {i}: max abs {mabs:.3e} max rel {mrel:.3e}"
+            assert np.abs(lse[b, i] - l_ref).max() <= 1e-3, (b, i)
