@@ -181,3 +181,20 @@ def test_fp8qk_llama8b_shape_sampled():
     out, lse = H.run_decode(bt)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     check(bt, out, lse, (0, 13, w.batch - 1))
+
+
+def test_fp8qk_zero_query_rows():
+    """An all-zero query row has scale 0 and all-zero codes: its scores are 0, so
+    the output is the plain mean of the visible dequantized V rows."""
+    w = workload("tiny", batch=2)
+    bt = H.build(w, lens=np.array([40, 300]))
+    bt.cache.attn_flags = kvq.KVQ_ATTN_FP8_QK
+    bt.q[0, 1] = 0
+    bt.q[1, 3] = 0
+    out, lse = H.run_decode(bt)
+    for b, h in ((0, 1), (1, 3)):
+        ref = H.oracle_seq(bt, b, q8=True)
+        mean = ref["v_hat"][:, h // w.group_size].mean(axis=0)
+        ok, mabs, mrel = H.allclose_report(out[b, h].cpu().numpy(), mean, ATOL, RTOL)
+        assert ok, (b, h, mabs, mrel)
+        assert abs(float(lse[b, h]) - np.log(int(bt.lens[b]))) <= LSE_ATOL

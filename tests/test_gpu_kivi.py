@@ -243,3 +243,20 @@ def test_kivi_verify_one_position_is_decode_bit_for_bit(bits):
                          bt.max_ctx, d ** -0.5, ws, out, lse)
     torch.cuda.synchronize()
     assert torch.equal(out[:, 0], out_d) and torch.equal(lse[:, 0], lse_d)
+
+
+@BITS
+@pytest.mark.parametrize("resid", [0, 32])
+def test_kivi_short_windows(bits, resid):
+    """The window rule with other residual sizes: residual 0 keeps only the
+    partial newest group in fp16 (n_q = 32 floor(n / 32)), residual 32 up to 63
+    tokens; state bit-exact, attention against the oracle."""
+    w = small(bits, batch=3, resid=resid)
+    lens = np.array([31, 64, 250])
+    say("kivi residual", resid, bits)
+    bt = H.build_kivi(w, lens)
+    out, lse = H.run_decode_kivi(bt)
+    for b in range(len(lens)):
+        ref = H.kivi_oracle_seq(bt, b)
+        check_state(bt, b, ref)
+        check_out(bt, out, lse, b, ref)
