@@ -315,6 +315,13 @@ __device__ __forceinline__ uint32_t row_swap8(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);   // row_ror:8
 }
 
+// Lanes of the DPP banks in BANKS (four lanes each: 0xC = lanes 8-15 of a row
+// of 16, 0x3 = lanes 0-7) take src of lane (j + 8) mod 16; the others keep keep.
+template <int BANKS>
+__device__ __forceinline__ uint32_t row_swap8_into(uint32_t keep, uint32_t src) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)src, 0x128, 0xF, BANKS, false);
+}
+
 // (w & mask) | c as one v_and_or_b32: the mask is held in a VGPR and c in an
 // SGPR (a VOP3 instruction takes no literal here), both opaque to the
 // compiler so that it neither rematerialises them nor splits the expression
@@ -355,8 +362,11 @@ __device__ __forceinline__ uint32_t v_pair(uint32_t w, uint32_t m0, uint32_t m1,
 }
 
 // SHARE (query group <= 8): lanes j and j + 8 hold the same head and each
-// forms q' = q s for half of the channel blocks; lane j receives the other
-// half from lane j + 8.  Columns 8-15 of the score tile are then unused.
+// forms q' = q s for half of the channel blocks.  The bf16 hi parts of head
+// j's q' (and of its P') then take column (row) j of the 16-wide tiles and the
+// lo parts column (row) j + 8, so one MFMA forms both products: column j + 8's
+// score part is added to column j's, and the accumulator rows 8-15 to rows 0-7
+// once, in the epilogue.
 // BITS = 2: one load brings a lane's codes of both token halves (hp = 0, 1),
 // in bits 0-1 and 2-3 of each 4-bit field; the buffers' [0] entries hold them.
 template <int BITS, bool SHARE>
@@ -536,19 +546,22 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
             }
         }
         u32x4_t BH[4], BL[4];
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) {
-            BH[kk] = bh[kk];
-            BL[kk] = bl[kk];
-        }
         if constexpr (SHARE) {
+            // lanes j hold blocks 0-1, lanes j + 8 blocks 2-3: column j gets the
+            // hi parts of all four, column j + 8 the lo parts
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    BH[2 + kk][e] = row_swap8(bh[kk][e]);
-                    BL[2 + kk][e] = row_swap8(bl[kk][e]);
+                    BH[kk][e] = row_swap8_into<0xC>(bh[kk][e], bl[kk][e]);
+                    BH[2 + kk][e] = row_swap8_into<0x3>(bl[kk][e], bh[kk][e]);
                 }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < NKB; ++kk) {
+                BH[kk] = bh[kk];
+                BL[kk] = bl[kk];
+            }
         }
 
 #pragma unroll
@@ -569,7 +582,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 const u32x4_t a = {perm(kC, x, 0x04010400u), perm(kC, y, 0x04010400u),
                                    perm(kC, x, 0x04030402u), perm(kC, y, 0x04030402u)};
                 d = mfma_16x16x32_bf16(a, BH[kb], d);
-                d = mfma_16x16x32_bf16(a, BL[kb], d);
+                if constexpr (!SHARE) d = mfma_16x16x32_bf16(a, BL[kb], d);
             }
             F.dq[hp] = d;
         }
@@ -582,16 +595,17 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         const float bias_s = F.bias_s;
         u32x4_t ahi, alo;
         if constexpr (SHARE) {
-            // Columns 8-15 are unused: lanes 8-15 of each row take the second
-            // half (tokens 16 + 4g + r) of head j - 8 (DPP row rotation by 8,
-            // written to banks 2-3 only), so each lane exponentiates and splits
-            // four scores, and lane j gets the second half's P' words back.
+            // Lanes j take the first half (tokens 4g + r) of head j's scores and
+            // lanes j + 8 the second (tokens 16 + 4g + r): each adds its half's hi
+            // part (column j) and lo part (column j + 8), so each lane
+            // exponentiates and splits four scores.
             float sc[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float dv = bits_to_f32((uint32_t)__builtin_amdgcn_update_dpp(
-                    (int)f32_to_bits(dq[0][r]), (int)f32_to_bits(dq[1][r]), 0x128, 0xF, 0xC, false));
-                sc[r] = __builtin_fmaf(dv, p.score_scale, bias_s);
+                const uint32_t d0 = f32_to_bits(dq[0][r]), d1 = f32_to_bits(dq[1][r]);
+                const float dhi = bits_to_f32(row_swap8_into<0xC>(d0, d1));
+                const float dlo = bits_to_f32(row_swap8_into<0x3>(d1, d0));
+                sc[r] = __builtin_fmaf(dhi + dlo, p.score_scale, bias_s);
             }
             float pp[4];
             kivi_softmax_half(st, sc, pp, g);
@@ -602,8 +616,10 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 st.pz += p0 * vzf[0][2 * rp] + p1 * vzf[0][2 * rp + 1];
                 hl[rp] = split_bf16(p0 * vsf[0][2 * rp], p1 * vsf[0][2 * rp + 1], neg_lo, neg_hi);
             }
-            ahi = u32x4_t{hl[0][0], hl[1][0], row_swap8(hl[0][0]), row_swap8(hl[1][0])};
-            alo = u32x4_t{hl[0][1], hl[1][1], row_swap8(hl[0][1]), row_swap8(hl[1][1])};
+            // row j: hi parts of both halves; row j + 8: lo parts
+            ahi = u32x4_t{row_swap8_into<0xC>(hl[0][0], hl[0][1]), row_swap8_into<0xC>(hl[1][0], hl[1][1]),
+                          row_swap8_into<0x3>(hl[0][1], hl[0][0]), row_swap8_into<0x3>(hl[1][1], hl[1][0])};
+            alo = u32x4_t{0u, 0u, 0u, 0u};
         } else {
             float sc[2][4];
 #pragma unroll
@@ -639,7 +655,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         // the code offset 128 multiplies exactly the P' the MFMAs consume: sum them
         // with the same MFMAs against ones
         st.pc = mfma_16x16x32_bf16(ahi, kOnes, st.pc);
-        st.pc = mfma_16x16x32_bf16(alo, kOnes, st.pc);
+        if constexpr (!SHARE) st.pc = mfma_16x16x32_bf16(alo, kOnes, st.pc);
 
         // V: channel 8j + t, tokens 16 hp + 4g + [0, 4) in slots 2 hp + [0, 2)
 #pragma unroll
@@ -661,7 +677,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                     bv[2 * hp + rp] = o;
                 }
             st.acc[t] = mfma_16x16x32_bf16(ahi, bv, st.acc[t]);
-            st.acc[t] = mfma_16x16x32_bf16(alo, bv, st.acc[t]);
+            if constexpr (!SHARE) st.acc[t] = mfma_16x16x32_bf16(alo, bv, st.acc[t]);
         }
     };
 
@@ -790,6 +806,14 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
     if constexpr (SHARE) {     // lanes j and j + 8 hold halves of head j's sums
         lsum += bits_to_f32(row_swap8(f32_to_bits(lsum)));
         pz += bits_to_f32(row_swap8(f32_to_bits(pz)));
+        // accumulator rows 8-15 (lane groups 2, 3) hold the lo-part products of
+        // heads 0-7 (the fp16 window chunks add p = 0 there)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            st.pc[r] += __shfl_xor(st.pc[r], 32);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st.acc[t][r] += __shfl_xor(st.acc[t][r], 32);
+        }
     }
     // Rows: output row of query row x is (b QL + x / G) n_q + h G + x % G;
     // partial results are kept per (b, h, x) at vrow0 + x.  A row that saw no
@@ -832,7 +856,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
 }
 
 template <int BITS, bool SHARE>
-__global__ __launch_bounds__(256) void kivi_split_kernel(KiviSplitParams kp) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SHARE ? 2 : 1))) void kivi_split_kernel(KiviSplitParams kp) {
     __shared__ __attribute__((aligned(16))) uint8_t s_meta[kSplitThreads / 64][kKiviMetaBytes];
     __shared__ __attribute__((aligned(16))) uint32_t s_zero[64];
     if (threadIdx.x < 64) s_zero[threadIdx.x] = 0u;   // visible after the first barrier below
