@@ -23,6 +23,7 @@ if not gpu_available():
 import quantized_kv_cache_08_amd as kvq  # noqa: E402
 import synthetic  # noqa: E402
 from tests import kvq_harness as H  # noqa: E402
+from oracle import oracle as O  # noqa: E402
 
 ATOL, RTOL = 2e-3, 1e-2
 LSE_ATOL = 1e-3
@@ -260,3 +261,33 @@ def test_kivi_short_windows(bits, resid):
         ref = H.kivi_oracle_seq(bt, b)
         check_state(bt, b, ref)
         check_out(bt, out, lse, b, ref)
+
+
+@BITS
+@pytest.mark.parametrize("G", [8, 16])
+def test_kivi_rescales_of_the_running_state(bits, G):
+    """At softmax scale 0.25 the chunk maxima of a head rise past the kernel's
+    rescale headroom (2^8) many times within a sequence (counted below on the
+    oracle's scores), so the running state is rescaled with non-zero sums; with
+    query groups up to 8 that includes the accumulator rows holding the
+    lo-part products.  One segment per sequence keeps every jump inside one
+    running state."""
+    w = small(bits, batch=2, num_q_heads=2 * G, num_kv_heads=2)
+    lens = np.array([700, 1000])
+    scale = 0.25
+    bt = H.build_kivi(w, lens)
+    out, lse = H.run_decode_kivi(bt, partition_pages=1024, softmax_scale=scale)
+    jumps = 0
+    for b in range(len(lens)):
+        ref = H.kivi_oracle_seq(bt, b, softmax_scale=scale)
+        q = O.bf16_value(H.u16(synthetic.gen_q(w, "cpu", batch=len(lens))[b])).astype(np.float64)
+        for hq in range(w.num_q_heads):
+            s = ref["k_hat"][:, hq // G] @ q[hq] * (scale / np.log(2.0))
+            m = s[:32].max()
+            for c in range(32, int(lens[b]), 32):
+                mx = s[c:c + 32].max()
+                jumps += int(mx > m + 8.0)
+                m = max(m, mx)
+        check_state(bt, b, ref)
+        check_out(bt, out, lse, b, ref)
+    assert jumps >= 10, jumps

@@ -431,3 +431,33 @@ def test_largest_batch_16383_sequences():
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
     for b in (0, 1, 8191, 16382) + tuple(range(5, 16383, 1601)):
         check_seq(bt, out, lse, int(b))
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "int8"])
+def test_rescales_of_the_running_state(dtype):
+    """At softmax scale 0.25 the chunk maxima of a head rise past the kernel's
+    rescale headroom (2^8) many times within a sequence (counted below on the
+    oracle's scores), so the running state is rescaled with non-zero sums.  One
+    segment per sequence keeps every jump inside one running state."""
+    w = small("tiny", dtype=dtype, batch=2, num_q_heads=16, num_kv_heads=2, context=1000)
+    lens = np.array([700, 1000])
+    scale = 0.25
+    say("rescale", dtype)
+    bt = H.build(w, lens=lens)
+    out, lse = H.run_decode(bt, partition_pages=1024, softmax_scale=scale)
+    jumps = 0
+    for b in range(len(lens)):
+        ref = H.oracle_seq(bt, b, softmax_scale=scale)
+        q = O.bf16_value(H.u16(synthetic.gen_q(w, "cpu", batch=len(lens))[b])).astype(np.float64)
+        for hq in range(w.num_q_heads):
+            s = ref["k_hat"][:, hq // 8] @ q[hq] * (scale / np.log(2.0))
+            m = s[:32].max()
+            for c in range(32, int(lens[b]), 32):
+                mx = s[c:c + 32].max()
+                jumps += int(mx > m + 8.0)
+                m = max(m, mx)
+        ok, mabs, mrel = H.allclose_report(out[b].cpu().numpy(), ref["out"], ATOL, RTOL)
+        assert ok, f"seq {b}: max abs {mabs:.3e} max rel {mrel:.3e}"
+        dl = np.abs(lse[b].cpu().numpy().astype(np.float64) - ref["lse"])
+        assert dl.max() <= LSE_ATOL, f"seq {b}: lse diff {dl.max():.3e}"
+    assert jumps >= 10, jumps
