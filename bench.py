@@ -7,7 +7,7 @@ One step = the whole hot path for one decode token per sequence:
 Inputs are seeded synthetic tensors (``synthetic.py``) with the workload's
 shapes, resident in HBM before timing starts.
 
-    python bench.py [--config llama8b] [--steps 100] [--warmup 10]
+    python bench.py [--config llama70b] [--steps 100] [--warmup 10]
 
 Prints one JSON line.  ``value`` is algorithmic bytes of the step / step time
 (GB/s); ``roofline`` reports the split-K decode kernel (the dominant one)
@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama8b",
+    ap.add_argument("--config", default="llama70b",
                     choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "kivi2", "verify", "e5m2", "static", "fp8qk"])
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto)")
     ap.add_argument("--partition-pages", type=int, default=0)
@@ -222,23 +222,24 @@ def cpu_baseline(w, budget_s: float):
             "quantize_s": round(t_quant, 3), "attention_s": round(t_attn, 3)}
 
 
-def attainable_read(kvq, nbytes: int, launches: int = 20) -> dict:
+def attainable_read(nbytes: int, launches: int = 20) -> dict:
     """A plain streaming read (kvq_read_probe) of as many bytes as the split
     kernel reads per launch, from two buffers used in turn (so that each launch
     reads data the previous one did not leave in the last-level cache), timed
     back to back between two events; the best of a few launch shapes."""
     import torch
+    from quantized_kv_cache_08_amd import testing as KT
     n = max(16, nbytes // 16 * 16)
     bufs = [torch.full((n,), i + 1, dtype=torch.uint8, device="cuda") for i in range(2)]
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     best = None
     for bpc in (1, 2, 4, 8):
         for i in range(4):
-            kvq.read_probe(bufs[i % 2], sink, bpc)
+            KT.read_probe(bufs[i % 2], sink, bpc)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(launches):
-            kvq.read_probe(bufs[i % 2], sink, bpc)
+            KT.read_probe(bufs[i % 2], sink, bpc)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / launches
@@ -463,7 +464,7 @@ def main():
     kv_gbs = (by["split"] + by["reduce"]) / (attn_ms * 1e-3) / 1e9
 
     traffic = read_traffic(args.config)
-    attain = attainable_read(kvq, by["split"])
+    attain = attainable_read(by["split"])
 
     res = {
         "metric": "paged FP8/INT8 decode-attn KV GB/s (% of HBM peak) + tokens/s at 1 GPU",

@@ -80,10 +80,10 @@ extern "C" {
 
 typedef enum kvq_status {
     KVQ_OK = 0,
-    KVQ_ERR_INVALID = 1,      /* null pointer, negative size, inconsistent descriptor     */
-    KVQ_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the kernels implement      */
-    KVQ_ERR_WORKSPACE = 3,    /* workspace smaller than kvq_decode_workspace_bytes()     */
-    KVQ_ERR_HIP = 4           /* a HIP runtime call or a kernel launch failed            */
+    KVQ_EINVAL = -1,          /* null pointer, negative size, inconsistent descriptor     */
+    KVQ_EUNSUPPORTED = -2,    /* well-formed but outside what the kernels implement      */
+    KVQ_EWORKSPACE = -3,      /* workspace smaller than kvq_decode_workspace_bytes()     */
+    KVQ_EHIP = -4             /* a HIP runtime call or a kernel launch failed            */
 } kvq_status;
 
 typedef enum kvq_dtype {
@@ -141,7 +141,14 @@ size_t kvq_record_bytes(int32_t dtype, int32_t scale_mode, int32_t page_size,
                         int32_t head_dim, int32_t which);
 
 /* Quantize-on-append (FP8 E4M3 / E5M2, INT8; a KIVI cache returns
- * KVQ_ERR_UNSUPPORTED, it has kvq_kivi_append).
+ * KVQ_EUNSUPPORTED, it has kvq_kivi_append).  Each new token's K and V rows
+ * are quantized once, at store time, from the full-precision values, and
+ * their BF16 scale (and zero-point) is stored beside the codes ("KV 캐시
+ * 양자화(KV cache quantization) ...", molayo1419.me, section "KV 캐시 양자화란
+ * 실제로 무엇인가", the storage-side steps of its pipeline; "KV Cache 압축",
+ * ryotta.opik.net, section 5.1 steps 1-3).  Per-token scales are per (token,
+ * KV head) row; per-tensor and per-head scales are the caller's static ones
+ * (molayo1419.me, formats-table notes).
  * k, v:          device bf16 [num_tokens][num_kv_heads][head_dim], contiguous.
  * slot_mapping:  device int32 [num_tokens]; slot = page*page_size + row; a
  *                negative slot (or one beyond the pool) skips that token.
@@ -176,19 +183,33 @@ kvq_status kvq_kivi_append(const kvq_cache* cache, const void* k, const void* v,
                            const int32_t* block_table, int32_t max_pages_per_seq, int32_t num_seqs,
                            int32_t max_new_tokens, hipStream_t stream);
 
-/* Workspace bytes that kvq_decode_attention / kvq_decode_split need for this
- * shape.  partition_pages as in kvq_decode_attention. */
+/* Workspace bytes that kvq_decode_attention, kvq_kivi_decode_attention and
+ * kvq_decode_split / kvq_decode_reduce need for this shape: a 256-byte
+ * header, num_seqs + 1 ints, and partial results of (ranges + num_seqs) slots
+ * per KV head, each slot num_q_heads / num_kv_heads rows of 129 floats.  The
+ * automatic plan has at most 2048 ranges over all KV heads, whatever the
+ * device; partition_pages > 0 (as in kvq_decode_attention) sizes for that
+ * forced range length instead.  Depends only on the descriptor's page size
+ * and KV heads and the arguments; no HIP call. */
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_context_len,
                                       int32_t partition_pages, size_t* bytes);
 
 /* One decode step of attention for one query token per sequence, reading the
- * quantized paged cache (FP8 / INT8, or INT4 / INT2 pages plus the fp16 window
- * for the KIVI dtypes, sequence b reading window slot b) with dequantization
- * fused in:
+ * quantized paged FP8 / INT8 cache with dequantization fused in (KIVI caches:
+ * kvq_kivi_decode_attention; here they return KVQ_EUNSUPPORTED):
  *   out[b][h] = sum_t softmax_t(softmax_scale * q[b][h] . k^[t]) v^[t]
  * over every cached token t < context_lens[b] of KV head h / (num_q_heads /
  * num_kv_heads).  fp32 accumulation, flash-decoding split over the context.
+ * Every cached K and V row is read again at each decode step, so the step is
+ * bound by the bytes the cache holds ("KV cache FP8로 동시 요청 76배 수용하기",
+ * storycompiler.tistory.com, sections 1 and 4; "FP8 KV Cache부터 INT4
+ * Weight-Only까지", daewooki.github.io, core concept 1); dequantization
+ * happens inside the attention kernel, whose arithmetic stays in high
+ * precision with fp32 accumulation (ryotta.opik.net "KV Cache 압축", section
+ * 5.1 steps 4-5 and the kernel-fusion note; storycompiler.tistory.com,
+ * section 4); pages come from a per-request block table over one pool
+ * (daewooki.github.io, core concept 2) PagedAttention).
  * q:             device bf16 [num_seqs][num_q_heads][head_dim]
  * block_table:   device int32 [num_seqs][max_pages_per_seq]
  * context_lens:  device int32 [num_seqs]; values above max_context_len are
@@ -202,7 +223,7 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
  *                scaled scores, or NULL.
  * num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16, and num_seqs at most
  * 16383 (the kernels keep a per-sequence work table in LDS); beyond either,
- * KVQ_ERR_UNSUPPORTED. */
+ * KVQ_EUNSUPPORTED. */
 kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t num_seqs,
                                 int32_t num_q_heads, const int32_t* block_table,
                                 int32_t max_pages_per_seq, const int32_t* context_lens,
@@ -210,12 +231,32 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
                                 int32_t partition_pages, void* workspace, size_t workspace_bytes,
                                 float* out, float* lse, hipStream_t stream);
 
-/* The two launches of kvq_decode_attention, exposed separately so that each
+/* KIVI-style decode step (cache->dtype KVQ_INT4_KIVI or KVQ_INT2_KIVI; other
+ * caches return KVQ_EUNSUPPORTED): the same attention as
+ * kvq_decode_attention over tokens held as 4-bit or 2-bit pages (K quantized
+ * per channel over each 32-token group, V per token) followed by the fp16
+ * window of the most recent tokens, sequence b reading window slot b
+ * ("KV Cache 압축", ryotta.opik.net, section 3.1, KIVI: K per channel and V
+ * per token, a full-precision window of recent tokens; molayo1419.me,
+ * formats-table notes on mixed-precision 4-bit).  Arguments, layouts and
+ * errors as kvq_decode_attention; the workspace comes from
+ * kvq_decode_workspace_bytes. */
+kvq_status kvq_kivi_decode_attention(const kvq_cache* cache, const void* q, int32_t num_seqs,
+                                     int32_t num_q_heads, const int32_t* block_table,
+                                     int32_t max_pages_per_seq, const int32_t* context_lens,
+                                     int32_t max_context_len, float softmax_scale,
+                                     int32_t partition_pages, void* workspace, size_t workspace_bytes,
+                                     float* out, float* lse, hipStream_t stream);
+
+/* The two launches of kvq_decode_attention and kvq_kivi_decode_attention
+ * (every cache dtype), exposed separately so that each
  * kernel can be timed and a context-sharded caller can run the merge itself.
  * kvq_decode_split writes every (sequence, head) whose context one wave covers
  * straight to out/lse and the others as partial results into the workspace;
- * kvq_decode_reduce merges the partial results (log-sum-exp weights).  Call
- * them in this order on one stream with identical arguments. */
+ * kvq_decode_reduce merges the partial results with log-sum-exp weights,
+ * the exact identity for softmax attention over a union of disjoint token
+ * sets (out = sum_i e^(lse_i - L) out_i / sum_i e^(lse_i - L), L = max_i
+ * lse_i).  Call them in this order on one stream with identical arguments. */
 kvq_status kvq_decode_split(const kvq_cache* cache, const void* q, int32_t num_seqs,
                             int32_t num_q_heads, const int32_t* block_table,
                             int32_t max_pages_per_seq, const int32_t* context_lens,
@@ -244,9 +285,9 @@ kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t n
  * Other arguments as kvq_decode_attention; the workspace size comes from
  * kvq_verify_workspace_bytes.  The q_len x (num_q_heads / num_kv_heads) query
  * rows of a KV head are one 16-row tile: their product must be <= 16
- * (KVQ_ERR_UNSUPPORTED otherwise).  KIVI caches (INT4 / INT2 pages plus the
+ * (KVQ_EUNSUPPORTED otherwise).  KIVI caches (INT4 / INT2 pages plus the
  * fp16 window) need q_len - 1 <= cache->residual, so that every position a
- * row cannot see is a window token (KVQ_ERR_UNSUPPORTED otherwise).  The KV
+ * row cannot see is a window token (KVQ_EUNSUPPORTED otherwise).  The KV
  * bytes are read once for all q_len rows. */
 kvq_status kvq_verify_workspace_bytes(const kvq_cache* cache, int32_t num_seqs, int32_t q_len,
                                       int32_t num_q_heads, int32_t max_context_len,
@@ -269,30 +310,6 @@ kvq_status kvq_verify_split(const kvq_cache* cache, const void* q, int32_t num_s
 kvq_status kvq_verify_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
                              int32_t max_context_len, int32_t partition_pages, void* workspace,
                              size_t workspace_bytes, float* out, float* lse, hipStream_t stream);
-
-/* The FP8 E4M3 encoder of kvq_append applied to n float32 values (nearest-even,
- * saturating at +-448, sign of zero kept, NaN -> 0x7F).  x: device fp32 [n],
- * codes: device u8 [n]. */
-kvq_status kvq_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
-
-/* The E5M2 encoder of kvq_append (KVQ_FP8_E5M2 caches) applied to n float32
- * values: nearest-even, saturating at +-57344 (no infinities), sign of zero
- * kept, NaN -> 0x7F.  OCP E5M2 is the wider-range, lower-precision FP8 format
- * ("KV 캐시 양자화(KV cache quantization) ...", molayo1419.me, formats notes
- * and the serving-flag values; "KV Cache 압축", ryotta.opik.net, section 3.1).
- * x: device fp32 [n], codes: device u8 [n]. */
-kvq_status kvq_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
-
-/* Measurement helper, not part of the method: a plain streaming read of
- * `bytes` bytes at `buf` (16-byte loads, four in flight per thread, a
- * grid-stride loop over blocks_per_cu x (compute units) workgroups of 256
- * threads), for timing the HBM read rate a buffer of that size attains on
- * this device.  buf: device, 16-byte aligned, bytes a multiple of 16.  sink:
- * one device uint32 the kernel may write (it almost never does).
- * blocks_per_cu in 1..32.  For benchmarks that compare the decode kernels
- * with the attainable read rate. */
-kvq_status kvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks_per_cu,
-                          hipStream_t stream);
 
 /* Static text for a status code. */
 const char* kvq_status_string(kvq_status status);

@@ -15,11 +15,12 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2", "KVQ_INT2_KIVI", "KIVI_DTYPES", "KVQ_ATTN_FP8_QK", "read_probe",
+    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2", "KVQ_INT2_KIVI", "KIVI_DTYPES", "KVQ_ATTN_FP8_QK",
     "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
+    "KVQ_OK", "KVQ_EINVAL", "KVQ_EUNSUPPORTED", "KVQ_EWORKSPACE", "KVQ_EHIP",
     "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
     "verify_workspace_bytes", "verify_attention", "verify_split", "verify_reduce",
-    "decode_attention", "decode_split", "decode_reduce", "e4m3_encode", "e5m2_encode", "status_string",
+    "decode_attention", "kivi_decode_attention", "decode_split", "decode_reduce", "status_string",
     "LIB_PATH",
 ]
 
@@ -27,6 +28,7 @@ KVQ_FP8_E4M3, KVQ_INT8_ASYM, KVQ_INT4_KIVI, KVQ_FP8_E5M2, KVQ_INT2_KIVI = 1, 2, 
 KIVI_DTYPES = (KVQ_INT4_KIVI, KVQ_INT2_KIVI)
 KVQ_ATTN_FP8_QK = 1          # kvq_cache.attn_flags: FP8-domain QK (query quantized to E4M3)
 KVQ_SCALE_PER_TENSOR, KVQ_SCALE_PER_HEAD, KVQ_SCALE_PER_TOKEN_HEAD = 0, 1, 2
+KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
@@ -72,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_workspace_bytes.restype = ctypes.c_int
         L.kvq_decode_workspace_bytes.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32,
                                                  ctypes.POINTER(ctypes.c_size_t)]
-        for fn in ("kvq_decode_attention", "kvq_decode_split"):
+        for fn in ("kvq_decode_attention", "kvq_kivi_decode_attention", "kvq_decode_split"):
             getattr(L, fn).restype = ctypes.c_int
             getattr(L, fn).argtypes = _DECODE_ARGS
         L.kvq_decode_reduce.restype = ctypes.c_int
@@ -87,11 +89,6 @@ def lib() -> ctypes.CDLL:
         L.kvq_verify_reduce.restype = ctypes.c_int
         L.kvq_verify_reduce.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32, _I32, _P,
                                         ctypes.c_size_t, _P, _P, _P]
-        for fn in ("kvq_e4m3_encode", "kvq_e5m2_encode"):
-            getattr(L, fn).restype = ctypes.c_int
-            getattr(L, fn).argtypes = [_P, _P, ctypes.c_int64, _P]
-        L.kvq_read_probe.restype = ctypes.c_int
-        L.kvq_read_probe.argtypes = [_P, ctypes.c_int64, _P, _I32, _P]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -161,7 +158,7 @@ class Cache:
         self.rec_k = record_bytes(dtype, scale_mode, page_size, head_dim, 0)
         self.rec_v = record_bytes(dtype, scale_mode, page_size, head_dim, 1)
         if self.rec_k == 0 or self.rec_v == 0:
-            raise KvqError("kvq_record_bytes", 1)
+            raise KvqError("kvq_record_bytes", KVQ_EINVAL)
         n = num_pages * num_kv_heads
         alloc = torch.empty if fill is None else (lambda *a, **k: torch.full(*a, fill, **k))
         self.k_pages = alloc((n * self.rec_k,), dtype=torch.uint8, device=device)
@@ -267,6 +264,15 @@ def decode_attention(cache: Cache, q, block_table, context_lens, max_context_len
             workspace, out, lse, partition_pages, stream)
 
 
+def kivi_decode_attention(cache: Cache, q, block_table, context_lens, max_context_len: int,
+                          softmax_scale: float, workspace, out, lse=None, partition_pages: int = 0,
+                          stream=None) -> None:
+    """One decode step over a KIVI INT4 / INT2 cache plus its fp16 window
+    (kvq_kivi_decode_attention)."""
+    _decode("kvq_kivi_decode_attention", cache, q, block_table, context_lens, max_context_len, softmax_scale,
+            workspace, out, lse, partition_pages, stream)
+
+
 def decode_split(cache: Cache, q, block_table, context_lens, max_context_len: int, softmax_scale: float,
                  workspace, out, lse=None, partition_pages: int = 0, stream=None) -> None:
     _decode("kvq_decode_split", cache, q, block_table, context_lens, max_context_len, softmax_scale,
@@ -329,26 +335,3 @@ def verify_reduce(cache: Cache, num_seqs: int, q_len: int, num_q_heads: int, max
         ctypes.byref(cache.desc), num_seqs, q_len, num_q_heads, int(max_context_len), int(partition_pages),
         _ptr(workspace), int(workspace.numel() * workspace.element_size()), _ptr(out), _ptr(lse),
         _stream(stream)))
-
-
-def e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
-    """float32 -> OCP E4M3 codes with the encoder the append kernel uses."""
-    _need(x, "x", torch.float32)
-    _need(codes, "codes", torch.uint8, min_numel=x.numel())
-    _check("kvq_e4m3_encode", lib().kvq_e4m3_encode(_ptr(x), _ptr(codes), int(x.numel()), _stream(stream)))
-
-
-def e5m2_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
-    """float32 -> OCP E5M2 codes with the encoder the append kernel uses for E5M2 caches."""
-    _need(x, "x", torch.float32)
-    _need(codes, "codes", torch.uint8, min_numel=x.numel())
-    _check("kvq_e5m2_encode", lib().kvq_e5m2_encode(_ptr(x), _ptr(codes), int(x.numel()), _stream(stream)))
-
-
-def read_probe(buf: torch.Tensor, sink: torch.Tensor, blocks_per_cu: int = 2, stream=None) -> None:
-    """Plain streaming read of a device byte buffer (kvq_read_probe): a
-    measurement of the attainable HBM read rate, not part of the method."""
-    _need(buf, "buf", torch.uint8)
-    _need(sink, "sink", torch.int32, min_numel=1)
-    _check("kvq_read_probe", lib().kvq_read_probe(_ptr(buf), int(buf.numel()), _ptr(sink), int(blocks_per_cu),
-                                                  _stream(stream)))

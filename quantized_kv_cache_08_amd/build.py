@@ -1,4 +1,6 @@
-"""Build libkvq.so (the HIP/gfx950 kernels and the C ABI of include/kvq.h).
+"""Build libkvq.so (the HIP/gfx950 kernels and the C ABI of include/kvq.h)
+and libkvq_testing.so (test and measurement hooks of include/kvq_testing.h,
+not part of the method).
 
     python -m quantized_kv_cache_08_amd.build   (or python quantized_kv_cache_08_amd/build.py)
 
@@ -18,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INC = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libkvq.so")
+OUT_TESTING = os.path.join(PKG, "libkvq_testing.so")
 BUILD = os.path.join(PKG, "_build")
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
@@ -32,6 +35,10 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+def testing_sources():
+    return sorted(glob.glob(os.path.join(CSRC, "testing", "*.hip")))
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = ["hipcc", *FLAGS, "-x", "hip", "-c", src, "-o", obj]
@@ -43,17 +50,23 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = OUT + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    tsrcs = testing_sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(tsrcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + tsrcs))
+    _link(objs[:len(srcs)], OUT, verbose)
+    _link(objs[len(srcs):], OUT_TESTING, verbose)
     return OUT
 
 

@@ -132,36 +132,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     }
 }
 
-__global__ __launch_bounds__(256) void e4m3_encode_kernel(const float* x, uint8_t* codes,
-                                                          long long n) {
-    const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i + 3 < n) {
-        const float* p = x + i;
-        uint32_t w = e4m3_encode4(p[0], p[1], p[2], p[3]);
-        codes[i] = (uint8_t)w;
-        codes[i + 1] = (uint8_t)(w >> 8);
-        codes[i + 2] = (uint8_t)(w >> 16);
-        codes[i + 3] = (uint8_t)(w >> 24);
-    } else {
-        for (long long j = i; j < n; ++j) codes[j] = (uint8_t)e4m3_encode4(x[j], 0.f, 0.f, 0.f);
-    }
-}
-
-__global__ __launch_bounds__(256) void e5m2_encode_kernel(const float* x, uint8_t* codes,
-                                                          long long n) {
-    const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i + 3 < n) {
-        const float* p = x + i;
-        uint32_t w = e5m2_encode4(p[0], p[1], p[2], p[3]);
-        codes[i] = (uint8_t)w;
-        codes[i + 1] = (uint8_t)(w >> 8);
-        codes[i + 2] = (uint8_t)(w >> 16);
-        codes[i + 3] = (uint8_t)(w >> 24);
-    } else {
-        for (long long j = i; j < n; ++j) codes[j] = (uint8_t)e5m2_encode4(x[j], 0.f, 0.f, 0.f);
-    }
-}
-
 template <int DT, bool STATIC, int PS>
 static hipError_t launch_append_t(const AppendParams& p, hipStream_t stream) {
     const long long threads = (long long)p.num_tokens * p.n_kv * 2 * 8;
@@ -190,20 +160,6 @@ hipError_t launch_append(int dtype, bool static_scale, int page_size, const Appe
     }
     return page_size == 16 ? launch_append_t<kINT8, false, 16>(p, stream)
                            : launch_append_t<kINT8, false, 32>(p, stream);
-}
-
-hipError_t launch_e4m3_encode(const float* x, uint8_t* codes, long long n, hipStream_t stream) {
-    const long long grid = (n + 1023) / 1024;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(e4m3_encode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, codes, n);
-    return hipGetLastError();
-}
-
-hipError_t launch_e5m2_encode(const float* x, uint8_t* codes, long long n, hipStream_t stream) {
-    const long long grid = (n + 1023) / 1024;
-    if (grid == 0) return hipSuccess;
-    hipLaunchKernelGGL(e5m2_encode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, x, codes, n);
-    return hipGetLastError();
 }
 
 }  // namespace kvq

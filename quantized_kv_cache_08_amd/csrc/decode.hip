@@ -82,7 +82,7 @@ __device__ __forceinline__ f32x4_t mfma_16x16x128_fp8(const u32x4_t (&a)[2], con
 
 template <int DT, bool STATIC, int PS, bool Q8>
 __device__ __forceinline__ void process_segment(const SplitParams& p, const int b, const int h,
-                                                const int page0, const int page1, const int seg,
+                                                const int page0, const int page1, const int slot,
                                                 const int n_seg, const int lane) {
     const int j = lane & 15;
     const int g = lane >> 4;
@@ -438,9 +438,10 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
         pz += __shfl_xor(pz, 32);
     }
     // Rows: output row of query row x is (b QL + x / G) n_q + h G + x % G;
-    // partial results are kept per (b, h, x) at vrow0 + x.  A row that saw no
-    // token (lsum = 0: causal rows of a short context) gives o = 0, lse = -inf.
-    const size_t vrow0 = ((size_t)b * p.n_kv + h) * GQ;
+    // a partial result goes to row x of partial slot `slot` of head h.  A row
+    // that saw no token (lsum = 0: causal rows of a short context) gives
+    // o = 0, lse = -inf.
+    const size_t prow0 = ((size_t)h * p.slots + slot) * GQ;
     auto out_row = [&](int x) {
         const int xi = x / G;
         return ((size_t)b * QL + xi) * p.n_q + (size_t)h * G + (x - xi * G);
@@ -460,7 +461,7 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
             }
             float* dst = (n_seg == 1)
                              ? p.out + out_row(head) * kHeadDim + 8 * j
-                             : p.part_o + ((vrow0 + head) * p.max_parts + seg) * kHeadDim + 8 * j;
+                             : p.part_o + (prow0 + head) * kHeadDim + 8 * j;
             *(f32x4_t*)dst = o0;
             *(f32x4_t*)(dst + 4) = o1;
         }
@@ -470,24 +471,25 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
         if (n_seg == 1) {
             if (p.lse) p.lse[out_row(j)] = l2 * kLn2;
         } else {
-            p.part_lse[(vrow0 + j) * p.max_parts + seg] = l2;
+            p.part_lse[prow0 + j] = l2;
         }
     }
 }
 
 template <int DT, bool STATIC, int PS, bool Q8>
 __global__ __launch_bounds__(256) void split_kernel(SplitParams p) {
-    for_each_segment<PS>(p, [&](int b, int h, int page0, int page1, int seg, int n_seg, int lane) {
-        process_segment<DT, STATIC, PS, Q8>(p, b, h, page0, page1, seg, n_seg, lane);
+    for_each_segment<PS>(p, [&](int b, int h, int page0, int page1, int slot, int n_seg, int lane) {
+        process_segment<DT, STATIC, PS, Q8>(p, b, h, page0, page1, slot, n_seg, lane);
     });
 }
 
 // Merge of the partial results of each (sequence, query head), one wave per
-// row (merge_rows).
+// row (merge_row).  Item (b, h)'s partials sit in the consecutive slots of
+// head h starting at (range holding the item's first weight unit) + b.
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const int lane = threadIdx.x & 63;
-    // idx: partial-result row (b, h, x), x < GQ = group q_len (see the split
-    // kernel's epilogue); orow: its output row
+    // idx: query row (b, h, x), x < GQ = group q_len (see the split kernel's
+    // epilogue); orow: its output row
     const long long idx = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int GQ = p.group * p.q_len;
     const long long per_seq = (long long)p.n_kv * GQ;
@@ -510,8 +512,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     const long long item_start = p.ws_pfx[b];          // offset inside head h's weight space
     const int n_seg = (int)((item_start + pb - 1) / chunk - item_start / chunk + 1);
     if (n_seg == 1) return;   // written by the split kernel
-    merge_rows<1>(p.part_lse + idx * p.max_parts, p.part_o + idx * p.max_parts * kHeadDim, p.max_parts, n_seg,
-                  p.out + orow * kHeadDim, p.lse ? p.lse + orow : nullptr, lane);
+    const size_t prow = ((size_t)h * p.slots + (size_t)(item_start / chunk + b)) * GQ + x;
+    merge_row(p.part_lse + prow, p.part_o + prow * kHeadDim, GQ, n_seg, p.out + orow * kHeadDim,
+              p.lse ? p.lse + orow : nullptr, lane);
 }
 
 template <int DT, bool STATIC, int PS>

@@ -369,9 +369,11 @@ __device__ __forceinline__ uint32_t v_pair(uint32_t w, uint32_t m0, uint32_t m1,
 // once, in the epilogue.
 // BITS = 2: one load brings a lane's codes of both token halves (hp = 0, 1),
 // in bits 0-1 and 2-3 of each 4-bit field; the buffers' [0] entries hold them.
+constexpr int kFoldPages = 16;   // pages between folds of the code offset (a power of two)
+
 template <int BITS, bool SHARE>
 __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const int b, const int h,
-                                             const int page0, const int page1, const int seg,
+                                             const int page0, const int page1, const int slot,
                                              const int n_seg, const int lane, lds_u8* smeta,
                                              const lds_u8* szero) {
     const SplitParams& p = kp.s;
@@ -681,6 +683,21 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         }
     };
 
+    // The accumulators hold 128 sum P' on top of the products: fold that
+    // offset out every kFoldPages pages, so that the fp32 rounding of a long
+    // segment stays relative to 16 pages' offset, not to the whole
+    // segment's (4096 pages of 2-bit codes put a 128 / 1.5 times larger
+    // offset beside the products and measured 2.5e-3 off the oracle without
+    // folding).  It is the epilogue's subtraction, done early.
+    auto fold = [&]() {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st.acc[t][r] = __builtin_fmaf(-128.0f, st.pc[r], st.acc[t][r]);
+            st.pc[r] = 0.0f;
+        }
+    };
+
     // ---- quantized pages: the loads of the next page are in flight while a
     // page is computed, and page c's back part shares a basic block with page
     // c + 1's front part (independent work to interleave).  The scheduling
@@ -716,7 +733,11 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
                 back(pd);
                 mid(F, b0, pd);
             }
-            ++c;
+            ++c;   // odd here: pages [0, c - 1) are in acc and pc, page c - 1 is pending
+            if (((c + 1) & (kFoldPages - 1)) == 0) {
+                __asm__ volatile("");
+                fold();
+            }
         }
         back(pd);
     }
@@ -816,9 +837,10 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         }
     }
     // Rows: output row of query row x is (b QL + x / G) n_q + h G + x % G;
-    // partial results are kept per (b, h, x) at vrow0 + x.  A row that saw no
-    // token (lsum = 0: causal rows of a short context) gives o = 0, lse = -inf.
-    const size_t vrow0 = ((size_t)b * p.n_kv + h) * GQ;
+    // a partial result goes to row x of partial slot `slot` of head h.  A row
+    // that saw no token (lsum = 0: causal rows of a short context) gives
+    // o = 0, lse = -inf.
+    const size_t prow0 = ((size_t)h * p.slots + slot) * GQ;
     auto out_row = [&](int x) {
         const int xi = x / G;
         return ((size_t)b * QL + xi) * p.n_q + (size_t)h * G + (x - xi * G);
@@ -840,7 +862,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
             }
             float* dst = (n_seg == 1)
                              ? p.out + out_row(head) * kHeadDim + 8 * j
-                             : p.part_o + ((vrow0 + head) * p.max_parts + seg) * kHeadDim + 8 * j;
+                             : p.part_o + (prow0 + head) * kHeadDim + 8 * j;
             *(f32x4_t*)dst = o0;
             *(f32x4_t*)(dst + 4) = o1;
         }
@@ -850,7 +872,7 @@ __device__ __forceinline__ void kivi_segment(const KiviSplitParams& kp, const in
         if (n_seg == 1) {
             if (p.lse) p.lse[out_row(j)] = l2 * kLn2;
         } else {
-            p.part_lse[(vrow0 + j) * p.max_parts + seg] = l2;
+            p.part_lse[prow0 + j] = l2;
         }
     }
 }
@@ -863,8 +885,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SHARE ? 2 :
     const int wid = threadIdx.x >> 6;
     lds_u8* smeta = (lds_u8*)&s_meta[wid][0];
     const lds_u8* szero = (const lds_u8*)&s_zero[0];
-    for_each_segment<kKiviGroup>(kp.s, [&](int b, int h, int page0, int page1, int seg, int n_seg, int lane) {
-        kivi_segment<BITS, SHARE>(kp, b, h, page0, page1, seg, n_seg, lane, smeta, szero);
+    for_each_segment<kKiviGroup>(kp.s, [&](int b, int h, int page0, int page1, int slot, int n_seg, int lane) {
+        kivi_segment<BITS, SHARE>(kp, b, h, page0, page1, slot, n_seg, lane, smeta, szero);
     });
 }
 

@@ -9,6 +9,7 @@
 #include <mutex>
 
 #include "kvq_internal.h"
+#include "split_plan.h"
 
 using namespace kvq;
 
@@ -45,62 +46,57 @@ int kivi_bits(int dtype) { return dtype == KVQ_INT2_KIVI ? 2 : 4; }
 // Descriptor checks.  kivi: whether the KIVI window layout is accepted (the
 // decode entry points) or refused as unsupported (the slot-based append).
 kvq_status check_cache(const kvq_cache* c, bool kivi) {
-    if (!c) return KVQ_ERR_INVALID;
+    if (!c) return KVQ_EINVAL;
     if (c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2 && c->dtype != KVQ_INT8_ASYM &&
         !is_kivi(c->dtype))
-        return KVQ_ERR_INVALID;
+        return KVQ_EINVAL;
     if (c->scale_mode < KVQ_SCALE_PER_TENSOR || c->scale_mode > KVQ_SCALE_PER_TOKEN_HEAD)
-        return KVQ_ERR_INVALID;
+        return KVQ_EINVAL;
     if (c->num_pages <= 0 || c->num_kv_heads <= 0 || c->page_size <= 0 || c->head_dim <= 0)
-        return KVQ_ERR_INVALID;
-    if (!c->k_pages || !c->v_pages) return KVQ_ERR_INVALID;
-    if (c->head_dim != kHeadDim) return KVQ_ERR_UNSUPPORTED;
+        return KVQ_EINVAL;
+    if (!c->k_pages || !c->v_pages) return KVQ_EINVAL;
+    if (c->head_dim != kHeadDim) return KVQ_EUNSUPPORTED;
     if (is_kivi(c->dtype)) {
-        if (!kivi) return KVQ_ERR_UNSUPPORTED;
+        if (!kivi) return KVQ_EUNSUPPORTED;
         if (c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD || c->page_size != kKiviGroup)
-            return KVQ_ERR_UNSUPPORTED;
+            return KVQ_EUNSUPPORTED;
         if (!c->k_window || !c->v_window || c->max_seqs <= 0 || c->residual < 0 ||
             c->window_tokens < c->residual + kKiviGroup)
-            return KVQ_ERR_INVALID;
+            return KVQ_EINVAL;
         return KVQ_OK;
     }
     if (c->dtype == KVQ_INT8_ASYM && c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD)
-        return KVQ_ERR_UNSUPPORTED;
-    if (c->page_size != 16 && c->page_size != 32) return KVQ_ERR_UNSUPPORTED;
-    if (c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD && !c->static_scales) return KVQ_ERR_INVALID;
+        return KVQ_EUNSUPPORTED;
+    if (c->page_size != 16 && c->page_size != 32) return KVQ_EUNSUPPORTED;
+    if (c->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD && !c->static_scales) return KVQ_EINVAL;
     return KVQ_OK;
 }
 
 struct Plan {
     int max_pages = 0;     // ceil(max_context_len / page_size)
-    int max_parts = 1;
+    int slots = 1;         // partial slots per KV head
     int min_chunk = 1;
     int forced_chunk = 0;
     size_t off_pfx = 0, off_lse = 0, off_o = 0, total = 0;
 };
 
-Plan make_plan(int page_size, int num_seqs, int num_q_heads, int max_ctx, int partition_pages, int q_len) {
+// Workspace: a 256-byte header (range length, start-up weight), the prefix of
+// item weights [B + 1], then per KV head `slots` partial slots of GQ rows:
+// lse [n_kv][slots][GQ] (log2 domain) and o [n_kv][slots][GQ][128] fp32.
+Plan make_plan(int page_size, int n_kv, int num_seqs, int num_q_heads, int max_ctx, int partition_pages,
+               int q_len) {
     Plan pl;
     pl.max_pages = (max_ctx + page_size - 1) / page_size;
     const int mp = std::max(1, pl.max_pages);
-    if (partition_pages > 0) {
-        const long long need = (mp + (long long)partition_pages - 1) / partition_pages + 1;
-        pl.max_parts = (int)std::max(1LL, std::min<long long>(mp, need));
-        pl.forced_chunk = partition_pages;
-        pl.min_chunk = partition_pages;
-    } else {
-        pl.max_parts = std::min(mp, kMaxParts);
-        pl.min_chunk = kMinChunkPages;
-        if (mp > pl.max_parts) {
-            const int bound = (mp + pl.max_parts - 2) / (pl.max_parts - 1);
-            pl.min_chunk = std::max(pl.min_chunk, bound);
-        }
-    }
-    const size_t rows = (size_t)num_seqs * (size_t)num_q_heads * (size_t)q_len;
+    pl.forced_chunk = partition_pages;
+    pl.min_chunk = partition_pages > 0 ? partition_pages : plan_min_chunk(mp);
+    const long long slots = plan_slots(num_seqs, n_kv, mp, partition_pages);
+    pl.slots = (int)std::min<long long>(slots, 0x7FFFFFFF);
+    const size_t rows = (size_t)n_kv * (size_t)slots * (size_t)(num_q_heads / n_kv) * (size_t)q_len;
     pl.off_pfx = 256;
     pl.off_lse = pl.off_pfx + align256(((size_t)num_seqs + 1) * sizeof(int32_t));
-    pl.off_o = pl.off_lse + align256(rows * pl.max_parts * sizeof(float));
-    pl.total = pl.off_o + align256(rows * pl.max_parts * kHeadDim * sizeof(float));
+    pl.off_o = pl.off_lse + align256(rows * sizeof(float));
+    pl.total = pl.off_o + align256(rows * kHeadDim * sizeof(float));
     return pl;
 }
 
@@ -113,25 +109,27 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
     if (st != KVQ_OK) return st;
     if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || max_pages_per_seq < 0 ||
         partition_pages < 0 || q_len < 1)
-        return KVQ_ERR_INVALID;
-    if (num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID;
-    if (c->attn_flags & ~KVQ_ATTN_FP8_QK) return KVQ_ERR_INVALID;
+        return KVQ_EINVAL;
+    if (num_q_heads % c->num_kv_heads != 0) return KVQ_EINVAL;
+    if (c->attn_flags & ~KVQ_ATTN_FP8_QK) return KVQ_EINVAL;
     if ((c->attn_flags & KVQ_ATTN_FP8_QK) && c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2)
-        return KVQ_ERR_UNSUPPORTED;
-    if (!valid_group(num_q_heads / c->num_kv_heads)) return KVQ_ERR_UNSUPPORTED;
+        return KVQ_EUNSUPPORTED;
+    if (!valid_group(num_q_heads / c->num_kv_heads)) return KVQ_EUNSUPPORTED;
     // the query rows of one KV head (group x positions) form one 16-wide MFMA tile
-    if ((long long)q_len * (num_q_heads / c->num_kv_heads) > 16) return KVQ_ERR_UNSUPPORTED;
+    if ((long long)q_len * (num_q_heads / c->num_kv_heads) > 16) return KVQ_EUNSUPPORTED;
     // KIVI verification: the positions a row cannot see must lie in the fp16
     // window, which holds at least `residual` tokens
-    if (q_len > 1 && is_kivi(c->dtype) && q_len - 1 > c->residual) return KVQ_ERR_UNSUPPORTED;
+    if (q_len > 1 && is_kivi(c->dtype) && q_len - 1 > c->residual) return KVQ_EUNSUPPORTED;
     if ((long long)max_context_len > (long long)max_pages_per_seq * c->page_size)
-        return KVQ_ERR_INVALID;
-    if (num_seqs > 16383) return KVQ_ERR_UNSUPPORTED;   // prefix table lives in LDS
-    if (is_kivi(c->dtype) && num_seqs > c->max_seqs) return KVQ_ERR_INVALID;
+        return KVQ_EINVAL;
+    if (num_seqs > 16383) return KVQ_EUNSUPPORTED;   // prefix table lives in LDS
+    if (is_kivi(c->dtype) && num_seqs > c->max_seqs) return KVQ_EINVAL;
     if (num_seqs == 0) return KVQ_OK;
-    if (!q || !block_table || !context_lens || !out || !workspace) return KVQ_ERR_INVALID;
-    *plan = make_plan(c->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, q_len);
-    if (workspace_bytes < plan->total) return KVQ_ERR_WORKSPACE;
+    if (!q || !block_table || !context_lens || !out || !workspace) return KVQ_EINVAL;
+    *plan = make_plan(c->page_size, c->num_kv_heads, num_seqs, num_q_heads, max_context_len, partition_pages,
+                      q_len);
+    if (plan->slots == 0x7FFFFFFF) return KVQ_EUNSUPPORTED;   // forced ranges far too short for the batch
+    if (workspace_bytes < plan->total) return KVQ_EWORKSPACE;
     return KVQ_OK;
 }
 
@@ -165,7 +163,7 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     p.max_pages_per_seq = max_pages_per_seq;
     p.max_ctx = max_context_len;
     p.max_pages = pl.max_pages;
-    p.max_parts = pl.max_parts;
+    p.slots = pl.slots;
     p.min_chunk = pl.min_chunk;
     p.forced_chunk = pl.forced_chunk;
     p.q_len = q_len;
@@ -179,9 +177,9 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     const bool q8 = (c->attn_flags & KVQ_ATTN_FP8_QK) != 0;
     hipError_t e = kivi ? kivi_split_occupancy(kivi_bits(c->dtype), p.group * q_len, lds, &per_cu)
                         : split_occupancy(c->dtype, is_static, c->page_size, q8, lds, &per_cu);
-    if (e != hipSuccess) return KVQ_ERR_HIP;
+    if (e != hipSuccess) return KVQ_EHIP;
     const int cus = device_cus();
-    if (cus <= 0 || per_cu <= 0) return KVQ_ERR_HIP;
+    if (cus <= 0 || per_cu <= 0) return KVQ_EHIP;
     // FP8: one workgroup (one wave per SIMD) per CU, although two fit: with
     // two waves per SIMD the memory system holds more requests than it
     // serves best, and the measured kernel time is about 2% longer
@@ -201,7 +199,7 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     } else {
         e = launch_split(c->dtype, is_static, c->page_size, q8, p, grid, lds, stream);
     }
-    return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+    return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
 
 kvq_status run_reduce(const kvq_cache* c, int32_t num_seqs, int32_t num_q_heads, const Plan& pl,
@@ -218,9 +216,27 @@ kvq_status run_reduce(const kvq_cache* c, int32_t num_seqs, int32_t num_q_heads,
     r.n_q = num_q_heads;
     r.n_kv = c->num_kv_heads;
     r.group = num_q_heads / c->num_kv_heads;
-    r.max_parts = pl.max_parts;
+    r.slots = pl.slots;
     r.q_len = q_len;
-    return launch_reduce(r, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+    return launch_reduce(r, stream) == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+// One decode step: split kernel, then reduce kernel (q_len 1).
+kvq_status decode_step(const kvq_cache* cache, const void* q, int32_t num_seqs,
+                             int32_t num_q_heads, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* context_lens,
+                             int32_t max_context_len, float softmax_scale, int32_t partition_pages,
+                             void* workspace, size_t workspace_bytes, float* out, float* lse,
+                             hipStream_t stream) {
+    Plan pl;
+    kvq_status st = check_decode(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq,
+                                 context_lens, max_context_len, partition_pages, workspace,
+                                 workspace_bytes, out, 1, &pl);
+    if (st != KVQ_OK || num_seqs == 0) return st;
+    st = run_split(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
+                   max_context_len, softmax_scale, pl, workspace, out, lse, 1, stream);
+    if (st != KVQ_OK) return st;
+    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, 1, stream);
 }
 
 }  // namespace
@@ -260,9 +276,9 @@ kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,
                       const int32_t* slot_mapping, int32_t num_tokens, hipStream_t stream) {
     kvq_status st = check_cache(cache, false);
     if (st != KVQ_OK) return st;
-    if (num_tokens < 0) return KVQ_ERR_INVALID;
+    if (num_tokens < 0) return KVQ_EINVAL;
     if (num_tokens == 0) return KVQ_OK;
-    if (!k || !v || !slot_mapping) return KVQ_ERR_INVALID;
+    if (!k || !v || !slot_mapping) return KVQ_EINVAL;
     AppendParams p{};
     p.k = (const uint16_t*)k;
     p.v = (const uint16_t*)v;
@@ -281,7 +297,7 @@ kvq_status kvq_append(const kvq_cache* cache, const void* k, const void* v,
     p.static_kv_stride = cache->scale_mode == KVQ_SCALE_PER_HEAD ? cache->num_kv_heads : 1;
     const bool is_static = cache->scale_mode != KVQ_SCALE_PER_TOKEN_HEAD;
     if (launch_append(cache->dtype, is_static, cache->page_size, p, stream) != hipSuccess)
-        return KVQ_ERR_HIP;
+        return KVQ_EHIP;
     return KVQ_OK;
 }
 
@@ -289,17 +305,17 @@ kvq_status kvq_kivi_append(const kvq_cache* cache, const void* k, const void* v,
                            const int32_t* token_offsets, const int32_t* context_lens,
                            const int32_t* block_table, int32_t max_pages_per_seq, int32_t num_seqs,
                            int32_t max_new_tokens, hipStream_t stream) {
-    if (!cache) return KVQ_ERR_INVALID;
+    if (!cache) return KVQ_EINVAL;
     if (!is_kivi(cache->dtype)) return check_cache(cache, false) == KVQ_OK
-                                                  ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
+                                                  ? KVQ_EUNSUPPORTED : KVQ_EINVAL;
     kvq_status st = check_cache(cache, true);
     if (st != KVQ_OK) return st;
-    if (num_seqs < 0 || max_new_tokens < 0 || max_pages_per_seq < 0) return KVQ_ERR_INVALID;
-    if (num_seqs > cache->max_seqs) return KVQ_ERR_INVALID;
-    if (num_seqs > 65535 || cache->num_kv_heads > 65535) return KVQ_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || max_new_tokens < 0 || max_pages_per_seq < 0) return KVQ_EINVAL;
+    if (num_seqs > cache->max_seqs) return KVQ_EINVAL;
+    if (num_seqs > 65535 || cache->num_kv_heads > 65535) return KVQ_EUNSUPPORTED;
     if (num_seqs == 0 || max_new_tokens == 0) return KVQ_OK;
     if (!k || !v || !token_offsets || !context_lens || !block_table || max_pages_per_seq == 0)
-        return KVQ_ERR_INVALID;
+        return KVQ_EINVAL;
     KiviAppendParams p{};
     p.k = (const uint16_t*)k;
     p.v = (const uint16_t*)v;
@@ -322,19 +338,21 @@ kvq_status kvq_kivi_append(const kvq_cache* cache, const void* k, const void* v,
     p.max_new = max_new_tokens;
     p.num_pages = cache->num_pages;
     p.bits = kivi_bits(cache->dtype);
-    return launch_kivi_append(p, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+    return launch_kivi_append(p, stream) == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
 
 kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
                                       int32_t num_q_heads, int32_t max_context_len,
                                       int32_t partition_pages, size_t* bytes) {
-    if (!bytes) return KVQ_ERR_INVALID;
+    if (!bytes) return KVQ_EINVAL;
     *bytes = 0;
-    if (!cache) return KVQ_ERR_INVALID;
+    if (!cache) return KVQ_EINVAL;
     if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_pages < 0)
-        return KVQ_ERR_INVALID;
-    if (cache->page_size <= 0) return KVQ_ERR_INVALID;
-    *bytes = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, 1)
+        return KVQ_EINVAL;
+    if (cache->page_size <= 0 || cache->num_kv_heads <= 0 || num_q_heads % cache->num_kv_heads)
+        return KVQ_EINVAL;
+    *bytes = make_plan(cache->page_size, cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
+                       partition_pages, 1)
                  .total;
     return KVQ_OK;
 }
@@ -357,15 +375,16 @@ kvq_status kvq_decode_split(const kvq_cache* cache, const void* q, int32_t num_s
 kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t num_q_heads,
                              int32_t max_context_len, int32_t partition_pages, void* workspace,
                              size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
-    if (!cache) return KVQ_ERR_INVALID;
+    if (!cache) return KVQ_EINVAL;
     if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_pages < 0)
-        return KVQ_ERR_INVALID;
+        return KVQ_EINVAL;
     if (cache->num_kv_heads <= 0 || cache->page_size <= 0 || num_q_heads % cache->num_kv_heads)
-        return KVQ_ERR_INVALID;
+        return KVQ_EINVAL;
     if (num_seqs == 0) return KVQ_OK;
-    if (!workspace || !out) return KVQ_ERR_INVALID;
-    Plan pl = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, 1);
-    if (workspace_bytes < pl.total) return KVQ_ERR_WORKSPACE;
+    if (!workspace || !out) return KVQ_EINVAL;
+    Plan pl = make_plan(cache->page_size, cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
+                        partition_pages, 1);
+    if (workspace_bytes < pl.total) return KVQ_EWORKSPACE;
     return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, 1, stream);
 }
 
@@ -375,27 +394,37 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
                                 int32_t max_context_len, float softmax_scale,
                                 int32_t partition_pages, void* workspace, size_t workspace_bytes,
                                 float* out, float* lse, hipStream_t stream) {
-    Plan pl;
-    kvq_status st = check_decode(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq,
-                                 context_lens, max_context_len, partition_pages, workspace,
-                                 workspace_bytes, out, 1, &pl);
-    if (st != KVQ_OK || num_seqs == 0) return st;
-    st = run_split(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
-                   max_context_len, softmax_scale, pl, workspace, out, lse, 1, stream);
-    if (st != KVQ_OK) return st;
-    return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, 1, stream);
+    if (cache && is_kivi(cache->dtype)) return KVQ_EUNSUPPORTED;   // kvq_kivi_decode_attention
+    return decode_step(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
+                       max_context_len, softmax_scale, partition_pages, workspace, workspace_bytes, out, lse,
+                       stream);
+}
+
+kvq_status kvq_kivi_decode_attention(const kvq_cache* cache, const void* q, int32_t num_seqs,
+                                     int32_t num_q_heads, const int32_t* block_table,
+                                     int32_t max_pages_per_seq, const int32_t* context_lens,
+                                     int32_t max_context_len, float softmax_scale,
+                                     int32_t partition_pages, void* workspace, size_t workspace_bytes,
+                                     float* out, float* lse, hipStream_t stream) {
+    if (!cache) return KVQ_EINVAL;
+    if (!is_kivi(cache->dtype)) return check_cache(cache, false) == KVQ_OK ? KVQ_EUNSUPPORTED : KVQ_EINVAL;
+    return decode_step(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
+                       max_context_len, softmax_scale, partition_pages, workspace, workspace_bytes, out, lse,
+                       stream);
 }
 
 kvq_status kvq_verify_workspace_bytes(const kvq_cache* cache, int32_t num_seqs, int32_t q_len,
                                       int32_t num_q_heads, int32_t max_context_len,
                                       int32_t partition_pages, size_t* bytes) {
-    if (!bytes) return KVQ_ERR_INVALID;
+    if (!bytes) return KVQ_EINVAL;
     *bytes = 0;
-    if (!cache) return KVQ_ERR_INVALID;
+    if (!cache) return KVQ_EINVAL;
     if (num_seqs < 0 || q_len < 1 || num_q_heads <= 0 || max_context_len < 0 || partition_pages < 0)
-        return KVQ_ERR_INVALID;
-    if (cache->page_size <= 0) return KVQ_ERR_INVALID;
-    *bytes = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, q_len)
+        return KVQ_EINVAL;
+    if (cache->page_size <= 0 || cache->num_kv_heads <= 0 || num_q_heads % cache->num_kv_heads)
+        return KVQ_EINVAL;
+    *bytes = make_plan(cache->page_size, cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
+                       partition_pages, q_len)
                  .total;
     return KVQ_OK;
 }
@@ -417,16 +446,17 @@ kvq_status kvq_verify_split(const kvq_cache* cache, const void* q, int32_t num_s
 kvq_status kvq_verify_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
                              int32_t max_context_len, int32_t partition_pages, void* workspace,
                              size_t workspace_bytes, float* out, float* lse, hipStream_t stream) {
-    if (!cache) return KVQ_ERR_INVALID;
+    if (!cache) return KVQ_EINVAL;
     if (num_seqs < 0 || q_len < 1 || num_q_heads <= 0 || max_context_len < 0 || partition_pages < 0)
-        return KVQ_ERR_INVALID;
+        return KVQ_EINVAL;
     if (cache->num_kv_heads <= 0 || cache->page_size <= 0 || num_q_heads % cache->num_kv_heads)
-        return KVQ_ERR_INVALID;
-    if ((long long)q_len * (num_q_heads / cache->num_kv_heads) > 16) return KVQ_ERR_UNSUPPORTED;
+        return KVQ_EINVAL;
+    if ((long long)q_len * (num_q_heads / cache->num_kv_heads) > 16) return KVQ_EUNSUPPORTED;
     if (num_seqs == 0) return KVQ_OK;
-    if (!workspace || !out) return KVQ_ERR_INVALID;
-    Plan pl = make_plan(cache->page_size, num_seqs, num_q_heads, max_context_len, partition_pages, q_len);
-    if (workspace_bytes < pl.total) return KVQ_ERR_WORKSPACE;
+    if (!workspace || !out) return KVQ_EINVAL;
+    Plan pl = make_plan(cache->page_size, cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
+                        partition_pages, q_len);
+    if (workspace_bytes < pl.total) return KVQ_EWORKSPACE;
     return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, q_len, stream);
 }
 
@@ -447,38 +477,13 @@ kvq_status kvq_verify_attention(const kvq_cache* cache, const void* q, int32_t n
     return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, q_len, stream);
 }
 
-kvq_status kvq_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
-    if (n < 0) return KVQ_ERR_INVALID;
-    if (n == 0) return KVQ_OK;
-    if (!x || !codes) return KVQ_ERR_INVALID;
-    return launch_e4m3_encode(x, codes, n, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
-}
-
-kvq_status kvq_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream) {
-    if (n < 0) return KVQ_ERR_INVALID;
-    if (n == 0) return KVQ_OK;
-    if (!x || !codes) return KVQ_ERR_INVALID;
-    return launch_e5m2_encode(x, codes, n, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
-}
-
-kvq_status kvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks_per_cu,
-                          hipStream_t stream) {
-    if (bytes < 0 || (bytes & 15) || blocks_per_cu <= 0 || blocks_per_cu > 32) return KVQ_ERR_INVALID;
-    if (bytes == 0) return KVQ_OK;
-    if (!buf || !sink) return KVQ_ERR_INVALID;
-    const int cus = device_cus();
-    if (cus <= 0) return KVQ_ERR_HIP;
-    return launch_read_probe(buf, bytes, sink, cus * blocks_per_cu, stream) == hipSuccess ? KVQ_OK
-                                                                                          : KVQ_ERR_HIP;
-}
-
 const char* kvq_status_string(kvq_status s) {
     switch (s) {
         case KVQ_OK: return "ok";
-        case KVQ_ERR_INVALID: return "invalid argument";
-        case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
-        case KVQ_ERR_WORKSPACE: return "workspace too small";
-        case KVQ_ERR_HIP: return "HIP runtime error";
+        case KVQ_EINVAL: return "invalid argument";
+        case KVQ_EUNSUPPORTED: return "unsupported configuration";
+        case KVQ_EWORKSPACE: return "workspace too small";
+        case KVQ_EHIP: return "HIP runtime error";
     }
     return "unknown status";
 }

@@ -9,7 +9,8 @@
 namespace kvq {
 
 constexpr int kHeadDim = 128;
-constexpr int kMaxParts = 32;      // partial results kept per (sequence, query head)
+constexpr int kMaxSegments = 128;  // most pieces one (sequence, KV head) item is cut into (automatic plan)
+constexpr int kMaxRanges = 2048;   // most work ranges (over all KV heads) of one automatic plan
 constexpr int kMinChunkPages = 4;  // smallest automatic work range per wave
 constexpr int kSegmentCost = 8;    // start-up of a segment, in pages, for ragged batches (measured best on the mixed workload)
 constexpr int kSplitThreads = 256; // 4 waves per workgroup
@@ -37,14 +38,15 @@ struct SplitParams {
     const uint16_t* static_scales; // see AppendParams
     float* out;                    // fp32 [B][q_len][Hq][128]
     float* lse;                    // fp32 [B][q_len][Hq] or null
-    float* part_o;                 // fp32 [B][n_kv][group q_len][max_parts][128]
-    float* part_lse;               // fp32 [B][n_kv][group q_len][max_parts] (log2 domain)
+    float* part_o;                 // fp32 [n_kv][slots][group q_len][128]
+    float* part_lse;               // fp32 [n_kv][slots][group q_len] (log2 domain)
     int32_t* ws_header;            // [0] = range length, [1] = per-item start-up weight
     int32_t* ws_pfx;               // [B + 1] exclusive prefix of pages per sequence
     long long rec_k, rec_v;
     int num_seqs, n_q, n_kv, group, num_pages;
     int max_pages_per_seq, max_ctx, max_pages;
-    int max_parts, min_chunk, forced_chunk, total_waves;
+    int slots;                     // partial-result slots per KV head (>= ranges per head + num_seqs)
+    int min_chunk, forced_chunk, total_waves;
     int q_len;                     // query positions per sequence (1: decode; >1: causal verification)
     int static_head_stride, static_kv_stride;
     float score_scale;             // softmax_scale * log2(e)
@@ -57,7 +59,7 @@ struct ReduceParams {
     const int32_t* ws_pfx;
     float* out;
     float* lse;
-    int num_seqs, n_q, n_kv, group, max_parts;
+    int num_seqs, n_q, n_kv, group, slots;
     int q_len;
 };
 
@@ -91,11 +93,6 @@ hipError_t launch_split(int dtype, bool static_scale, int page_size, bool q8, co
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
 hipError_t split_occupancy(int dtype, bool static_scale, int page_size, bool q8, size_t lds_bytes,
                            int* blocks_per_cu);
-hipError_t launch_e4m3_encode(const float* x, uint8_t* codes, long long n, hipStream_t stream);
-hipError_t launch_e5m2_encode(const float* x, uint8_t* codes, long long n, hipStream_t stream);
-
-hipError_t launch_read_probe(const void* buf, long long bytes, uint32_t* sink, int grid, hipStream_t stream);
-
 hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream);
 hipError_t launch_kivi_split(const KiviSplitParams& p, int grid, size_t lds_bytes,
                              hipStream_t stream);

@@ -107,11 +107,14 @@ def read_seq(bt: Built, b: int, which: int, dtype: int, mode: int):
 
 def oracle_seq(bt: Built, b: int, mode: int = kvq.KVQ_SCALE_PER_TOKEN_HEAD, static_kv=None,
                softmax_scale=None, q8: Optional[bool] = None) -> Dict[str, np.ndarray]:
-    """Oracle result for sequence b from the same seeded inputs (generated on the CPU).
-    q8 (default: the cache's KVQ_ATTN_FP8_QK flag): FP8-domain QK reference."""
+    """Oracle result for sequence b from the same seeded inputs.  The generator
+    is counter-based and bitwise device-independent (tests/test_gpu_inputs.py),
+    so the inputs are drawn on the cache's device and copied to the host; the
+    oracle itself runs on the CPU.  q8 (default: the cache's KVQ_ATTN_FP8_QK
+    flag): FP8-domain QK reference."""
     w = bt.w
     T = int(bt.lens[b])
-    k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
+    k, v = synthetic.gen_kv(w, b, 0, T, bt.q.device)
     q = synthetic.gen_q(w, "cpu", batch=len(bt.lens))[b]
     if q8 is None:
         q8 = bool(bt.cache.attn_flags & kvq.KVQ_ATTN_FP8_QK)
@@ -188,10 +191,12 @@ def build_kivi(w: synthetic.Workload, lens: Optional[np.ndarray] = None, plan=No
 
 
 def kivi_oracle_seq(bt: BuiltKivi, b: int, softmax_scale=None):
-    """Oracle KIVI state of every KV head of sequence b plus its fp64 attention."""
+    """Oracle KIVI state of every KV head of sequence b plus its fp64 attention
+    (inputs drawn on the cache's device, as in oracle_seq; the oracle runs on
+    the CPU)."""
     w = bt.w
     T = int(bt.lens[b])
-    k, v = synthetic.gen_kv(w, b, 0, T, "cpu")
+    k, v = synthetic.gen_kv(w, b, 0, T, bt.q.device)
     k16 = O.bf16_to_f16_bits(u16(k))          # [T][n_kv][d]
     v16 = O.bf16_to_f16_bits(u16(v))
     heads = [O.kivi_stream(k16[:, h], v16[:, h], w.resid, w.page_size, w.kivi_bits) for h in range(w.num_kv_heads)]
@@ -257,7 +262,7 @@ def run_decode_kivi(bt: BuiltKivi, partition_pages: int = 0, softmax_scale=None)
                      dtype=torch.uint8, device=bt.q.device)
     out = torch.full((B, Hq, bt.w.head_dim), float("nan"), dtype=torch.float32, device=bt.q.device)
     lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=bt.q.device)
-    kvq.decode_attention(bt.cache, bt.q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws, out, lse,
-                         partition_pages)
+    kvq.kivi_decode_attention(bt.cache, bt.q, bt.block_table, bt.context_lens, bt.max_ctx, scale, ws, out, lse,
+                              partition_pages)
     torch.cuda.synchronize()
     return out, lse

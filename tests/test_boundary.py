@@ -1,23 +1,29 @@
-"""The C-ABI boundary on the CPU: the library loads, exports what include/kvq.h
-declares, sizes records and workspaces, and rejects invalid requests before
-any HIP call (no kernel is launched by these tests)."""
+"""The C-ABI boundary on the CPU: the libraries load, export what include/kvq.h
+and include/kvq_testing.h declare, size records and workspaces, plan the
+split as intended, and reject invalid requests before any HIP call (no kernel
+is launched by these tests)."""
 import ctypes
 import os
 import re
+
+import numpy as np
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvq.h")
+TESTING_HEADER = os.path.join(ROOT, "include", "kvq_testing.h")
 
 kvq = pytest.importorskip("quantized_kv_cache_08_amd")
+from quantized_kv_cache_08_amd import testing as KT  # noqa: E402
 
-OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+# status values (include/kvq.h)
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
 FAKE = ctypes.c_void_p(0x1000)      # never dereferenced: every call below fails validation first
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
 
@@ -29,11 +35,39 @@ def L():
     return kvq.lib()
 
 
-def test_exports_every_declared_symbol(L):
+@pytest.fixture(scope="module")
+def T():
+    if not os.path.exists(KT.LIB_PATH):
+        pytest.fail("libkvq_testing.so is not built (run quantized_kv_cache_08_amd/build.py)")
+    return KT.lib()
+
+
+def test_exports_every_declared_symbol(L, T):
     names = _declared()
-    assert "kvq_append" in names and "kvq_decode_attention" in names
+    for n in ("kvq_append", "kvq_kivi_append", "kvq_decode_attention", "kvq_kivi_decode_attention",
+              "kvq_decode_workspace_bytes", "kvq_status_string"):
+        assert n in names, n
     for n in names:
         assert hasattr(L, n), n
+    tnames = _declared(TESTING_HEADER)
+    assert set(tnames) == {"kvq_e4m3_encode", "kvq_e5m2_encode", "kvq_read_probe", "kvq_plan_stats"}
+    for n in tnames:
+        assert hasattr(T, n), n
+
+
+def test_product_library_carries_no_test_hooks(L):
+    """The encoders, the read probe and the plan query live in libkvq_testing.so only."""
+    for n in ("kvq_e4m3_encode", "kvq_e5m2_encode", "kvq_read_probe", "kvq_plan_stats"):
+        assert not hasattr(L, n), n
+
+
+def test_status_values_and_strings(L):
+    assert (kvq.KVQ_OK, kvq.KVQ_EINVAL, kvq.KVQ_EUNSUPPORTED, kvq.KVQ_EWORKSPACE, kvq.KVQ_EHIP) == (0, -1, -2, -3, -4)
+    assert kvq.status_string(0) == "ok"
+    assert "invalid" in kvq.status_string(-1)
+    assert "unsupported" in kvq.status_string(-2)
+    assert "workspace" in kvq.status_string(-3)
+    assert "HIP" in kvq.status_string(-4)
 
 
 def test_record_bytes(L):
@@ -148,26 +182,104 @@ def test_kivi_validation(L, dtype):
     assert _kivi_append(L, d, maxp=0) == INVALID
     assert _kivi_append(L, d, num_seqs=0) == OK
     assert _kivi_append(L, d, max_new=0) == OK
-    # decode on a KIVI cache: same checks as FP8 / INT8 plus the window slots
-    assert _decode(L, d, num_seqs=5, hq=16, maxp=4, max_ctx=128) == INVALID
-    assert _decode(L, d, hq=16, maxp=1, max_ctx=64) == INVALID            # 2 pages of 32 needed
-    assert _decode(L, _kivi_desc(dtype=dtype, v_window=None), hq=16, maxp=4, max_ctx=128) == INVALID
-    assert _decode(L, d, num_seqs=0, hq=16, maxp=4, max_ctx=128) == OK
-    assert _decode(L, d, hq=16, maxp=4, max_ctx=128, ws_bytes=0) == WORKSPACE
+    # decode on a KIVI cache (kvq_kivi_decode_attention): same checks as FP8 /
+    # INT8 plus the window slots; the FP8 / INT8 entry point refuses KIVI
+    # caches, and the KIVI one refuses the others
+    kd = "kvq_kivi_decode_attention"
+    assert _decode(L, d, kd, num_seqs=5, hq=16, maxp=4, max_ctx=128) == INVALID
+    assert _decode(L, d, kd, hq=16, maxp=1, max_ctx=64) == INVALID        # 2 pages of 32 needed
+    assert _decode(L, _kivi_desc(dtype=dtype, v_window=None), kd, hq=16, maxp=4, max_ctx=128) == INVALID
+    assert _decode(L, d, kd, num_seqs=0, hq=16, maxp=4, max_ctx=128) == OK
+    assert _decode(L, d, kd, hq=16, maxp=4, max_ctx=128, ws_bytes=0) == WORKSPACE
+    assert _decode(L, d, num_seqs=0, hq=16, maxp=4, max_ctx=128) == UNSUPPORTED
+    assert _decode(L, _desc(), kd, num_seqs=0) == UNSUPPORTED
+    assert _decode(L, _desc(dtype=7), kd, num_seqs=0) == INVALID
+    # the split / reduce launches take every dtype
+    assert _decode(L, d, "kvq_decode_split", num_seqs=0, hq=16, maxp=4, max_ctx=128) == OK
+
+
+def _ws(L, d, B, hq, ctx, part=0, q_len=1):
+    out = ctypes.c_size_t(0)
+    if q_len == 1:
+        st = L.kvq_decode_workspace_bytes(ctypes.byref(d), B, hq, ctx, part, ctypes.byref(out))
+    else:
+        st = L.kvq_verify_workspace_bytes(ctypes.byref(d), B, q_len, hq, ctx, part, ctypes.byref(out))
+    assert st == OK
+    return out.value
+
+
+def _ws_expected(B, n_kv, group, q_len, slots):
+    """256-byte header, (B + 1) int prefix, then lse and o of n_kv x slots x rows, each part 256-aligned."""
+    a = lambda x: (x + 255) // 256 * 256        # noqa: E731
+    rows = n_kv * slots * group * q_len
+    return 256 + a((B + 1) * 4) + a(rows * 4) + a(rows * 128 * 4)
 
 
 def test_workspace_bytes(L):
-    d = _desc()
+    d = _desc()                                   # 2 KV heads, page 16
+    # automatic plan: at most 2048 ranges over all heads -> 1024 per head, plus
+    # one slot per sequence; each slot holds group x q_len rows of 129 floats
+    assert _ws(L, d, 32, 32, 8192) == _ws_expected(32, 2, 16, 1, 1024 + 32)
+    # a short context bounds the ranges instead: 32 sequences x (1 page + 8) / 4
+    assert _ws(L, d, 32, 32, 16) == _ws_expected(32, 2, 16, 1, 72 + 32)
+    # forced range length: ceil(B (pages + 8) / forced) ranges
+    assert _ws(L, d, 32, 32, 8192, part=64) == _ws_expected(32, 2, 16, 1, -(-32 * 520 // 64) + 32)
+    # the 70B shape (64 sequences, 64 / 8 heads, 32768 tokens): 2048 / 8 ranges per head
+    d8 = _desc(num_kv_heads=8, dtype=2)
+    assert _ws(L, d8, 64, 64, 32768) == _ws_expected(64, 8, 8, 1, 256 + 64)
+    assert _ws(L, d8, 64, 64, 32768) < 12 << 20
+    # verification rows grow with q_len
+    assert _ws(L, d, 32, 8, 8192, q_len=4) == _ws_expected(32, 2, 4, 4, 1024 + 32)
     out = ctypes.c_size_t(0)
-    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 32, 8192, 0, ctypes.byref(out)) == OK
-    ws = out.value
-    # header + prefix table + per (sequence, query head) up to 32 partials of 129 floats
-    assert ws >= 32 * 32 * 32 * 129 * 4
-    assert ws <= 32 * 32 * 32 * 129 * 4 + 4096
-    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 32, 8192, 64, ctypes.byref(out)) == OK
-    assert out.value >= 32 * 32 * (512 // 64 + 1) * 129 * 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), -1, 32, 8192, 0, ctypes.byref(out)) == INVALID
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8192, 0, None) == INVALID
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 4, 7, 8192, 0, ctypes.byref(out)) == INVALID
+
+
+def _plan(lens, n_kv=8, waves=1024, ps=16, max_ctx=None, part=0):
+    lens = np.asarray(lens)
+    return KT.plan_stats(ps, n_kv, waves, lens, int(lens.max()) if max_ctx is None else max_ctx, part)
+
+
+def test_plan_keeps_every_wave_busy():
+    """The split plan on the host (the kernels' own plan functions): every
+    workload of the benchmark gets one range per resident wave, each range
+    holding pages, and a multiple of 32 ranges per head where the batch is
+    uniform (so the heads of one page run on one XCD).  Resident waves on the
+    MI355X: 256 CUs x 1 workgroup (FP8, INT8) or 2 (KIVI, groups <= 8) x 4."""
+    # KIVI, 4 x 131072 tokens in 32-token pages, 2048 waves: 256 ranges per head
+    p = _plan([131072] * 4, waves=2048, ps=32)
+    assert p["ranges_per_head"] * 8 == 2048 and p["busy_ranges_per_head"] == 256
+    assert p["chunk"] == 64 and p["max_segments_per_item"] == 64
+    assert p["slots_used"] <= p["slots"]
+    # 70B shape (INT8): 64 x 32768 tokens, 1024 waves
+    p = _plan([32768] * 64)
+    assert p["ranges_per_head"] == p["busy_ranges_per_head"] == 128 and p["chunk"] == 1024
+    assert p["max_segments_per_item"] == 2
+    # 8B shape (FP8): 32 x 8192
+    p = _plan([8192] * 32)
+    assert p["ranges_per_head"] == p["busy_ranges_per_head"] == 128
+    # mixed chat lengths (ragged: start-up weight 8 per item)
+    import synthetic
+    w = synthetic.WORKLOADS["mixed"]
+    p = _plan(synthetic.seq_lens(w), max_ctx=w.context)
+    assert p["cost"] == 8 and p["busy_ranges_per_head"] >= 127 and p["slots_used"] <= p["slots"]
+
+
+def test_plan_bounds_segments_and_slots():
+    """One long sequence beside short ones: the item is cut into at most 128
+    pieces; slots stay within what the workspace holds, also for forced
+    range lengths."""
+    p = _plan([131072, 1], waves=1024)
+    assert p["max_segments_per_item"] <= 128 and p["slots_used"] <= p["slots"]
+    p = _plan([131072] + [17] * 300, n_kv=3, waves=1024)
+    assert p["max_segments_per_item"] <= 128 and p["slots_used"] <= p["slots"]
+    for part in (1, 3, 7, 64):
+        p = _plan([1000, 1, 450, 161, 0], n_kv=2, part=part)
+        assert p["chunk"] == part and p["slots_used"] <= p["slots"]
+    # an empty batch has no ranges
+    p = _plan([0, 0], max_ctx=16)
+    assert p["ranges_per_head"] == 0 and p["segments_per_head"] == 0
 
 
 def _verify(L, desc, num_seqs=2, q_len=4, hq=8, maxp=4, max_ctx=64, part=0, ws=FAKE, ws_bytes=1 << 30,
@@ -198,7 +310,7 @@ def test_verify_validation(L):
     assert L.kvq_verify_workspace_bytes(ctypes.byref(d), 32, 4, 8, 8192, 0, ctypes.byref(out4)) == OK
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 8, 8192, 0, ctypes.byref(dec)) == OK
     assert out1.value == dec.value
-    assert out4.value >= 4 * 32 * 8 * 32 * 129 * 4
+    assert out4.value > 3 * out1.value
     assert L.kvq_verify_workspace_bytes(ctypes.byref(d), 32, 0, 8, 8192, 0, ctypes.byref(out4)) == INVALID
 
 
@@ -219,17 +331,16 @@ def test_e5m2_cache_and_encoder_validation(L):
     assert _append(L, _desc(dtype=4), n=0) == OK
     assert _append(L, _desc(dtype=6)) == INVALID                        # no such dtype
     assert _append(L, _desc(dtype=5)) == UNSUPPORTED                    # INT2 KIVI: kvq_kivi_append
-    assert L.kvq_e5m2_encode(FAKE, FAKE, -1, None) == INVALID
-    assert L.kvq_e5m2_encode(FAKE, FAKE, 0, None) == OK
-    assert L.kvq_e5m2_encode(None, FAKE, 5, None) == INVALID
+    T = KT.lib()
+    assert T.kvq_e5m2_encode(FAKE, FAKE, -1, None) == INVALID
+    assert T.kvq_e5m2_encode(FAKE, FAKE, 0, None) == OK
+    assert T.kvq_e5m2_encode(None, FAKE, 5, None) == INVALID
 
 
-def test_encode_and_status(L):
-    assert L.kvq_e4m3_encode(FAKE, FAKE, -1, None) == INVALID
-    assert L.kvq_e4m3_encode(FAKE, FAKE, 0, None) == OK
-    assert L.kvq_e4m3_encode(None, FAKE, 5, None) == INVALID
-    assert kvq.status_string(0) == "ok"
-    assert "workspace" in kvq.status_string(3)
+def test_encode_validation(T):
+    assert T.kvq_e4m3_encode(FAKE, FAKE, -1, None) == INVALID
+    assert T.kvq_e4m3_encode(FAKE, FAKE, 0, None) == OK
+    assert T.kvq_e4m3_encode(None, FAKE, 5, None) == INVALID
 
 
 def test_attn_flags_validation(L):
@@ -251,7 +362,7 @@ def test_attn_flags_validation(L):
     assert _append(L, d, n=0) == OK
     d = _kivi_desc()
     d.attn_flags = kvq.KVQ_ATTN_FP8_QK
-    assert _decode(L, d, num_seqs=0, hq=16, maxp=4, max_ctx=128) == UNSUPPORTED
+    assert _decode(L, d, "kvq_kivi_decode_attention", num_seqs=0, hq=16, maxp=4, max_ctx=128) == UNSUPPORTED
 
 
 def test_binding_rejects_malformed_tensors():
@@ -275,12 +386,11 @@ def test_binding_rejects_malformed_tensors():
     with pytest.raises(TypeError, match="context_lens"):
         kvq.kivi_append(c, bf, bf, i32, torch.zeros(3, dtype=torch.int64), i32.view(4, 1), 1)
     with pytest.raises(TypeError, match="x"):
-        kvq.e4m3_encode(torch.zeros(4, dtype=torch.float64), torch.zeros(4, dtype=torch.uint8))
+        KT.e4m3_encode(torch.zeros(4, dtype=torch.float64), torch.zeros(4, dtype=torch.uint8))
 
 
-def test_read_probe_validation(L):
-    L.kvq_read_probe.restype = ctypes.c_int
-    L.kvq_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+def test_read_probe_validation(T):
+    L = T
     assert L.kvq_read_probe(FAKE, -16, FAKE, 2, None) == INVALID
     assert L.kvq_read_probe(FAKE, 17, FAKE, 2, None) == INVALID          # not a multiple of 16
     assert L.kvq_read_probe(FAKE, 1024, FAKE, 0, None) == INVALID

@@ -171,16 +171,16 @@ def test_fp8qk_mixed_small_shuffled_pool():
     check(bt, out, lse, range(0, 24, 5))
 
 
-def test_fp8qk_llama8b_shape_sampled():
+def test_fp8qk_llama8b_shape_every_sequence():
     """The 8B-shaped batch (B 32, context 8192) with FP8-domain QK, in the
-    benchmark's launch configuration; three sequences checked."""
+    benchmark's launch configuration; every sequence checked."""
     w = synthetic.WORKLOADS["llama8b"]
     say("fp8qk llama8b shape")
     bt = H.build(w)
     bt.cache.attn_flags = kvq.KVQ_ATTN_FP8_QK
     out, lse = H.run_decode(bt)
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
-    check(bt, out, lse, (0, 13, w.batch - 1))
+    check(bt, out, lse, range(w.batch))
 
 
 def test_fp8qk_zero_query_rows():
