@@ -231,6 +231,26 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
                                 int32_t partition_pages, void* workspace, size_t workspace_bytes,
                                 float* out, float* lse, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * kvq_decode_attention with the workspace in a static device array of the
+ * library, 32 MiB per device (allocated when the library's code is loaded on
+ * a device, held until the process ends; its address is looked up on the
+ * first call on each device).  Arguments, results and errors as
+ * kvq_decode_attention; a shape whose workspace
+ * (kvq_decode_workspace_bytes) exceeds 32 MiB returns KVQ_EWORKSPACE and
+ * launches nothing.  The call allocates and frees nothing.  All calls on one
+ * device share that array: calls that overlap in time on one device (other
+ * streams, other threads) race and give wrong results; calls in one stream
+ * are ordered.  Nothing in the array needs to start at zero: each call
+ * writes what it reads. */
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, int32_t num_seqs,
+                                        int32_t num_q_heads, const int32_t* block_table,
+                                        int32_t max_pages_per_seq, const int32_t* context_lens,
+                                        int32_t max_context_len, float softmax_scale,
+                                        int32_t partition_pages, float* out, float* lse,
+                                        hipStream_t stream);
+
 /* KIVI-style decode step (cache->dtype KVQ_INT4_KIVI or KVQ_INT2_KIVI; other
  * caches return KVQ_EUNSUPPORTED): the same attention as
  * kvq_decode_attention over tokens held as 4-bit or 2-bit pages (K quantized

@@ -20,7 +20,7 @@ __all__ = [
     "KVQ_OK", "KVQ_EINVAL", "KVQ_EUNSUPPORTED", "KVQ_EWORKSPACE", "KVQ_EHIP",
     "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
     "verify_workspace_bytes", "verify_attention", "verify_split", "verify_reduce",
-    "decode_attention", "kivi_decode_attention", "decode_split", "decode_reduce", "status_string",
+    "decode_attention", "decode_attention_noalloc", "kivi_decode_attention", "decode_split", "decode_reduce", "status_string",
     "LIB_PATH",
 ]
 
@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         for fn in ("kvq_decode_attention", "kvq_kivi_decode_attention", "kvq_decode_split"):
             getattr(L, fn).restype = ctypes.c_int
             getattr(L, fn).argtypes = _DECODE_ARGS
+        L.kvq_decode_attention_noalloc.restype = ctypes.c_int
+        L.kvq_decode_attention_noalloc.argtypes = _DECODE_ARGS[:10] + [_P, _P, _P]
         L.kvq_decode_reduce.restype = ctypes.c_int
         L.kvq_decode_reduce.argtypes = [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32, _P,
                                         ctypes.c_size_t, _P, _P, _P]
@@ -262,6 +264,27 @@ def decode_attention(cache: Cache, q, block_table, context_lens, max_context_len
     """One decode step over the quantized paged cache (kvq_decode_attention)."""
     _decode("kvq_decode_attention", cache, q, block_table, context_lens, max_context_len, softmax_scale,
             workspace, out, lse, partition_pages, stream)
+
+
+def decode_attention_noalloc(cache: Cache, q, block_table, context_lens, max_context_len: int,
+                             softmax_scale: float, out, lse=None, partition_pages: int = 0,
+                             stream=None) -> None:
+    """kvq_decode_attention with the library's static device workspace (no
+    allocation; calls overlapping on one device race)."""
+    if q.dim() != 3:
+        raise ValueError(f"q: expected [num_seqs][num_q_heads][head_dim], got {tuple(q.shape)}")
+    num_seqs, num_q_heads = int(q.shape[0]), int(q.shape[1])
+    _need(q, "q", torch.bfloat16, (num_seqs, num_q_heads, cache.head_dim))
+    _need(out, "out", torch.float32, (num_seqs, num_q_heads, cache.head_dim))
+    _need(lse, "lse", torch.float32, (num_seqs, num_q_heads), optional=True)
+    _need(context_lens, "context_lens", torch.int32, (num_seqs,))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] < num_seqs:
+        raise ValueError(f"block_table: expected [>= {num_seqs}][max_pages], got {tuple(block_table.shape)}")
+    _check("kvq_decode_attention_noalloc", lib().kvq_decode_attention_noalloc(
+        ctypes.byref(cache.desc), _ptr(q), num_seqs, num_q_heads, _ptr(block_table), int(block_table.shape[1]),
+        _ptr(context_lens), int(max_context_len), float(softmax_scale), int(partition_pages), _ptr(out), _ptr(lse),
+        _stream(stream)))
 
 
 def kivi_decode_attention(cache: Cache, q, block_table, context_lens, max_context_len: int,

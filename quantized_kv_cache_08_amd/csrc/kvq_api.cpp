@@ -19,9 +19,31 @@ constexpr int kMaxDevices = 64;
 
 struct DeviceInfo {
     int cus = 0;
+    void* scratch = nullptr;   // this device's copy of `scratch` (device address)
 };
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_mu;
+
+// Workspace of kvq_decode_attention_noalloc: one copy per device, held from
+// module load to process exit.  In host code `scratch` names a host-side
+// stand-in; only the address hipGetSymbolAddress returns for the current
+// device may reach a kernel.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with it current) and kept; null on a HIP error.
+void* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_dev[dev].scratch) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_dev[dev].scratch = ptr;
+    }
+    return g_dev[dev].scratch;
+}
 
 int device_cus() {
     int dev = 0;
@@ -398,6 +420,21 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t n
     return decode_step(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
                        max_context_len, softmax_scale, partition_pages, workspace, workspace_bytes, out, lse,
                        stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, int32_t num_seqs,
+                                        int32_t num_q_heads, const int32_t* block_table,
+                                        int32_t max_pages_per_seq, const int32_t* context_lens,
+                                        int32_t max_context_len, float softmax_scale,
+                                        int32_t partition_pages, float* out, float* lse,
+                                        hipStream_t stream) {
+    if (cache && is_kivi(cache->dtype)) return KVQ_EUNSUPPORTED;
+    void* ws = scratch_ptr();
+    if (!ws) return KVQ_EHIP;
+    // the plan is checked against the array's size: a larger shape returns
+    // KVQ_EWORKSPACE before any launch
+    return decode_step(cache, q, num_seqs, num_q_heads, block_table, max_pages_per_seq, context_lens,
+                       max_context_len, softmax_scale, partition_pages, ws, kScratchBytes, out, lse, stream);
 }
 
 kvq_status kvq_kivi_decode_attention(const kvq_cache* cache, const void* q, int32_t num_seqs,
