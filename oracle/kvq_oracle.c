@@ -13,6 +13,7 @@
 
 #include <float.h>
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
@@ -113,12 +114,13 @@ double kvqo_e4m3_value(uint8_t c)
 }
 
 /* Round to the nearest E4M3 value, ties to the even mantissa, saturating at
- * +-448; the sign of zero is kept (-0 and negatives that round to 0 give 0x80). */
-uint8_t kvqo_e4m3_encode(float y)
+ * +-448; the sign of zero is kept (-0 and negatives that round to 0 give 0x80).
+ * The rule is applied to the exact value y (float32 inputs convert exactly). */
+uint8_t kvqo_e4m3_encode_f64(double y)
 {
     if (isnan(y)) return 0x7F;
     uint8_t sg = signbit(y) ? 0x80 : 0x00;
-    double a = fabs((double)y);
+    double a = fabs(y);
     if (a >= 448.0) return sg | 0x7E;
     if (a < ldexp(1.0, -6)) {                           /* subnormal binade    */
         double m = nearbyint(a * ldexp(1.0, 9));        /* 0 .. 8; 8 = 2^-6    */
@@ -131,6 +133,8 @@ uint8_t kvqo_e4m3_encode(float y)
     if (m == 8.0) { e += 1; m = 0.0; }
     return sg | (uint8_t)(((e + 7) << 3) | (int)m);
 }
+
+uint8_t kvqo_e4m3_encode(float y) { return kvqo_e4m3_encode_f64((double)y); }
 
 void kvqo_e4m3_encode_range(uint32_t first_bits, uint32_t count, uint8_t* codes)
 {
@@ -400,6 +404,106 @@ void kvqo_attention(const double* q, const double* k, const double* v, int64_t T
         }
         for (int i = 0; i < d; ++i) o[i] /= z;
         if (lse) lse[h] = mx + log(z);
+    }
+}
+
+/* ======================================================================= *
+ * Attention with the score-V product in the FP8 domain.  Some backends run   *
+ * QK and the score-V product themselves in FP8 ([daewooki] core concept 3);  *
+ * the pages give no rule for the probabilities, so this reading fixes one:   *
+ *  - scores as above; lambda_t = score_t / ln 2 (log2 units);               *
+ *  - the context is cut into blocks of `block` tokens from token 0; block    *
+ *    c takes the reference mu_c = ceil(max_{t in c} lambda_t) (an integer);  *
+ *  - P_t = 2^(lambda_t - mu_c) * vs_t, the weight of token t relative to its *
+ *    block times the token's V scale (the V row is x^ = vs_t * vcode_t);    *
+ *  - S_c = 2^E_c, the smallest power of two with max_{t in c} P_t <= 448 S_c;*
+ *  - pi_t = E4M3 code of P_t / S_c (nearest-even; never saturates);          *
+ *  - out = sum_t 2^(mu_c - M) S_c e4m3(pi_t) vcode_t / sum_t 2^(lambda_t - M)*
+ *    for any M (the largest mu_c here): the exact attention with each       *
+ *    P_t replaced by its E4M3 value.  lse is the exact one.                  *
+ * vcode: decoded V codes without their scale [T][n_kv][d]; vs [T][n_kv].    *
+ * allowance [n_q][d]: for every token whose P_t / S_c lies within a relative *
+ * 2^-18 of an E4M3 rounding boundary (where a float32 evaluation may take    *
+ * the neighbouring code), one code step times its weight and |vcode|; where  *
+ * the block maximum lies that close to a power-of-two boundary of S_c, the   *
+ * block's subnormal-range codes count one subnormal step of 2 S_c too.      *
+ * All divided by the softmax denominator, like out.                          *
+ * ======================================================================= */
+static int e4m3_neighbour_steps(double y, double* lo_step, double* hi_step, double* lo_mid, double* hi_mid)
+{
+    uint8_t c = kvqo_e4m3_encode_f64(y);              /* y >= 0 here        */
+    double v = kvqo_e4m3_value(c);
+    double vl = c > 0 ? kvqo_e4m3_value((uint8_t)(c - 1)) : v;
+    double vh = c < 0x7E ? kvqo_e4m3_value((uint8_t)(c + 1)) : v;
+    *lo_step = v - vl;
+    *hi_step = vh - v;
+    *lo_mid = 0.5 * (v + vl);
+    *hi_mid = 0.5 * (v + vh);
+    return c;
+}
+
+void kvqo_attention_fp8pv(const double* q, const double* k, const double* vcode, const double* vs,
+                          int64_t T, int n_q, int n_kv, int d, double softmax_scale, int block,
+                          double* out, double* lse, double* allowance)
+{
+    const double amb = ldexp(1.0, -18);
+    int grp = n_q / n_kv;
+    #pragma omp parallel for schedule(static)
+    for (int h = 0; h < n_q; ++h) {
+        int g = h / grp;
+        double* o = out + (int64_t)h * d;
+        double* al = allowance + (int64_t)h * d;
+        for (int i = 0; i < d; ++i) { o[i] = 0.0; al[i] = 0.0; }
+        if (T == 0) { if (lse) lse[h] = -INFINITY; continue; }
+        double* lam = (double*)malloc(sizeof(double) * (size_t)T);
+        for (int64_t t = 0; t < T; ++t) {
+            const double* kt = k + (t * n_kv + g) * d;
+            double sdot = 0.0;
+            for (int i = 0; i < d; ++i) sdot += q[(int64_t)h * d + i] * kt[i];
+            lam[t] = softmax_scale * sdot / M_LN2;
+        }
+        /* M = the largest block reference; L = sum_t 2^(lambda_t - M) */
+        double M = -INFINITY;
+        for (int64_t t = 0; t < T; ++t) if (ceil(lam[t]) > M) M = ceil(lam[t]);
+        double L = 0.0;
+        for (int64_t t = 0; t < T; ++t) L += exp2(lam[t] - M);
+        for (int64_t b0 = 0; b0 < T; b0 += block) {
+            int64_t b1 = b0 + block < T ? b0 + block : T;
+            double mx = -INFINITY;
+            for (int64_t t = b0; t < b1; ++t) if (lam[t] > mx) mx = lam[t];
+            double mu = ceil(mx);
+            double pmax = 0.0;
+            for (int64_t t = b0; t < b1; ++t) {
+                double P = exp2(lam[t] - mu) * vs[t * n_kv + g];
+                if (P > pmax) pmax = P;
+            }
+            if (pmax == 0.0) continue;
+            /* smallest E with pmax <= 448 * 2^E (exact comparisons) */
+            int E = ilogb(pmax) - 8;
+            while (pmax > ldexp(448.0, E)) ++E;
+            while (pmax <= ldexp(448.0, E - 1)) --E;
+            double S = ldexp(1.0, E);
+            int s_edge = fabs(pmax - ldexp(448.0, E - 1)) <= amb * pmax;   /* S or 2 S */
+            double wgt = S * exp2(mu - M);
+            for (int64_t t = b0; t < b1; ++t) {
+                double y = exp2(lam[t] - mu) * vs[t * n_kv + g] / S;       /* exact division */
+                double ls, hs, lm, hm;
+                uint8_t c = (uint8_t)e4m3_neighbour_steps(y, &ls, &hs, &lm, &hm);
+                double w = kvqo_e4m3_value(c) * wgt;
+                double step = 0.0;
+                if (fabs(y - lm) <= amb * y && ls > 0.0) step = ls;
+                if (fabs(y - hm) <= amb * y && hs > step) step = hs;
+                if (s_edge && y < ldexp(1.0, -5)) step += ldexp(1.0, -8);
+                const double* vt = vcode + (t * n_kv + g) * d;
+                for (int i = 0; i < d; ++i) {
+                    o[i] += w * vt[i];
+                    al[i] += step * wgt * fabs(vt[i]);
+                }
+            }
+        }
+        for (int i = 0; i < d; ++i) { o[i] /= L; al[i] /= L; }
+        if (lse) lse[h] = M * M_LN2 + log(L);
+        free(lam);
     }
 }
 

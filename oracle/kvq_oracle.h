@@ -36,6 +36,7 @@ uint16_t kvqo_f16_rne(double x);     /* IEEE binary16, nearest-even, subnormals 
 void     kvqo_bf16_to_f16_array(const uint16_t* bf16, int64_t n, uint16_t* f16);
 double   kvqo_e4m3_value(uint8_t code);      /* OCP E4M3 (FN): NaN for 0x7F/0xFF */
 uint8_t  kvqo_e4m3_encode(float y);          /* nearest-even, saturating at +-448 */
+uint8_t  kvqo_e4m3_encode_f64(double y);     /* the same rule on an exact double */
 void     kvqo_e4m3_encode_range(uint32_t first_bits, uint32_t count, uint8_t* codes);
 void     kvqo_e4m3_encode_array(const float* y, int64_t n, uint8_t* codes);
 double   kvqo_e5m2_value(uint8_t code);      /* OCP E5M2: +-inf at 0x7C/0xFC, NaN for 0x7D-0x7F/0xFD-0xFF */
@@ -76,6 +77,13 @@ void kvqo_kivi_v(const uint16_t* x16, int64_t nq, int n, int bits,
  * Query head h reads KV head h / (n_q / n_kv).  T == 0: out = 0, lse = -inf. */
 void kvqo_attention(const double* q, const double* k, const double* v, int64_t T,
                     int n_q, int n_kv, int d, double softmax_scale, double* out, double* lse);
+/* Score-V product in the FP8 domain (kvq_oracle.c): P per block of `block`
+ * tokens relative to the block's integer log2 reference, times the V scale,
+ * in E4M3 with a power-of-two block scale.  vcode: V code values without
+ * their scale; vs: V scales [T][n_kv]. */
+void kvqo_attention_fp8pv(const double* q, const double* k, const double* vcode, const double* vs,
+                          int64_t T, int n_q, int n_kv, int d, double softmax_scale, int block,
+                          double* out, double* lse, double* allowance);
 /* merge P partial results (o [P][d], lse [P]) of disjoint token ranges */
 void kvqo_lse_merge(const double* o, const double* lse, int P, int d, double* out, double* lse_out);
 

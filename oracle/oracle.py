@@ -73,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.kvqo_kivi_v.argtypes = [_P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _P, _P, _P]
         L.kvqo_attention.argtypes = [_P, _P, _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_double, _P, _P]
+        L.kvqo_attention_fp8pv.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_double, ctypes.c_int, _P, _P, _P]
+        L.kvqo_e4m3_encode_f64.restype = ctypes.c_uint8
+        L.kvqo_e4m3_encode_f64.argtypes = [ctypes.c_double]
         L.kvqo_lse_merge.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, _P, _P]
         L.kvqo_kv_bytes.restype = ctypes.c_double
         L.kvqo_kv_bytes.argtypes = [ctypes.c_double] * 6
@@ -247,6 +251,38 @@ def attention(q, k, v, softmax_scale: float):
     return out, lse
 
 
+FP8_PV_BLOCK = 32      # tokens per probability block of the FP8 score-V product
+
+
+def attention_fp8pv(q, k, vcode, vs, softmax_scale: float, block: int = FP8_PV_BLOCK):
+    """Attention with the score-V product in the FP8 domain (kvq_oracle.c,
+    kvqo_attention_fp8pv; "FP8 KV Cache부터 INT4 Weight-Only까지", core concept
+    3): each token's weight relative to its 32-token block's integer log2
+    reference, times its V scale, held as an E4M3 code under a power-of-two
+    block scale.  q [Hq][d], k [T][n_kv][d] (fp64, dequantized), vcode
+    [T][n_kv][d] (decoded V codes without their scale), vs [T][n_kv] (V scales).
+    Returns (out [Hq][d], lse [Hq], allowance [Hq][d]); allowance bounds what a
+    float32 evaluation may differ by at the E4M3 rounding boundaries it meets."""
+    q = _c(q, np.float64)
+    k = _c(k, np.float64)
+    vcode = _c(vcode, np.float64)
+    vs = _c(vs, np.float64)
+    Hq, d = q.shape
+    T, n_kv = (k.shape[0], k.shape[1]) if k.ndim == 3 else (0, 1)
+    out = np.empty((Hq, d), dtype=np.float64)
+    lse = np.empty(Hq, dtype=np.float64)
+    allow = np.empty((Hq, d), dtype=np.float64)
+    lib().kvqo_attention_fp8pv(_ptr(q), _ptr(k), _ptr(vcode), _ptr(vs), T, Hq, n_kv, d,
+                               float(np.float32(softmax_scale)), int(block), _ptr(out), _ptr(lse), _ptr(allow))
+    return out, lse, allow
+
+
+def v_code_values(dtype: int, codes) -> np.ndarray:
+    """Decoded FP8 codes (E4M3 or E5M2) without their scale, fp64."""
+    tab = e5m2_table() if dtype == E5M2 else e4m3_table()
+    return tab[np.asarray(codes, dtype=np.uint8)]
+
+
 def lse_merge(o_parts, lse_parts):
     o = _c(o_parts, np.float64)
     l = _c(lse_parts, np.float64)
@@ -274,21 +310,38 @@ def fp8_query(q_bf16) -> np.ndarray:
     return dequantize_rows(FP8, c, s)
 
 
+def _attend(q, res, dtype: int, scale: float, pv8: bool, n_vis=None):
+    """Attention of q over the first n_vis cached tokens of a quantized_cache
+    result: plain (fp64 on the dequantized cache) or FP8 score-V (pv8).
+    Returns (out, lse, allowance or None)."""
+    T = res["k_hat"].shape[0]
+    n = T if n_vis is None else n_vis
+    if not pv8:
+        out, lse = attention(q, res["k_hat"][:n], res["v_hat"][:n], scale)
+        return out, lse, None
+    vcode = v_code_values(dtype, res["v_codes"][:n])
+    vs = bf16_value(res["v_scale"][:n]).astype(np.float64)
+    return attention_fp8pv(q, res["k_hat"][:n], vcode, vs, scale)
+
+
 def decode_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD,
-                     static_kv=None, softmax_scale: Optional[float] = None, q8: bool = False):
+                     static_kv=None, softmax_scale: Optional[float] = None, q8: bool = False,
+                     pv8: bool = False):
     """Reference for one sequence.
 
     q_bf16 [Hq][d], k_bf16 / v_bf16 [T][n_kv][d] (bf16 bits).  ``static_kv`` =
     (k_scale, v_scale) bf16 bits broadcastable to [n_kv] for static modes.
     q8: FP8-domain QK, i.e. attention of fp8_query(q) instead of q.
+    pv8: FP8 score-V product (attention_fp8pv; FP8 caches); adds "allow".
     Returns dict: K/V codes, scales, zeros, and fp64 out [Hq][d], lse [Hq].
     """
     q = fp8_query(q_bf16) if q8 else bf16_value(q_bf16).astype(np.float64)
     d = q.shape[-1]
     scale = (1.0 / np.sqrt(d)) if softmax_scale is None else softmax_scale
     res = quantized_cache(k_bf16, v_bf16, dtype, mode, static_kv)
-    out, lse = attention(q, res["k_hat"], res["v_hat"], scale)
-    res["out"], res["lse"] = out, lse
+    res["out"], res["lse"], allow = _attend(q, res, dtype, scale, pv8)
+    if allow is not None:
+        res["allow"] = allow
     return res
 
 
@@ -313,7 +366,8 @@ def quantized_cache(k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD, stat
 
 # ---------------------------------------------------------------- verification step
 def verify_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD,
-                     static_kv=None, softmax_scale: Optional[float] = None, q8: bool = False):
+                     static_kv=None, softmax_scale: Optional[float] = None, q8: bool = False,
+                     pv8: bool = False):
     """Reference for one sequence in a speculative-decoding verification pass.
 
     The target model scores the K+1 newest positions of the sequence in one
@@ -324,6 +378,8 @@ def verify_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_H
     [T][n_kv][d].  Position i (0 = oldest of the new ones) attends causally:
     to cache positions t < T - n_new + 1 + i.  A position that sees no token
     (T < n_new) gets out = 0 and lse = -inf.  q8: FP8-domain QK (fp8_query).
+    pv8: FP8 score-V product over each position's visible tokens (blocks from
+    token 0), adding "allow" [n_new][Hq][d].
     Returns the dict of quantized_cache plus fp64 out [n_new][Hq][d] and lse
     [n_new][Hq].
     """
@@ -334,8 +390,13 @@ def verify_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_H
     T = res["k_hat"].shape[0]
     out = np.zeros((n_new, Hq, d), dtype=np.float64)
     lse = np.full((n_new, Hq), -np.inf, dtype=np.float64)
+    allow = np.zeros((n_new, Hq, d), dtype=np.float64)
     for i in range(n_new):
         n_vis = max(0, T - n_new + 1 + i)
-        out[i], lse[i] = attention(q[i], res["k_hat"][:n_vis], res["v_hat"][:n_vis], scale)
+        out[i], lse[i], a = _attend(q[i], res, dtype, scale, pv8, n_vis)
+        if a is not None:
+            allow[i] = a
     res["out"], res["lse"] = out, lse
+    if pv8:
+        res["allow"] = allow
     return res

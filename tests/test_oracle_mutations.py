@@ -119,3 +119,68 @@ def test_encoder_tie_mutant_is_caught(oracle):
         code = np.where(d == best, np.arange(0x7F)[None, :], -1).max(axis=1)   # larger magnitude on ties
         return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
     rejects(P.test_e4m3_encode_brute_force, Mutant(oracle, e4m3_encode=ties_away))
+
+
+def _np_attention_fp8pv(oracle, q, k, vcode, vs, scale, block=32, s_nearest=False, vs_after=False,
+                        truncate=False, drop_ref=False):
+    """The FP8 score-V reading in numpy (for planting mistakes): per block of
+    `block` tokens from token 0, P = 2^(lam - ceil(max lam)) vs, the smallest
+    power-of-two S with max P <= 448 S, E4M3 of P / S (torch's cast), weights
+    2^(mu - M) S e4m3."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    vcode = np.asarray(vcode, np.float64)
+    vs = np.asarray(vs, np.float64)
+    Hq, d = q.shape
+    T, n_kv = k.shape[0], k.shape[1]
+    G = Hq // n_kv
+    s32 = float(np.float32(scale))
+    out = np.zeros((Hq, d))
+    lse = np.zeros(Hq)
+    for h in range(Hq):
+        g = h // G
+        lam = s32 * (k[:, g, :] @ q[h]) / np.log(2.0)
+        M = max(np.ceil(lam[b:b + block].max()) for b in range(0, T, block))
+        w = np.zeros(T)
+        for b in range(0, T, block):
+            blk = slice(b, min(b + block, T))
+            mu = np.ceil(lam[blk].max())
+            P = np.exp2(lam[blk] - mu) * (1.0 if vs_after else vs[blk, g])
+            E = np.log2(P.max() / 448.0)
+            E = np.round(E) if s_nearest else np.ceil(E)
+            S = 2.0**E
+            y = torch.from_numpy(P / S)
+            e = y.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+            if truncate:                         # toward zero instead of to nearest
+                grid = oracle.e4m3_table()[:127]
+                e = grid[np.searchsorted(grid, (P / S), side="right") - 1]
+            w[blk] = e * S * (1.0 if drop_ref else 2.0**(mu - M))
+            if vs_after:
+                w[blk] *= vs[blk, g]
+        L = np.exp2(lam - M).sum()
+        out[h] = w @ vcode[:, g, :] / L
+        lse[h] = M * np.log(2.0) + np.log(L)
+    return out, lse, np.zeros((Hq, d))
+
+
+def test_fp8pv_mutants_are_caught(oracle):
+    std = lambda **kw: Mutant(oracle, attention_fp8pv=lambda q, k, v, s, sc: _np_attention_fp8pv(  # noqa: E731
+        oracle, q, k, v, s, sc, **kw))
+    # the stand-in without a mistake passes
+    P.test_fp8pv_exact_when_every_weight_is_representable(std())
+    P.test_fp8pv_weights_match_torch_e4m3_cast(std())
+    P.test_fp8pv_within_half_an_e4m3_step_of_exact_attention(std())
+    # blocks of 16 tokens: other block scales for the subnormal-range weights
+    rejects(P.test_fp8pv_weights_match_torch_e4m3_cast, std(block=16))
+    # block scale rounded to the nearest power of two: the top weights saturate
+    rejects(P.test_fp8pv_exact_when_every_weight_is_representable, std(s_nearest=True))
+    rejects(P.test_fp8pv_weights_match_torch_e4m3_cast, std(s_nearest=True))
+    # the V scale applied after the probabilities are rounded to E4M3
+    rejects(P.test_fp8pv_weights_match_torch_e4m3_cast, std(vs_after=True))
+    # E4M3 rounding toward zero instead of to nearest (within a full step, so
+    # the half-step bound on the aggregate output need not see it; the
+    # per-weight cast does)
+    rejects(P.test_fp8pv_weights_match_torch_e4m3_cast, std(truncate=True))
+    # the factor 2^(mu - M) dropped: the blocks' weights lose their relative size
+    rejects(P.test_fp8pv_exact_when_every_weight_is_representable, std(drop_ref=True))
+    rejects(P.test_fp8pv_within_half_an_e4m3_step_of_exact_attention, std(drop_ref=True))

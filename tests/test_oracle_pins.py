@@ -649,3 +649,140 @@ def test_fp8_domain_reference_exact_for_representable_query(oracle):
     c = oracle.decode_reference(q2, k, v, oracle.FP8)
     e = oracle.decode_reference(q2, k, v, oracle.FP8, q8=True)
     assert np.abs(c["out"] - e["out"]).max() > 1e-4
+
+
+# ---------------------------------------------------------------- FP8 score-V product
+# attention_fp8pv: the score-V product of FP8-domain attention ("FP8 KV Cache부터
+# INT4 Weight-Only까지", core concept 3).  Reading: each token's weight relative
+# to its 32-token block's integer log2 reference, times its V scale, held as an
+# E4M3 code under the smallest power-of-two block scale that fits 448.
+
+def _softmax_weights(scores):
+    m = scores.max()
+    w = np.exp(scores - m)
+    return w / w.sum()
+
+
+def _log2_scores_as_keys(lam, d, ln2_32):
+    """Keys whose score against q = e_0 at softmax scale ln2_32 (a float32
+    value, as the oracle takes it) is lam_t ln 2: channel 0 holds lam ln2 /
+    ln2_32."""
+    T, n_kv = lam.shape
+    k = np.zeros((T, n_kv, d))
+    k[:, :, 0] = lam * math.log(2.0) / ln2_32
+    return k
+
+
+LN2_32 = float(np.float32(math.log(2.0)))
+
+
+def test_fp8pv_exact_when_every_weight_is_representable(oracle):
+    """Scores on an integer log2 grid and power-of-two V scales make every
+    P / S a power of two within 2^-4..256 (12 binades of scores and scales
+    below the block's top), exactly representable in E4M3: the result is then
+    the plain softmax attention (the pinned fp64 oracle) over x^ = vs * vcode,
+    to rounding."""
+    rng = np.random.default_rng(5)
+    T, Hq, n_kv, d = 150, 4, 2, 6
+    lam = rng.integers(-8, 3, size=(T, n_kv)).astype(np.float64)         # log2 scores
+    lam[32:64] -= 5.0                                                    # a block with a lower reference
+    k = _log2_scores_as_keys(lam, d, LN2_32)
+    q = np.zeros((Hq, d))
+    q[:, 0] = 1.0
+    vs = np.ldexp(1.0, rng.integers(-8, -5, size=(T, n_kv)))
+    vcode = rng.standard_normal((T, n_kv, d))
+    out, lse, allow = oracle.attention_fp8pv(q, k, vcode, vs, LN2_32)
+    ref, ref_lse = oracle.attention(q, k, vcode * vs[:, :, None], LN2_32)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-15)
+    assert np.allclose(lse, ref_lse, rtol=0, atol=1e-12)
+    # every weight sits on a representable value, far from a rounding boundary
+    assert not allow.any()
+
+
+def test_fp8pv_within_half_an_e4m3_step_of_exact_attention(oracle):
+    """Random scores and scales: each weight is off by at most half an E4M3
+    step (2^-4 relative; 2^-10 S absolute in the subnormal range, S <= 2^-7
+    of the block's largest weight times 448 / 256), so the output is within
+    2^-4 sum_t p_t |x^_t| + 2^-14.8 max_t |x^_t| of the exact softmax attention
+    (p from a plain softmax here); and the error is not zero."""
+    rng = np.random.default_rng(6)
+    T, Hq, n_kv, d = 333, 8, 2, 16
+    q = rng.standard_normal((Hq, d))
+    k = rng.standard_normal((T, n_kv, d)) * 1.5
+    vcode = rng.standard_normal((T, n_kv, d))
+    vs = np.abs(rng.standard_normal((T, n_kv))) * 0.02 + 1e-3
+    scale = float(np.float32(0.4))
+    out, lse, _ = oracle.attention_fp8pv(q, k, vcode, vs, scale)
+    x = vcode * vs[:, :, None]
+    G = Hq // n_kv
+    worst = 0.0
+    for h in range(Hq):
+        g = h // G
+        sc = scale * (k[:, g, :] @ q[h])
+        p = _softmax_weights(sc)
+        exact = p @ x[:, g, :]
+        bound = 2.0**-4 * (p @ np.abs(x[:, g, :])) + 2.0**-14.8 * np.abs(x[:, g, :]).max()
+        err = np.abs(out[h] - exact)
+        assert np.all(err <= bound * (1 + 1e-9)), h
+        worst = max(worst, float((err / bound).max()))
+        m = sc.max()
+        assert abs(lse[h] - (m + math.log(np.exp(sc - m).sum()))) < 1e-12
+    assert 0.05 < worst <= 1.0
+
+
+def test_fp8pv_weights_match_torch_e4m3_cast(oracle):
+    """Weights read back through one-hot V rows (vcode_t = e_t, d = T): each
+    token's weight times the softmax denominator is 2^(mu - M) S times the
+    E4M3 value of P / S, with the E4M3 rounding done by torch's float8_e4m3fn
+    cast, bit for bit, for two 32-token blocks and a partial third."""
+    rng = np.random.default_rng(7)
+    T = 77
+    lam = rng.uniform(-9.0, 4.0, size=(T, 1))
+    lam[40] = 7.3                                            # block 1 peaks higher
+    k = _log2_scores_as_keys(lam, T, LN2_32)
+    q = np.zeros((1, T))
+    q[0, 0] = 1.0
+    vs = rng.uniform(0.004, 0.03, size=(T, 1))
+    vcode = np.eye(T).reshape(T, 1, T)
+    out, _, _ = oracle.attention_fp8pv(q, k, vcode, vs, LN2_32)
+    lam = (LN2_32 * k[:, 0, 0]) / math.log(2.0)              # the log2 score as the oracle forms it
+    M = max(math.ceil(lam[b:b + 32].max()) for b in range(0, T, 32))
+    L = np.exp2(lam - M).sum()
+    for b in range(0, T, 32):
+        blk = slice(b, min(b + 32, T))
+        mu = math.ceil(lam[blk].max())
+        P = np.exp2(lam[blk] - mu) * vs[blk, 0]
+        E = math.ceil(math.log2(P.max() / 448.0))
+        S = 2.0**E
+        assert P.max() <= 448.0 * S and P.max() > 224.0 * S
+        codes = torch.from_numpy(P / S).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        want = codes * S * 2.0**(mu - M)
+        got = out[0, blk] * L
+        assert np.allclose(got, want, rtol=1e-12, atol=0), b
+
+
+def test_fp8pv_integer_shift_invariance_and_block_alignment(oracle):
+    """Adding an integer to every log2 score moves each block reference by the
+    same integer: the output is unchanged (to the rounding of forming the
+    scores).  Blocks start at token 0 of the context: dropping the first token
+    shifts every block boundary, which regroups the tokens whose weights fall
+    in E4M3's subnormal range under other block scales and changes the result,
+    while the plain attention moves only by that token's (vanishing) weight."""
+    rng = np.random.default_rng(8)
+    T, Hq, n_kv, d = 200, 2, 1, 8
+    lam = rng.uniform(-16, 6, size=(T, n_kv))
+    vcode = rng.standard_normal((T, n_kv, d))
+    vs = rng.uniform(0.005, 0.05, size=(T, n_kv))
+    q = np.zeros((Hq, d))
+    q[:, 0] = 1.0
+    a, _, _ = oracle.attention_fp8pv(q, _log2_scores_as_keys(lam, d, LN2_32), vcode, vs, LN2_32)
+    b, _, _ = oracle.attention_fp8pv(q, _log2_scores_as_keys(lam + 3.0, d, LN2_32), vcode, vs, LN2_32)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-16)
+    lam[0] = -60.0                                            # token 0 carries no weight
+    k = _log2_scores_as_keys(lam, d, LN2_32)
+    c, _, _ = oracle.attention_fp8pv(q, k, vcode, vs, LN2_32)
+    e, _, _ = oracle.attention_fp8pv(q, k[1:], vcode[1:], vs[1:], LN2_32)
+    ref, _ = oracle.attention(q, k, vcode * vs[:, :, None], LN2_32)
+    ref1, _ = oracle.attention(q, k[1:], vcode[1:] * vs[1:, :, None], LN2_32)
+    assert np.abs(ref - ref1).max() < 1e-15
+    assert np.abs(c - e).max() > 1e-10
