@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="llama70b",
-                    choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "kivi2", "verify", "e5m2", "static", "fp8qk"])
+                    choices=["tiny", "llama8b", "llama70b", "mixed", "kivi", "kivi2", "verify", "e5m2", "static", "fp8qk",
+                             "fp8attn"])
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto)")
     ap.add_argument("--partition-pages", type=int, default=0)
     ap.add_argument("--graph", action="store_true",
@@ -174,7 +175,9 @@ def cpu_baseline(w, budget_s: float):
                 kh[:, h], vh[:, h] = O.kivi_dequant(st, w.page_size)
         t1 = time.perf_counter()
         q = O.fp8_query(qb) if w.fp8_qk else O.bf16_value(qb).astype(np.float64)
-        if QL == 1:
+        if w.fp8_pv:
+            O.attention_fp8pv(q, kh, O.v_code_values(dt, res["v_codes"]), O.bf16_value(res["v_scale"]), scale)
+        elif QL == 1:
             O.attention(q, kh, vh, scale)
         else:
             T = kh.shape[0]
@@ -331,8 +334,9 @@ def main():
         else:
             code = {"fp8": kvq.KVQ_FP8_E4M3, "e5m2": kvq.KVQ_FP8_E5M2, "int8": kvq.KVQ_INT8_ASYM}[w.dtype]
             ss = synthetic.static_scales(w).cuda() if w.scale_mode != 2 else None
+            flags = (kvq.KVQ_ATTN_FP8_QK if w.fp8_qk else 0) | (kvq.KVQ_ATTN_FP8_PV if w.fp8_pv else 0)
             cache = kvq.Cache(code, full_layout.num_pages, w.num_kv_heads, w.page_size, d, w.scale_mode, ss,
-                              attn_flags=kvq.KVQ_ATTN_FP8_QK if w.fp8_qk else 0)
+                              attn_flags=flags)
             for b, n in enumerate(lens):
                 m = int(n) - QL
                 for p0 in range(0, m, 1 << 16):
@@ -478,6 +482,8 @@ def main():
                    "partition_pages": args.partition_pages or "auto", "positions_per_seq": QL,
                    "scale_mode": {2: "per_token_head", 1: "static_per_head", 0: "static_per_tensor"}[w.scale_mode],
                    "qk": "fp8_domain (query in E4M3)" if w.fp8_qk else "bf16 query",
+                   "pv": "fp8_domain (probabilities in E4M3, 32-token power-of-two block scales)" if w.fp8_pv
+                         else "bf16 hi + lo probabilities",
                    "step_launch": "hip_graph" if args.graph else "eager"},
         "tokens_per_s": round(B * QL / (ms_step * 1e-3), 1),
         # attention-only extrapolation to a whole model of this layer's shape:

@@ -104,7 +104,20 @@ typedef enum kvq_attn_flag {
      * over the cache.  Softmax and PV keep their precision.  Some backends
      * compute attention in FP8 ("FP8 KV Cache부터 INT4 Weight-Only까지",
      * daewooki.github.io, core concept 3).  Not for INT8 or KIVI caches. */
-    KVQ_ATTN_FP8_QK = 1
+    KVQ_ATTN_FP8_QK = 1,
+    /* FP8 score-V product (FP8 E4M3 / E5M2 caches; the same page names QK
+     * and the score-V product in the FP8 domain): the weights of each block of
+     * 32 tokens from token 0, P_t = 2^(lambda_t - mu) * vs_t (lambda_t the
+     * score in log2 units, mu = ceil(max lambda over the block), vs_t the
+     * token's V scale), are held as E4M3 codes of P_t / S under the block's
+     * smallest power-of-two scale S with max P <= 448 S, and multiply the V
+     * codes on the scaled FP8 matrix cores:
+     *   out = sum_t 2^(mu - M) S e4m3(P_t / S) vcode_t / sum_t 2^(lambda_t - M).
+     * The softmax denominator and lse stay exact (fp32).  Combined with
+     * KVQ_ATTN_FP8_QK it gives attention with both products in FP8.  With
+     * page size 16, partition_pages counts 32-token blocks.  Not for INT8 or
+     * KIVI caches. */
+    KVQ_ATTN_FP8_PV = 2
 } kvq_attn_flag;
 
 typedef enum kvq_scale_mode {
@@ -133,7 +146,8 @@ typedef struct kvq_cache {
     int32_t window_tokens;    /* residual + page_size (160 for residual 128, group 32)   */
     int32_t residual;         /* tokens always kept in fp16 (128)                        */
     int32_t attn_flags;       /* kvq_attn_flag bits read by the decode / verify entry
-                                 points (0: query in bf16); the append calls ignore it */
+                                 points (0: query and probabilities in bf16 / fp32
+                                 precision); the append calls ignore it */
 } kvq_cache;
 
 /* Bytes of one page record: which = 0 for K, 1 for V.  0 for an invalid combination. */

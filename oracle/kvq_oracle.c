@@ -423,9 +423,11 @@ void kvqo_attention(const double* q, const double* k, const double* v, int64_t T
  *    P_t replaced by its E4M3 value.  lse is the exact one.                  *
  * vcode: decoded V codes without their scale [T][n_kv][d]; vs [T][n_kv].    *
  * allowance [n_q][d]: for every token whose P_t / S_c lies within a relative *
- * 2^-18 of an E4M3 rounding boundary (where a float32 evaluation may take    *
- * the neighbouring code), one code step times its weight and |vcode|; where  *
- * the block maximum lies that close to a power-of-two boundary of S_c, the   *
+ * a_t of an E4M3 rounding boundary, one code step times its weight and       *
+ * |vcode|, where a_t = 2^-18 + score_rel * softmax_scale * sum_i |q_i k_ti|: *
+ * an evaluation whose scores are off by up to score_rel of that sum (and     *
+ * whose P is otherwise float32) may take the neighbouring code.  Where the   *
+ * block maximum lies that close to a power-of-two boundary of S_c, the       *
  * block's subnormal-range codes count one subnormal step of 2 S_c too.      *
  * All divided by the softmax denominator, like out.                          *
  * ======================================================================= */
@@ -444,9 +446,8 @@ static int e4m3_neighbour_steps(double y, double* lo_step, double* hi_step, doub
 
 void kvqo_attention_fp8pv(const double* q, const double* k, const double* vcode, const double* vs,
                           int64_t T, int n_q, int n_kv, int d, double softmax_scale, int block,
-                          double* out, double* lse, double* allowance)
+                          double score_rel, double* out, double* lse, double* allowance)
 {
-    const double amb = ldexp(1.0, -18);
     int grp = n_q / n_kv;
     #pragma omp parallel for schedule(static)
     for (int h = 0; h < n_q; ++h) {
@@ -456,11 +457,16 @@ void kvqo_attention_fp8pv(const double* q, const double* k, const double* vcode,
         for (int i = 0; i < d; ++i) { o[i] = 0.0; al[i] = 0.0; }
         if (T == 0) { if (lse) lse[h] = -INFINITY; continue; }
         double* lam = (double*)malloc(sizeof(double) * (size_t)T);
+        double* amb = (double*)malloc(sizeof(double) * (size_t)T);
         for (int64_t t = 0; t < T; ++t) {
             const double* kt = k + (t * n_kv + g) * d;
-            double sdot = 0.0;
-            for (int i = 0; i < d; ++i) sdot += q[(int64_t)h * d + i] * kt[i];
+            double sdot = 0.0, sabs = 0.0;
+            for (int i = 0; i < d; ++i) {
+                sdot += q[(int64_t)h * d + i] * kt[i];
+                sabs += fabs(q[(int64_t)h * d + i] * kt[i]);
+            }
             lam[t] = softmax_scale * sdot / M_LN2;
+            amb[t] = ldexp(1.0, -18) + score_rel * softmax_scale * sabs;
         }
         /* M = the largest block reference; L = sum_t 2^(lambda_t - M) */
         double M = -INFINITY;
@@ -472,10 +478,10 @@ void kvqo_attention_fp8pv(const double* q, const double* k, const double* vcode,
             double mx = -INFINITY;
             for (int64_t t = b0; t < b1; ++t) if (lam[t] > mx) mx = lam[t];
             double mu = ceil(mx);
-            double pmax = 0.0;
+            double pmax = 0.0, amax_amb = 0.0;
             for (int64_t t = b0; t < b1; ++t) {
                 double P = exp2(lam[t] - mu) * vs[t * n_kv + g];
-                if (P > pmax) pmax = P;
+                if (P > pmax) { pmax = P; amax_amb = amb[t]; }
             }
             if (pmax == 0.0) continue;
             /* smallest E with pmax <= 448 * 2^E (exact comparisons) */
@@ -483,7 +489,7 @@ void kvqo_attention_fp8pv(const double* q, const double* k, const double* vcode,
             while (pmax > ldexp(448.0, E)) ++E;
             while (pmax <= ldexp(448.0, E - 1)) --E;
             double S = ldexp(1.0, E);
-            int s_edge = fabs(pmax - ldexp(448.0, E - 1)) <= amb * pmax;   /* S or 2 S */
+            int s_edge = fabs(pmax - ldexp(448.0, E - 1)) <= amax_amb * pmax;   /* S or 2 S */
             double wgt = S * exp2(mu - M);
             for (int64_t t = b0; t < b1; ++t) {
                 double y = exp2(lam[t] - mu) * vs[t * n_kv + g] / S;       /* exact division */
@@ -491,8 +497,8 @@ void kvqo_attention_fp8pv(const double* q, const double* k, const double* vcode,
                 uint8_t c = (uint8_t)e4m3_neighbour_steps(y, &ls, &hs, &lm, &hm);
                 double w = kvqo_e4m3_value(c) * wgt;
                 double step = 0.0;
-                if (fabs(y - lm) <= amb * y && ls > 0.0) step = ls;
-                if (fabs(y - hm) <= amb * y && hs > step) step = hs;
+                if (fabs(y - lm) <= amb[t] * y && ls > 0.0) step = ls;
+                if (fabs(y - hm) <= amb[t] * y && hs > step) step = hs;
                 if (s_edge && y < ldexp(1.0, -5)) step += ldexp(1.0, -8);
                 const double* vt = vcode + (t * n_kv + g) * d;
                 for (int i = 0; i < d; ++i) {
@@ -504,6 +510,7 @@ void kvqo_attention_fp8pv(const double* q, const double* k, const double* vcode,
         for (int i = 0; i < d; ++i) { o[i] /= L; al[i] /= L; }
         if (lse) lse[h] = M * M_LN2 + log(L);
         free(lam);
+        free(amb);
     }
 }
 

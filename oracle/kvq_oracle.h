@@ -80,10 +80,11 @@ void kvqo_attention(const double* q, const double* k, const double* v, int64_t T
 /* Score-V product in the FP8 domain (kvq_oracle.c): P per block of `block`
  * tokens relative to the block's integer log2 reference, times the V scale,
  * in E4M3 with a power-of-two block scale.  vcode: V code values without
- * their scale; vs: V scales [T][n_kv]. */
+ * their scale; vs: V scales [T][n_kv].  score_rel: relative score uncertainty
+ * of the evaluation the result is compared with (for the allowance only). */
 void kvqo_attention_fp8pv(const double* q, const double* k, const double* vcode, const double* vs,
                           int64_t T, int n_q, int n_kv, int d, double softmax_scale, int block,
-                          double* out, double* lse, double* allowance);
+                          double score_rel, double* out, double* lse, double* allowance);
 /* merge P partial results (o [P][d], lse [P]) of disjoint token ranges */
 void kvqo_lse_merge(const double* o, const double* lse, int P, int d, double* out, double* lse_out);
 

@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L.kvqo_attention.argtypes = [_P, _P, _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_double, _P, _P]
         L.kvqo_attention_fp8pv.argtypes = [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                           ctypes.c_double, ctypes.c_int, _P, _P, _P]
+                                           ctypes.c_double, ctypes.c_int, ctypes.c_double, _P, _P, _P]
         L.kvqo_e4m3_encode_f64.restype = ctypes.c_uint8
         L.kvqo_e4m3_encode_f64.argtypes = [ctypes.c_double]
         L.kvqo_lse_merge.argtypes = [_P, _P, ctypes.c_int, ctypes.c_int, _P, _P]
@@ -254,15 +254,26 @@ def attention(q, k, v, softmax_scale: float):
 FP8_PV_BLOCK = 32      # tokens per probability block of the FP8 score-V product
 
 
-def attention_fp8pv(q, k, vcode, vs, softmax_scale: float, block: int = FP8_PV_BLOCK):
+# Relative score uncertainty (of sum_i |q_i k_i|, times the softmax scale) of
+# the evaluations the FP8 score-V reference is compared with, for its
+# allowance: float32 accumulation of exact products, and the FP8 matrix core's
+# alignment within one 128-term dot product (FP8-domain QK).
+SCORE_REL_FP32 = 2.0**-20
+SCORE_REL_FP8_DOT = 2.0**-12
+
+
+def attention_fp8pv(q, k, vcode, vs, softmax_scale: float, block: int = FP8_PV_BLOCK,
+                    score_rel: float = SCORE_REL_FP32):
     """Attention with the score-V product in the FP8 domain (kvq_oracle.c,
     kvqo_attention_fp8pv; "FP8 KV Cache부터 INT4 Weight-Only까지", core concept
     3): each token's weight relative to its 32-token block's integer log2
     reference, times its V scale, held as an E4M3 code under a power-of-two
     block scale.  q [Hq][d], k [T][n_kv][d] (fp64, dequantized), vcode
     [T][n_kv][d] (decoded V codes without their scale), vs [T][n_kv] (V scales).
-    Returns (out [Hq][d], lse [Hq], allowance [Hq][d]); allowance bounds what a
-    float32 evaluation may differ by at the E4M3 rounding boundaries it meets."""
+    Returns (out [Hq][d], lse [Hq], allowance [Hq][d]); allowance bounds what
+    an evaluation with float32 probabilities and scores off by up to score_rel
+    * softmax_scale * sum_i |q_i k_i| may differ by at the E4M3 rounding
+    boundaries it meets."""
     q = _c(q, np.float64)
     k = _c(k, np.float64)
     vcode = _c(vcode, np.float64)
@@ -273,7 +284,8 @@ def attention_fp8pv(q, k, vcode, vs, softmax_scale: float, block: int = FP8_PV_B
     lse = np.empty(Hq, dtype=np.float64)
     allow = np.empty((Hq, d), dtype=np.float64)
     lib().kvqo_attention_fp8pv(_ptr(q), _ptr(k), _ptr(vcode), _ptr(vs), T, Hq, n_kv, d,
-                               float(np.float32(softmax_scale)), int(block), _ptr(out), _ptr(lse), _ptr(allow))
+                               float(np.float32(softmax_scale)), int(block), float(score_rel), _ptr(out), _ptr(lse),
+                               _ptr(allow))
     return out, lse, allow
 
 
@@ -310,7 +322,7 @@ def fp8_query(q_bf16) -> np.ndarray:
     return dequantize_rows(FP8, c, s)
 
 
-def _attend(q, res, dtype: int, scale: float, pv8: bool, n_vis=None):
+def _attend(q, res, dtype: int, scale: float, pv8: bool, n_vis=None, score_rel: float = SCORE_REL_FP32):
     """Attention of q over the first n_vis cached tokens of a quantized_cache
     result: plain (fp64 on the dequantized cache) or FP8 score-V (pv8).
     Returns (out, lse, allowance or None)."""
@@ -321,7 +333,7 @@ def _attend(q, res, dtype: int, scale: float, pv8: bool, n_vis=None):
         return out, lse, None
     vcode = v_code_values(dtype, res["v_codes"][:n])
     vs = bf16_value(res["v_scale"][:n]).astype(np.float64)
-    return attention_fp8pv(q, res["k_hat"][:n], vcode, vs, scale)
+    return attention_fp8pv(q, res["k_hat"][:n], vcode, vs, scale, score_rel=score_rel)
 
 
 def decode_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_HEAD,
@@ -332,14 +344,17 @@ def decode_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_H
     q_bf16 [Hq][d], k_bf16 / v_bf16 [T][n_kv][d] (bf16 bits).  ``static_kv`` =
     (k_scale, v_scale) bf16 bits broadcastable to [n_kv] for static modes.
     q8: FP8-domain QK, i.e. attention of fp8_query(q) instead of q.
-    pv8: FP8 score-V product (attention_fp8pv; FP8 caches); adds "allow".
+    pv8: FP8 score-V product (attention_fp8pv; FP8 caches); adds "allow", for
+    an evaluation whose scores carry the uncertainty of its QK (FP8 matrix
+    core with q8, float32 accumulation otherwise).
     Returns dict: K/V codes, scales, zeros, and fp64 out [Hq][d], lse [Hq].
     """
     q = fp8_query(q_bf16) if q8 else bf16_value(q_bf16).astype(np.float64)
     d = q.shape[-1]
     scale = (1.0 / np.sqrt(d)) if softmax_scale is None else softmax_scale
     res = quantized_cache(k_bf16, v_bf16, dtype, mode, static_kv)
-    res["out"], res["lse"], allow = _attend(q, res, dtype, scale, pv8)
+    res["out"], res["lse"], allow = _attend(q, res, dtype, scale, pv8,
+                                            score_rel=SCORE_REL_FP8_DOT if q8 else SCORE_REL_FP32)
     if allow is not None:
         res["allow"] = allow
     return res
@@ -393,7 +408,8 @@ def verify_reference(q_bf16, k_bf16, v_bf16, dtype: int, mode: int = PER_TOKEN_H
     allow = np.zeros((n_new, Hq, d), dtype=np.float64)
     for i in range(n_new):
         n_vis = max(0, T - n_new + 1 + i)
-        out[i], lse[i], a = _attend(q[i], res, dtype, scale, pv8, n_vis)
+        out[i], lse[i], a = _attend(q[i], res, dtype, scale, pv8, n_vis,
+                                    score_rel=SCORE_REL_FP8_DOT if q8 else SCORE_REL_FP32)
         if a is not None:
             allow[i] = a
     res["out"], res["lse"] = out, lse

@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2", "KVQ_INT2_KIVI", "KIVI_DTYPES", "KVQ_ATTN_FP8_QK",
+    "KVQ_FP8_E4M3", "KVQ_INT8_ASYM", "KVQ_INT4_KIVI", "KVQ_FP8_E5M2", "KVQ_INT2_KIVI", "KIVI_DTYPES", "KVQ_ATTN_FP8_QK", "KVQ_ATTN_FP8_PV",
     "KVQ_SCALE_PER_TENSOR", "KVQ_SCALE_PER_HEAD", "KVQ_SCALE_PER_TOKEN_HEAD",
     "KVQ_OK", "KVQ_EINVAL", "KVQ_EUNSUPPORTED", "KVQ_EWORKSPACE", "KVQ_EHIP",
     "KvqError", "Cache", "lib", "record_bytes", "append", "kivi_append", "decode_workspace_bytes",
@@ -27,6 +27,7 @@ __all__ = [
 KVQ_FP8_E4M3, KVQ_INT8_ASYM, KVQ_INT4_KIVI, KVQ_FP8_E5M2, KVQ_INT2_KIVI = 1, 2, 3, 4, 5
 KIVI_DTYPES = (KVQ_INT4_KIVI, KVQ_INT2_KIVI)
 KVQ_ATTN_FP8_QK = 1          # kvq_cache.attn_flags: FP8-domain QK (query quantized to E4M3)
+KVQ_ATTN_FP8_PV = 2          # kvq_cache.attn_flags: FP8 score-V product (probabilities in E4M3)
 KVQ_SCALE_PER_TENSOR, KVQ_SCALE_PER_HEAD, KVQ_SCALE_PER_TOKEN_HEAD = 0, 1, 2
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_EWORKSPACE, KVQ_EHIP = 0, -1, -2, -3, -4
 

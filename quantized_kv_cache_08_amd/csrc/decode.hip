@@ -49,6 +49,20 @@
 // PV are unchanged (P' in bf16 hi + lo): E4M3 probabilities, 3 mantissa bits,
 // would move outputs far past the 2e-3 bar, and their codes would depend on
 // this kernel's running maximum, which no plain definition fixes.
+//
+// FP8 score-V (PV; the descriptor's KVQ_ATTN_FP8_PV flag, FP8 caches): the
+// same page of that section names the score-V product in the FP8 domain too.
+// The probabilities of a 32-token chunk, P' = 2^(s - m) v_scale with the
+// running maximum m kept an integer, are held as E4M3 codes under the chunk's
+// smallest power-of-two scale S with max P' <= 448 S (per query row), and PV
+// runs on the scaled FP8 MFMA 16x16x128 straight from the V codes (E4M3, or
+// E5M2 as BF8), S entering as the E8M0 scale of the row: one instruction per
+// 16 channels, no V conversion.  Because m and the chunk's own reference
+// differ by an integer, the codes are those of a definition that does not
+// depend on m: the weight of token t relative to its 32-token block's integer
+// log2 reference, times its V scale, in E4M3 under the block's power-of-two
+// scale.  With page size 16 the work is planned in 32-token units so that a
+// segment starts on a block boundary.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "splitk.h"
@@ -80,7 +94,42 @@ __device__ __forceinline__ f32x4_t mfma_16x16x128_fp8(const u32x4_t (&a)[2], con
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, z, A_FMT, 0, 0, 127, 0, 127);
 }
 
-template <int DT, bool STATIC, int PS, bool Q8>
+// Scaled FP8 MFMA 16x16x128 for PV: A = 8 E4M3 codes per lane (bytes 0-7 of
+// the lane's 32; the rest zero), B = 8 codes of the same tokens (format
+// B_FMT: 0 E4M3, 1 E5M2), scale_a = E8M0 exponent of the lane's row (every
+// lane of a row carries the same one), B unscaled.
+template <int B_FMT>
+__device__ __forceinline__ f32x4_t mfma_pv_fp8(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, int scale_a,
+                                               f32x4_t c) {
+    typedef int i32x8_t __attribute__((ext_vector_type(8)));
+    const i32x8_t av = {(int)a0, (int)a1, 0, 0, 0, 0, 0, 0};
+    const i32x8_t bv = {(int)b0, (int)b1, 0, 0, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, B_FMT, 0, scale_a, 0, 127);
+}
+
+// Smallest E with a <= 448 2^E for a finite a >= 0 (0 and float32 subnormals
+// give at most -127; the E8M0 range is [-127, 127]):  a = 1.f 2^(e - 127) and
+// 448 = 1.75 2^8, so E = e - 135, plus one when 1.f > 1.75.
+__device__ __forceinline__ int pow2_scale_exp(float a) {
+    const uint32_t u = f32_to_bits(a);
+    const int e = (int)(u >> 23) - 135 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    return min(max(e, -127), 127);
+}
+
+// 4 x 4 byte transpose: out[c] byte r = in[r] byte c.
+__device__ __forceinline__ void transpose4x4_bytes(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                                   uint32_t (&o)[4]) {
+    const uint32_t t0 = perm(v1, v0, 0x05010400u);   // v0.b0 v1.b0 v0.b1 v1.b1
+    const uint32_t t1 = perm(v1, v0, 0x07030602u);   // v0.b2 v1.b2 v0.b3 v1.b3
+    const uint32_t t2 = perm(v3, v2, 0x05010400u);
+    const uint32_t t3 = perm(v3, v2, 0x07030602u);
+    o[0] = perm(t2, t0, 0x05040100u);
+    o[1] = perm(t2, t0, 0x07060302u);
+    o[2] = perm(t3, t1, 0x05040100u);
+    o[3] = perm(t3, t1, 0x07060302u);
+}
+
+template <int DT, bool STATIC, int PS, bool Q8, bool PV>
 __device__ __forceinline__ void process_segment(const SplitParams& p, const int b, const int h,
                                                 const int page0, const int page1, const int slot,
                                                 const int n_seg, const int lane) {
@@ -298,7 +347,8 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
             // rare: kept as a branch (an empty volatile asm stops the compiler
             // from flattening it into straight-line code run every chunk)
             __asm__ volatile("");
-            const float m_new = fmaxf(m_used, mx);
+            // PV: an integer maximum, so that every factor below is a power of two
+            const float m_new = PV ? ceilf(fmaxf(m_used, mx)) : fmaxf(m_used, mx);
             const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
             lsum *= alpha;
             pz *= alpha;
@@ -349,6 +399,38 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
             for (int hp = 0; hp < 2; ++hp)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) pz += pzr[hp][r];
+        }
+
+        if constexpr (PV) {
+            // ---- P' as E4M3 codes under the chunk's power-of-two row scale
+            float amax = 0.0f;
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) amax = fmaxf(amax, pp[hp][r]);
+            amax = max_over_groups(amax);
+            const int E = pow2_scale_exp(amax);
+            uint32_t pc[2];
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(pp[hp][0], -E),
+                                                        __builtin_amdgcn_ldexpf(pp[hp][1], -E), 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(pp[hp][2], -E),
+                                                    __builtin_amdgcn_ldexpf(pp[hp][3], -E), w, true);
+                pc[hp] = (uint32_t)w;
+            }
+            // ---- V codes of channel 8j + t for tokens 4g + r (half hp) in byte r
+            uint32_t vt[2][2][4];
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+                for (int w = 0; w < 2; ++w)
+                    transpose4x4_bytes(cb.v[hp][0][w], cb.v[hp][1][w], cb.v[hp][2][w], cb.v[hp][3][w], vt[hp][w]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                acc[t] = mfma_pv_fp8<DT == kE5M2 ? 1 : 0>(pc[0], pc[1], vt[0][t >> 2][t & 3], vt[1][t >> 2][t & 3],
+                                                           E + 127, acc[t]);
+            return;
         }
 
         // ---- P' as bf16 hi + lo (A operands of PV)
@@ -476,10 +558,19 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
     }
 }
 
-template <int DT, bool STATIC, int PS, bool Q8>
+// PV with page size 16: the plan's unit is a 32-token block (two pages), so
+// that every segment starts on a block boundary.
+template <int DT, bool STATIC, int PS, bool Q8, bool PV>
 __global__ __launch_bounds__(256) void split_kernel(SplitParams p) {
-    for_each_segment<PS>(p, [&](int b, int h, int page0, int page1, int slot, int n_seg, int lane) {
-        process_segment<DT, STATIC, PS, Q8>(p, b, h, page0, page1, slot, n_seg, lane);
+    constexpr int PU = (PV && PS == 16) ? 32 : PS;
+    for_each_segment<PU>(p, [&](int b, int h, int page0, int page1, int slot, int n_seg, int lane) {
+        if constexpr (PU == PS) {
+            process_segment<DT, STATIC, PS, Q8, PV>(p, b, h, page0, page1, slot, n_seg, lane);
+        } else {
+            const int pages = pages_of(p.context_lens[b], p.max_ctx, PS);
+            process_segment<DT, STATIC, PS, Q8, PV>(p, b, h, page0 * (PU / PS), min(page1 * (PU / PS), pages), slot,
+                                                    n_seg, lane);
+        }
     });
 }
 
@@ -517,38 +608,43 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
               p.lse ? p.lse + orow : nullptr, lane);
 }
 
+template <int DT, bool STATIC, int PS, bool Q8>
+static const void* split_fn(bool pv) {
+    return pv ? (const void*)&split_kernel<DT, STATIC, PS, Q8, true> : (const void*)&split_kernel<DT, STATIC, PS, Q8, false>;
+}
+
 template <int DT, bool STATIC, int PS>
-static const void* split_fn(bool q8) {
-    return q8 ? (const void*)&split_kernel<DT, STATIC, PS, true> : (const void*)&split_kernel<DT, STATIC, PS, false>;
+static const void* split_fn(bool q8, bool pv) {
+    return q8 ? split_fn<DT, STATIC, PS, true>(pv) : split_fn<DT, STATIC, PS, false>(pv);
 }
 
 template <int DT>
-static const void* pick_fp8(bool static_scale, int page_size, bool q8) {
-    if (static_scale) return page_size == 16 ? split_fn<DT, true, 16>(q8) : split_fn<DT, true, 32>(q8);
-    return page_size == 16 ? split_fn<DT, false, 16>(q8) : split_fn<DT, false, 32>(q8);
+static const void* pick_fp8(bool static_scale, int page_size, bool q8, bool pv) {
+    if (static_scale) return page_size == 16 ? split_fn<DT, true, 16>(q8, pv) : split_fn<DT, true, 32>(q8, pv);
+    return page_size == 16 ? split_fn<DT, false, 16>(q8, pv) : split_fn<DT, false, 32>(q8, pv);
 }
 
-// q8 (FP8-domain QK) exists for the FP8 formats only; the host refuses it
-// for INT8 caches.
-static const void* pick_split(int dtype, bool static_scale, int page_size, bool q8) {
-    if (dtype == kFP8) return pick_fp8<kFP8>(static_scale, page_size, q8);
-    if (dtype == kE5M2) return pick_fp8<kE5M2>(static_scale, page_size, q8);
-    return page_size == 16 ? (const void*)&split_kernel<kINT8, false, 16, false>
-                           : (const void*)&split_kernel<kINT8, false, 32, false>;
+// q8 (FP8-domain QK) and pv (FP8 score-V) exist for the FP8 formats only; the
+// host refuses them for INT8 caches.
+static const void* pick_split(int dtype, bool static_scale, int page_size, bool q8, bool pv) {
+    if (dtype == kFP8) return pick_fp8<kFP8>(static_scale, page_size, q8, pv);
+    if (dtype == kE5M2) return pick_fp8<kE5M2>(static_scale, page_size, q8, pv);
+    return page_size == 16 ? (const void*)&split_kernel<kINT8, false, 16, false, false>
+                           : (const void*)&split_kernel<kINT8, false, 32, false, false>;
 }
 
-hipError_t split_occupancy(int dtype, bool static_scale, int page_size, bool q8, size_t lds_bytes,
+hipError_t split_occupancy(int dtype, bool static_scale, int page_size, bool q8, bool pv, size_t lds_bytes,
                            int* blocks_per_cu) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        blocks_per_cu, pick_split(dtype, static_scale, page_size, q8), kSplitThreads, lds_bytes);
+        blocks_per_cu, pick_split(dtype, static_scale, page_size, q8, pv), kSplitThreads, lds_bytes);
 }
 
-hipError_t launch_split(int dtype, bool static_scale, int page_size, bool q8, const SplitParams& p, int grid,
-                        size_t lds_bytes, hipStream_t stream) {
+hipError_t launch_split(int dtype, bool static_scale, int page_size, bool q8, bool pv, const SplitParams& p,
+                        int grid, size_t lds_bytes, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     SplitParams args = p;
     void* kargs[] = {&args};
-    return hipLaunchKernel(pick_split(dtype, static_scale, page_size, q8), dim3(grid),
+    return hipLaunchKernel(pick_split(dtype, static_scale, page_size, q8, pv), dim3(grid),
                            dim3(kSplitThreads), kargs, lds_bytes, stream);
 }
 

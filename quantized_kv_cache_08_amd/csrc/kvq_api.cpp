@@ -94,6 +94,13 @@ kvq_status check_cache(const kvq_cache* c, bool kivi) {
     return KVQ_OK;
 }
 
+// Tokens per unit of the split plan: the page, or with the FP8 score-V
+// product on 16-token pages a 32-token block of two pages (a segment then
+// starts on a block boundary of that product's probability blocks).
+int plan_page_size(const kvq_cache* c) {
+    return ((c->attn_flags & KVQ_ATTN_FP8_PV) && c->page_size == 16) ? 32 : c->page_size;
+}
+
 struct Plan {
     int max_pages = 0;     // ceil(max_context_len / page_size)
     int slots = 1;         // partial slots per KV head
@@ -133,9 +140,8 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
         partition_pages < 0 || q_len < 1)
         return KVQ_EINVAL;
     if (num_q_heads % c->num_kv_heads != 0) return KVQ_EINVAL;
-    if (c->attn_flags & ~KVQ_ATTN_FP8_QK) return KVQ_EINVAL;
-    if ((c->attn_flags & KVQ_ATTN_FP8_QK) && c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2)
-        return KVQ_EUNSUPPORTED;
+    if (c->attn_flags & ~(KVQ_ATTN_FP8_QK | KVQ_ATTN_FP8_PV)) return KVQ_EINVAL;
+    if (c->attn_flags && c->dtype != KVQ_FP8_E4M3 && c->dtype != KVQ_FP8_E5M2) return KVQ_EUNSUPPORTED;
     if (!valid_group(num_q_heads / c->num_kv_heads)) return KVQ_EUNSUPPORTED;
     // the query rows of one KV head (group x positions) form one 16-wide MFMA tile
     if ((long long)q_len * (num_q_heads / c->num_kv_heads) > 16) return KVQ_EUNSUPPORTED;
@@ -148,8 +154,8 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t num_seqs, int
     if (is_kivi(c->dtype) && num_seqs > c->max_seqs) return KVQ_EINVAL;
     if (num_seqs == 0) return KVQ_OK;
     if (!q || !block_table || !context_lens || !out || !workspace) return KVQ_EINVAL;
-    *plan = make_plan(c->page_size, c->num_kv_heads, num_seqs, num_q_heads, max_context_len, partition_pages,
-                      q_len);
+    *plan = make_plan(plan_page_size(c), c->num_kv_heads, num_seqs, num_q_heads, max_context_len,
+                      partition_pages, q_len);
     if (plan->slots == 0x7FFFFFFF) return KVQ_EUNSUPPORTED;   // forced ranges far too short for the batch
     if (workspace_bytes < plan->total) return KVQ_EWORKSPACE;
     return KVQ_OK;
@@ -197,8 +203,9 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     const bool kivi = is_kivi(c->dtype);
     int per_cu = 0;
     const bool q8 = (c->attn_flags & KVQ_ATTN_FP8_QK) != 0;
+    const bool pv = (c->attn_flags & KVQ_ATTN_FP8_PV) != 0;
     hipError_t e = kivi ? kivi_split_occupancy(kivi_bits(c->dtype), p.group * q_len, lds, &per_cu)
-                        : split_occupancy(c->dtype, is_static, c->page_size, q8, lds, &per_cu);
+                        : split_occupancy(c->dtype, is_static, c->page_size, q8, pv, lds, &per_cu);
     if (e != hipSuccess) return KVQ_EHIP;
     const int cus = device_cus();
     if (cus <= 0 || per_cu <= 0) return KVQ_EHIP;
@@ -219,7 +226,7 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
         kp.bits = kivi_bits(c->dtype);
         e = launch_kivi_split(kp, grid, lds, stream);
     } else {
-        e = launch_split(c->dtype, is_static, c->page_size, q8, p, grid, lds, stream);
+        e = launch_split(c->dtype, is_static, c->page_size, q8, pv, p, grid, lds, stream);
     }
     return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
@@ -373,7 +380,7 @@ kvq_status kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t num_seqs,
         return KVQ_EINVAL;
     if (cache->page_size <= 0 || cache->num_kv_heads <= 0 || num_q_heads % cache->num_kv_heads)
         return KVQ_EINVAL;
-    *bytes = make_plan(cache->page_size, cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
+    *bytes = make_plan(plan_page_size(cache), cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
                        partition_pages, 1)
                  .total;
     return KVQ_OK;
@@ -404,7 +411,7 @@ kvq_status kvq_decode_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t n
         return KVQ_EINVAL;
     if (num_seqs == 0) return KVQ_OK;
     if (!workspace || !out) return KVQ_EINVAL;
-    Plan pl = make_plan(cache->page_size, cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
+    Plan pl = make_plan(plan_page_size(cache), cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
                         partition_pages, 1);
     if (workspace_bytes < pl.total) return KVQ_EWORKSPACE;
     return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, 1, stream);
@@ -460,7 +467,7 @@ kvq_status kvq_verify_workspace_bytes(const kvq_cache* cache, int32_t num_seqs, 
         return KVQ_EINVAL;
     if (cache->page_size <= 0 || cache->num_kv_heads <= 0 || num_q_heads % cache->num_kv_heads)
         return KVQ_EINVAL;
-    *bytes = make_plan(cache->page_size, cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
+    *bytes = make_plan(plan_page_size(cache), cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
                        partition_pages, q_len)
                  .total;
     return KVQ_OK;
@@ -491,7 +498,7 @@ kvq_status kvq_verify_reduce(const kvq_cache* cache, int32_t num_seqs, int32_t q
     if ((long long)q_len * (num_q_heads / cache->num_kv_heads) > 16) return KVQ_EUNSUPPORTED;
     if (num_seqs == 0) return KVQ_OK;
     if (!workspace || !out) return KVQ_EINVAL;
-    Plan pl = make_plan(cache->page_size, cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
+    Plan pl = make_plan(plan_page_size(cache), cache->num_kv_heads, num_seqs, num_q_heads, max_context_len,
                         partition_pages, q_len);
     if (workspace_bytes < pl.total) return KVQ_EWORKSPACE;
     return run_reduce(cache, num_seqs, num_q_heads, pl, workspace, out, lse, q_len, stream);

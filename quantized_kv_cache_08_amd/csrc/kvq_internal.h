@@ -88,10 +88,10 @@ struct KiviSplitParams {
 
 hipError_t launch_append(int dtype, bool static_scale, int page_size, const AppendParams& p,
                          hipStream_t stream);
-hipError_t launch_split(int dtype, bool static_scale, int page_size, bool q8, const SplitParams& p,
+hipError_t launch_split(int dtype, bool static_scale, int page_size, bool q8, bool pv, const SplitParams& p,
                         int grid, size_t lds_bytes, hipStream_t stream);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t stream);
-hipError_t split_occupancy(int dtype, bool static_scale, int page_size, bool q8, size_t lds_bytes,
+hipError_t split_occupancy(int dtype, bool static_scale, int page_size, bool q8, bool pv, size_t lds_bytes,
                            int* blocks_per_cu);
 hipError_t launch_kivi_append(const KiviAppendParams& p, hipStream_t stream);
 hipError_t launch_kivi_split(const KiviSplitParams& p, int grid, size_t lds_bytes,

@@ -144,6 +144,7 @@ class Workload:
     scale_mode: int = 2       # 2: per-(token, head) scales; 1: static per head; 0: static per tensor
     group: int = 32           # KIVI group along tokens
     fp8_qk: bool = False      # FP8-domain QK (query quantized to E4M3, QK on the FP8 matrix cores)
+    fp8_pv: bool = False      # FP8 score-V product (probabilities in E4M3, PV on the FP8 matrix cores)
     description: str = ""
 
     @property
@@ -185,6 +186,11 @@ WORKLOADS = {
                       description="Llama-3-8B-shaped decode layer, FP8 E4M3 cache with FP8-domain QK (the query "
                                   "quantized per (token, head) to E4M3, QK on the FP8 MFMA): 32 q / 8 kv heads, "
                                   "d128, batch 32, context 8192, page 16"),
+    "fp8attn": Workload("fp8attn", "fp8", 32, 32, 8, 128, 16, 8192, seed=2, fp8_qk=True, fp8_pv=True,
+                        description="Llama-3-8B-shaped decode layer, FP8 E4M3 cache with attention in the FP8 "
+                                    "domain (query in E4M3 for QK; probabilities in E4M3 under power-of-two "
+                                    "32-token block scales for score-V; both on the FP8 MFMA): 32 q / 8 kv heads, "
+                                    "d128, batch 32, context 8192, page 16"),
     "kivi": Workload("kivi", "kivi4", 4, 64, 8, 128, 32, 131072, seed=5,
                      description="KIVI-style 4-bit: 64 q / 8 kv heads, d128, batch 4, context 131072; K per-channel "
                                  "INT4 in 32-token groups, V per-token INT4, last 128 tokens fp16"),

@@ -106,19 +106,22 @@ def read_seq(bt: Built, b: int, which: int, dtype: int, mode: int):
 
 
 def oracle_seq(bt: Built, b: int, mode: int = kvq.KVQ_SCALE_PER_TOKEN_HEAD, static_kv=None,
-               softmax_scale=None, q8: Optional[bool] = None) -> Dict[str, np.ndarray]:
+               softmax_scale=None, q8: Optional[bool] = None, pv8: Optional[bool] = None) -> Dict[str, np.ndarray]:
     """Oracle result for sequence b from the same seeded inputs.  The generator
     is counter-based and bitwise device-independent (tests/test_gpu_inputs.py),
     so the inputs are drawn on the cache's device and copied to the host; the
     oracle itself runs on the CPU.  q8 (default: the cache's KVQ_ATTN_FP8_QK
-    flag): FP8-domain QK reference."""
+    flag): FP8-domain QK reference; pv8 (default: the KVQ_ATTN_FP8_PV flag):
+    FP8 score-V reference."""
     w = bt.w
     T = int(bt.lens[b])
     k, v = synthetic.gen_kv(w, b, 0, T, bt.q.device)
     q = synthetic.gen_q(w, "cpu", batch=len(bt.lens))[b]
     if q8 is None:
         q8 = bool(bt.cache.attn_flags & kvq.KVQ_ATTN_FP8_QK)
-    return O.decode_reference(u16(q), u16(k), u16(v), oracle_dtype(w), mode, static_kv, softmax_scale, q8)
+    if pv8 is None:
+        pv8 = bool(bt.cache.attn_flags & kvq.KVQ_ATTN_FP8_PV)
+    return O.decode_reference(u16(q), u16(k), u16(v), oracle_dtype(w), mode, static_kv, softmax_scale, q8, pv8)
 
 
 def allclose_report(got: np.ndarray, ref: np.ndarray, atol=2e-3, rtol=1e-2):

@@ -344,22 +344,30 @@ def test_encode_validation(T):
 
 
 def test_attn_flags_validation(L):
-    """KVQ_ATTN_FP8_QK: FP8 E4M3 / E5M2 caches only; unknown bits are invalid;
-    the append entry points ignore the field.  (num_seqs = 0 / n = 0: the
-    checks run, nothing is launched.)"""
+    """KVQ_ATTN_FP8_QK and KVQ_ATTN_FP8_PV: FP8 E4M3 / E5M2 caches only;
+    unknown bits are invalid; the append entry points ignore the field.
+    (num_seqs = 0 / n = 0: the checks run, nothing is launched.)"""
     for dt in (1, 4):
-        d = _desc(dtype=dt)
-        d.attn_flags = kvq.KVQ_ATTN_FP8_QK
-        assert _decode(L, d, num_seqs=0) == OK
-        assert _verify(L, d, q_len=2, num_seqs=0) == OK
-        assert _append(L, d, n=0) == OK
-        d.attn_flags = 2
+        for flags in (kvq.KVQ_ATTN_FP8_QK, kvq.KVQ_ATTN_FP8_PV, kvq.KVQ_ATTN_FP8_QK | kvq.KVQ_ATTN_FP8_PV):
+            d = _desc(dtype=dt)
+            d.attn_flags = flags
+            assert _decode(L, d, num_seqs=0) == OK
+            assert _verify(L, d, q_len=2, num_seqs=0) == OK
+            assert _append(L, d, n=0) == OK
+        d.attn_flags = 4
         assert _decode(L, d, num_seqs=0) == INVALID
         assert _verify(L, d, q_len=2, num_seqs=0) == INVALID
-    d = _desc(dtype=2)
-    d.attn_flags = kvq.KVQ_ATTN_FP8_QK
-    assert _decode(L, d, num_seqs=0) == UNSUPPORTED
-    assert _append(L, d, n=0) == OK
+    for flags in (kvq.KVQ_ATTN_FP8_QK, kvq.KVQ_ATTN_FP8_PV):
+        d = _desc(dtype=2)
+        d.attn_flags = flags
+        assert _decode(L, d, num_seqs=0) == UNSUPPORTED
+        assert _append(L, d, n=0) == OK
+    # with the FP8 score-V product on 16-token pages the plan counts 32-token
+    # blocks: the workspace is the one of a page-32 cache
+    d16, d32 = _desc(), _desc(page_size=32)
+    d16.attn_flags = kvq.KVQ_ATTN_FP8_PV
+    assert _ws(L, d16, 32, 32, 8192) == _ws(L, d32, 32, 32, 8192)
+    assert _ws(L, d16, 32, 32, 8192, part=3) == _ws(L, d32, 32, 32, 8192, part=3)
     d = _kivi_desc()
     d.attn_flags = kvq.KVQ_ATTN_FP8_QK
     assert _decode(L, d, "kvq_kivi_decode_attention", num_seqs=0, hq=16, maxp=4, max_ctx=128) == UNSUPPORTED
