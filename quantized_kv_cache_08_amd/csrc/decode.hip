@@ -480,11 +480,12 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
         }
     };
 
-    // ---- software pipeline.  FP8 keeps one chunk of loads in flight while a
-    // chunk is computed (two buffers, 194 VGPRs: two waves per SIMD); INT8
-    // keeps two (three buffers: one wave per SIMD, which measured faster for
-    // INT8 than two waves with two buffers)
-    if constexpr (is_fp8_format(DT)) {
+    // ---- software pipeline: one chunk of loads in flight while a chunk is
+    // computed (two buffers), for FP8 and INT8 alike.  Launched with one wave
+    // per SIMD, this measured faster than INT8 with two chunks in flight
+    // (three buffers; 70B shape 724 -> 712 us) and than two waves per SIMD:
+    // fewer requests in flight per CU serve the memory system better.
+    {
         ChunkBuf b0, b1;
         load(b0, 0);
         for (int c = 0;;) {
@@ -493,21 +494,6 @@ __device__ __forceinline__ void process_segment(const SplitParams& p, const int 
             if (++c >= n_chunks) break;
             load(b0, c + 1);
             compute(b1, c);
-            if (++c >= n_chunks) break;
-        }
-    } else {
-        ChunkBuf b0, b1, b2;
-        load(b0, 0);
-        load(b1, 1);
-        for (int c = 0;;) {
-            load(b2, c + 2);
-            compute(b0, c);
-            if (++c >= n_chunks) break;
-            load(b0, c + 2);
-            compute(b1, c);
-            if (++c >= n_chunks) break;
-            load(b1, c + 2);
-            compute(b2, c);
             if (++c >= n_chunks) break;
         }
     }

@@ -209,11 +209,11 @@ kvq_status run_split(const kvq_cache* c, const void* q, int32_t num_seqs, int32_
     if (e != hipSuccess) return KVQ_EHIP;
     const int cus = device_cus();
     if (cus <= 0 || per_cu <= 0) return KVQ_EHIP;
-    // FP8: one workgroup (one wave per SIMD) per CU, although two fit: with
-    // two waves per SIMD the memory system holds more requests than it
-    // serves best, and the measured kernel time is about 2% longer
-    const bool fp8 = c->dtype == KVQ_FP8_E4M3 || c->dtype == KVQ_FP8_E5M2;
-    const int blocks_per_cu = fp8 ? std::min(per_cu, kFp8BlocksPerCu) : per_cu;
+    // FP8 / INT8: one workgroup (one wave per SIMD) per CU, although two fit:
+    // with two waves per SIMD the memory system holds more requests than it
+    // serves best, and the measured kernel time is 2-3% longer.  KIVI keeps
+    // the occupancy limit (two per CU): its pages take more arithmetic per byte.
+    const int blocks_per_cu = kivi ? per_cu : std::min(per_cu, kSplitBlocksPerCu);
     const int grid = blocks_per_cu * cus;
     p.total_waves = grid * (kSplitThreads / 64);
     if (kivi) {

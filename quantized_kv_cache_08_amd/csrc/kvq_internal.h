@@ -14,7 +14,7 @@ constexpr int kMaxRanges = 2048;   // most work ranges (over all KV heads) of on
 constexpr int kMinChunkPages = 4;  // smallest automatic work range per wave
 constexpr int kSegmentCost = 8;    // start-up of a segment, in pages, for ragged batches (measured best on the mixed workload)
 constexpr int kSplitThreads = 256; // 4 waves per workgroup
-constexpr int kFp8BlocksPerCu = 1;  // FP8 split kernel workgroups per CU
+constexpr int kSplitBlocksPerCu = 1;  // FP8 / INT8 split kernel workgroups per CU
 constexpr int kKiviGroup = 32;     // KIVI path: tokens per K group = page size
 
 struct AppendParams {
