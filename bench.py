@@ -225,30 +225,37 @@ def cpu_baseline(w, budget_s: float):
             "quantize_s": round(t_quant, 3), "attention_s": round(t_attn, 3)}
 
 
+# (workgroups per CU, 16-byte loads in flight per thread) tried by the read
+# probe: 16 to 48 KiB in flight per CU, where a streaming read on this part
+# peaks (about 24 KiB)
+READ_SHAPES = ((1, 4), (1, 6), (2, 2), (2, 3), (2, 4), (3, 2), (4, 1), (4, 2), (3, 4))
+
+
 def attainable_read(nbytes: int, launches: int = 20) -> dict:
     """A plain streaming read (kvq_read_probe) of as many bytes as the split
     kernel reads per launch, from two buffers used in turn (so that each launch
     reads data the previous one did not leave in the last-level cache), timed
-    back to back between two events; the best of a few launch shapes."""
+    back to back between two events; the best of the launch shapes in
+    READ_SHAPES."""
     import torch
     from quantized_kv_cache_08_amd import testing as KT
     n = max(16, nbytes // 16 * 16)
     bufs = [torch.full((n,), i + 1, dtype=torch.uint8, device="cuda") for i in range(2)]
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     best = None
-    for bpc in (1, 2, 4, 8):
+    for bpc, lpt in READ_SHAPES:
         for i in range(4):
-            KT.read_probe(bufs[i % 2], sink, bpc)
+            KT.read_probe(bufs[i % 2], sink, bpc, lpt)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(launches):
-            KT.read_probe(bufs[i % 2], sink, bpc)
+            KT.read_probe(bufs[i % 2], sink, bpc, lpt)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / launches
         gbs = n / (us * 1e-6) / 1e9
         if best is None or gbs > best["gbs"]:
-            best = {"gbs": round(gbs, 1), "us": round(us, 2), "blocks_per_cu": bpc}
+            best = {"gbs": round(gbs, 1), "us": round(us, 2), "blocks_per_cu": bpc, "loads_per_thread": lpt}
     del bufs
     torch.cuda.empty_cache()
     return {"kernel": "plain streaming read of the split kernel's byte count (kvq_read_probe)", "bytes": n,

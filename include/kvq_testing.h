@@ -36,13 +36,15 @@ kvq_status kvq_e4m3_encode(const float* x, uint8_t* codes, int64_t n, hipStream_
  * NaN -> 0x7F.  x: device fp32 [n];  codes: device u8 [n]. */
 kvq_status kvq_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_t stream);
 
-/* A plain streaming read of `bytes` bytes at `buf` (16-byte loads, four in
- * flight per thread, a grid-stride loop over blocks_per_cu x (compute units)
- * workgroups of 256 threads).  buf: device, 16-byte aligned, bytes a multiple
- * of 16.  sink: one device uint32 the kernel may write (in practice never).
- * blocks_per_cu in 1..32. */
+/* A plain streaming read of `bytes` bytes at `buf`: blocks_per_cu x (compute
+ * units) workgroups of 256 threads step through the buffer in windows of
+ * loads_per_thread x 4 KiB, each thread keeping loads_per_thread 16-byte loads
+ * (one per 4 KiB of its window) in flight.  buf: device, 16-byte aligned,
+ * bytes a multiple of 16.  sink: one device uint32 the kernel may write (in
+ * practice never).  blocks_per_cu in 1..32; loads_per_thread 1, 2, 3, 4, 6
+ * or 8. */
 kvq_status kvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks_per_cu,
-                          hipStream_t stream);
+                          int32_t loads_per_thread, hipStream_t stream);
 
 /* What the decode kernels' split plan does with one batch, computed on the
  * host by the same plan functions the kernels run. */

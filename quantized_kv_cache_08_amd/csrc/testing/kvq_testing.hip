@@ -51,17 +51,23 @@ typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t fold(const u32x4v_t v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
-// Plain streaming read: 16-byte loads, four in flight per thread, grid-stride.
+// Plain streaming read: workgroup windows of L x 256 16-byte elements, thread t
+// loading elements t, t + 256, ... of its window (L loads in flight), windows
+// grid-stride.  A window cut by the end of the buffer is read up to the end.
+template <int L>
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4v_t* __restrict__ p, long long n16,
                                                          uint32_t* sink) {
-    const long long stride = (long long)gridDim.x * 256;
-    long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long step = (long long)gridDim.x * 256 * L;
+    long long i = (long long)blockIdx.x * 256 * L + threadIdx.x;
     uint32_t acc = 0;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4v_t a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-        acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
+    for (; i + 256 * (L - 1) < n16; i += step) {
+        u32x4v_t v[L];
+#pragma unroll
+        for (int k = 0; k < L; ++k) v[k] = p[i + 256 * k];
+#pragma unroll
+        for (int k = 0; k < L; ++k) acc ^= fold(v[k]);
     }
-    for (; i < n16; i += stride) acc ^= fold(p[i]);
+    for (; i < n16; i += 256) acc ^= fold(p[i]);   // the last, partial window
     // the loads must not be dropped: their folded value decides a store that
     // in practice never happens (sink is one valid word either way)
     if (acc == 0x9E3779B9u) sink[0] = acc;
@@ -92,16 +98,27 @@ kvq_status kvq_e5m2_encode(const float* x, uint8_t* codes, int64_t n, hipStream_
 }
 
 kvq_status kvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t blocks_per_cu,
-                          hipStream_t stream) {
-    if (bytes < 0 || (bytes & 15) || blocks_per_cu <= 0 || blocks_per_cu > 32) return KVQ_EINVAL;
+                          int32_t loads_per_thread, hipStream_t stream) {
+    const bool loads_ok = loads_per_thread >= 1 && loads_per_thread <= 8 && loads_per_thread != 5 &&
+                          loads_per_thread != 7;
+    if (bytes < 0 || (bytes & 15) || blocks_per_cu <= 0 || blocks_per_cu > 32 || !loads_ok) return KVQ_EINVAL;
     if (bytes == 0) return KVQ_OK;
     if (!buf || !sink) return KVQ_EINVAL;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return KVQ_EHIP;
-    hipLaunchKernelGGL(read_probe_kernel, dim3(cus * blocks_per_cu), dim3(256), 0, stream, (const u32x4v_t*)buf,
-                       (long long)(bytes / 16), sink);
+    const dim3 grid(cus * blocks_per_cu);
+    const u32x4v_t* b = (const u32x4v_t*)buf;
+    const long long n16 = bytes / 16;
+    switch (loads_per_thread) {
+        case 1: hipLaunchKernelGGL(read_probe_kernel<1>, grid, dim3(256), 0, stream, b, n16, sink); break;
+        case 2: hipLaunchKernelGGL(read_probe_kernel<2>, grid, dim3(256), 0, stream, b, n16, sink); break;
+        case 3: hipLaunchKernelGGL(read_probe_kernel<3>, grid, dim3(256), 0, stream, b, n16, sink); break;
+        case 4: hipLaunchKernelGGL(read_probe_kernel<4>, grid, dim3(256), 0, stream, b, n16, sink); break;
+        case 6: hipLaunchKernelGGL(read_probe_kernel<6>, grid, dim3(256), 0, stream, b, n16, sink); break;
+        default: hipLaunchKernelGGL(read_probe_kernel<8>, grid, dim3(256), 0, stream, b, n16, sink); break;
+    }
     return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_EHIP;
 }
 

@@ -45,7 +45,7 @@ def lib() -> ctypes.CDLL:
             getattr(L, fn).restype = ctypes.c_int
             getattr(L, fn).argtypes = [_P, _P, ctypes.c_int64, _P]
         L.kvq_read_probe.restype = ctypes.c_int
-        L.kvq_read_probe.argtypes = [_P, ctypes.c_int64, _P, _I32, _P]
+        L.kvq_read_probe.argtypes = [_P, ctypes.c_int64, _P, _I32, _I32, _P]
         L.kvq_plan_stats.restype = ctypes.c_int
         L.kvq_plan_stats.argtypes = [_I32, _I32, _I32, _P, _I32, _I32, _I32, ctypes.POINTER(PlanInfo)]
         _lib = L
@@ -71,12 +71,13 @@ def e5m2_encode(x: torch.Tensor, codes: torch.Tensor, stream=None) -> None:
     _check("kvq_e5m2_encode", lib().kvq_e5m2_encode(_ptr(x), _ptr(codes), int(x.numel()), _stream(stream)))
 
 
-def read_probe(buf: torch.Tensor, sink: torch.Tensor, blocks_per_cu: int = 2, stream=None) -> None:
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, blocks_per_cu: int = 2, loads_per_thread: int = 3,
+               stream=None) -> None:
     """Plain streaming read of a device byte buffer (kvq_read_probe)."""
     _need(buf, "buf", torch.uint8)
     _need(sink, "sink", torch.int32, min_numel=1)
     _check("kvq_read_probe", lib().kvq_read_probe(_ptr(buf), int(buf.numel()), _ptr(sink), int(blocks_per_cu),
-                                                  _stream(stream)))
+                                                  int(loads_per_thread), _stream(stream)))
 
 
 def plan_stats(page_size: int, num_kv_heads: int, total_waves: int, context_lens: Sequence[int],

@@ -399,10 +399,12 @@ def test_binding_rejects_malformed_tensors():
 
 def test_read_probe_validation(T):
     L = T
-    assert L.kvq_read_probe(FAKE, -16, FAKE, 2, None) == INVALID
-    assert L.kvq_read_probe(FAKE, 17, FAKE, 2, None) == INVALID          # not a multiple of 16
-    assert L.kvq_read_probe(FAKE, 1024, FAKE, 0, None) == INVALID
-    assert L.kvq_read_probe(FAKE, 1024, FAKE, 33, None) == INVALID
-    assert L.kvq_read_probe(None, 1024, FAKE, 2, None) == INVALID
-    assert L.kvq_read_probe(FAKE, 1024, None, 2, None) == INVALID
-    assert L.kvq_read_probe(FAKE, 0, FAKE, 2, None) == OK
+    assert L.kvq_read_probe(FAKE, -16, FAKE, 2, 3, None) == INVALID
+    assert L.kvq_read_probe(FAKE, 17, FAKE, 2, 3, None) == INVALID       # not a multiple of 16
+    assert L.kvq_read_probe(FAKE, 1024, FAKE, 0, 3, None) == INVALID
+    assert L.kvq_read_probe(FAKE, 1024, FAKE, 33, 3, None) == INVALID
+    for loads in (0, 5, 7, 9, -1):                                        # 1, 2, 3, 4, 6, 8 only
+        assert L.kvq_read_probe(FAKE, 1024, FAKE, 2, loads, None) == INVALID
+    assert L.kvq_read_probe(None, 1024, FAKE, 2, 3, None) == INVALID
+    assert L.kvq_read_probe(FAKE, 1024, None, 2, 3, None) == INVALID
+    assert L.kvq_read_probe(FAKE, 0, FAKE, 2, 3, None) == OK
