@@ -69,6 +69,40 @@ __device__ __forceinline__ void merge_row(const float* pl, const float* po, long
     if (lse && lane == 0) *lse = (m + __log2f(s)) * kLn2;
 }
 
+// Inclusive prefix over the lanes of each row of 16 (Hillis-Steele with DPP
+// row shifts; a lane whose source lies before its row takes `id`).
+template <class Op>
+__device__ __forceinline__ int row_incl_scan(int v, const int id, Op op) {
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xF, 0xF, false));   // row_shr:1
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xF, 0xF, false));   // row_shr:2
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xF, 0xF, false));   // row_shr:4
+    v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xF, 0xF, false));   // row_shr:8
+    return v;
+}
+
+// Inclusive sum over the 64 lanes of a wave, in registers: row scans, then
+// each row adds the totals of the rows before it (lanes 15, 31, 47).
+__device__ __forceinline__ int wave_incl_sum(const int v, const int lane) {
+    const int s = row_incl_scan(v, 0, [](int a, int b) { return a + b; });
+    const int t0 = __builtin_amdgcn_readlane(s, 15);
+    const int t1 = __builtin_amdgcn_readlane(s, 31);
+    const int t2 = __builtin_amdgcn_readlane(s, 47);
+    const int row = lane >> 4;
+    return s + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
+}
+
+// Minimum / maximum over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int wave_min(const int v) {
+    const int s = row_incl_scan(v, 0x7FFFFFFF, [](int a, int b) { return min(a, b); });
+    return min(min(__builtin_amdgcn_readlane(s, 15), __builtin_amdgcn_readlane(s, 31)),
+               min(__builtin_amdgcn_readlane(s, 47), __builtin_amdgcn_readlane(s, 63)));
+}
+__device__ __forceinline__ int wave_max(const int v) {
+    const int s = row_incl_scan(v, (int)0x80000000, [](int a, int b) { return max(a, b); });
+    return max(max(__builtin_amdgcn_readlane(s, 15), __builtin_amdgcn_readlane(s, 31)),
+               max(__builtin_amdgcn_readlane(s, 47), __builtin_amdgcn_readlane(s, 63)));
+}
+
 // Calls seg(b, h, page0, page1, slot, n_segments, lane) for every segment of
 // this wave's ranges (split_plan.h).  Must be called by every thread of a
 // workgroup of kSplitThreads threads (it synchronises twice); the dynamic LDS
@@ -97,62 +131,61 @@ __device__ __forceinline__ void merge_row(const float* pl, const float* po, long
 template <int PS, typename Seg>
 __device__ __forceinline__ void for_each_segment(const SplitParams& p, Seg&& seg) {
     extern __shared__ int s_pfx[];   // [num_seqs + 1]
-    __shared__ int s_wsum[kSplitThreads / 64];
-    __shared__ int s_wmin[kSplitThreads / 64], s_wmax[kSplitThreads / 64];
+    __shared__ int s_wred[4][kSplitThreads / 64];   // per wave: page sum, items with pages, min, max
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = tid >> 6;
     const int B = p.num_seqs;
 
-    // pages per sequence, their extremes (is the batch uniform?)
+    // One read of the thread's context lengths gives its pages, their sum,
+    // the count of items that hold pages and the extremes (is the batch
+    // uniform?).  An item weighs pages + K when it holds pages, so the
+    // exclusive prefix of the weights is P + K N, with P and N the exclusive
+    // prefixes of the pages and of the items with pages: both are scanned
+    // before K is known, and one barrier serves the scans and the extremes.
     const int per = (B + kSplitThreads - 1) / kSplitThreads;
     const int beg = min(tid * per, B);
     const int end = min(beg + per, B);
-    int pmin = 0x7FFFFFFF, pmax = 0;
+    int psum = 0, nz = 0, pmin = 0x7FFFFFFF, pmax = 0, pg0 = 0;
     for (int i = beg; i < end; ++i) {
         const int pg = pages_of(p.context_lens[i], p.max_ctx, PS);
+        if (i == beg) pg0 = pg;
+        psum += pg;
+        nz += pg > 0 ? 1 : 0;
         pmin = min(pmin, pg);
         pmax = max(pmax, pg);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        pmin = min(pmin, __shfl_xor(pmin, o));
-        pmax = max(pmax, __shfl_xor(pmax, o));
-    }
-    if (lane == 0) {
-        s_wmin[wid] = pmin;
-        s_wmax[wid] = pmax;
+    const int ps_incl = wave_incl_sum(psum, lane);
+    const int nz_incl = wave_incl_sum(nz, lane);
+    pmin = wave_min(pmin);
+    pmax = wave_max(pmax);
+    if (lane == 63) {
+        s_wred[0][wid] = ps_incl;
+        s_wred[1][wid] = nz_incl;
+        s_wred[2][wid] = pmin;
+        s_wred[3][wid] = pmax;
     }
     __syncthreads();
+    int P = ps_incl - psum, N = nz_incl - nz, Ptot = 0, Ntot = 0;
     for (int w = 0; w < kSplitThreads / 64; ++w) {
-        pmin = min(pmin, s_wmin[w]);
-        pmax = max(pmax, s_wmax[w]);
+        const int sp = s_wred[0][w], sn = s_wred[1][w];
+        if (w < wid) {
+            P += sp;
+            N += sn;
+        }
+        Ptot += sp;
+        Ntot += sn;
+        pmin = min(pmin, s_wred[2][w]);
+        pmax = max(pmax, s_wred[3][w]);
     }
     const int K = segment_cost(pmin, pmax);
-    auto weight = [&](int i) { return item_weight(pages_of(p.context_lens[i], p.max_ctx, PS), K); };
-
-    // exclusive prefix sum of the per-sequence item weights
-    int local = 0;
-    for (int i = beg; i < end; ++i) local += weight(i);
-    int incl = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) s_wsum[wid] = incl;
-    __syncthreads();
-    int run = incl - local;
-    for (int w = 0; w < wid; ++w) run += s_wsum[w];
+    int run = P + K * N;
     for (int i = beg; i < end; ++i) {
+        const int pg = (i == beg) ? pg0 : pages_of(p.context_lens[i], p.max_ctx, PS);
         s_pfx[i] = run;
-        run += weight(i);
+        run += item_weight(pg, K);
     }
-    if (tid == 0) {
-        int tot = 0;
-        for (int w = 0; w < kSplitThreads / 64; ++w) tot += s_wsum[w];
-        s_pfx[B] = tot;
-    }
+    if (tid == 0) s_pfx[B] = Ptot + K * Ntot;
     __syncthreads();
 
     const long long S = s_pfx[B];                     // weight of one head's items
